@@ -1,0 +1,147 @@
+/*
+ * commvq.h: C ABI of libcommvq, decode-step attention read directly from an additive
+ * vector-quantized ("CommVQ") KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   - Each key and each value vector is quantized as a whole by additive quantization: it is the sum,
+ *     group by group, of one codeword from each of R residual codebooks, so it decodes by a plain
+ *     codebook product ("1-bit quantization" tag page, CommVQ abstract; "CommVQ: Commutative Vector
+ *     Quantization for KV Cache Compression" summary, section Approach).
+ *   - The key codebook stores, per RoPE 2-D subspace, 2x2 blocks [[a,-b],[b,a]] that commute with the
+ *     RoPE rotation, so the query x codebook products are formed once per decode step and reused for
+ *     every cached position; values are reduced by weighting their codes with the softmax before the
+ *     codebook product (pith.science verdict for arXiv 2506.18879, pith_extraction.key_machinery and
+ *     pith_extraction.forward_implications).
+ *
+ * Shapes and layouts (all row-major, innermost last; D = head_dim, G = n_groups, W = D / G,
+ * R = n_residuals, N = n_codes, T = total cached token rows, P = D / 2 RoPE pairs):
+ *   q          [B][Hq][D]          query of the new token, already rotated by the caller (dtype)
+ *   k_codebook [Hkv][G][R][N][W]   key codewords; per RoPE pair u of a group the two numbers (a, b) of
+ *                                  the block [[a,-b],[b,a]] (dtype)
+ *   v_codebook [Hkv][G][R][N][W]   value codewords (dtype)
+ *   k_codes    [Hkv][T][R][G]      uint8 code indices (N = 256: one byte per index, no packing)
+ *   v_codes    [Hkv][T][R][G]      uint8
+ *   seq_start  [B] int64, seq_len [B] int32: sequence b owns token rows seq_start[b] ..
+ *              seq_start[b] + seq_len[b] - 1 of every KV head; its keys sit at positions 0 .. L_b - 1.
+ *   out        [B][Hq][D]          fp32
+ * q head h reads KV head h / (Hq / Hkv). Pair j covers dims (2j, 2j+1); RoPE frequency
+ * theta_j = rope_base^(-2j/D); group g holds pairs 4g .. 4g+3 (W = 8).
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless marked (host). Buffers are owned by the caller; the library
+ *     keeps no state, allocates nothing, frees nothing and never synchronizes.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream) and runs
+ *     asynchronously. Device faults surface at the caller's next synchronization.
+ *   - All argument checks run on the host before any launch; a failing call launches nothing and has
+ *     no side effects. Return value: COMMVQ_OK (0) or a negative commvq_status; the thread-local
+ *     commvq_last_error_detail() then names the offending argument.
+ *   - Supported now: head_dim 128, n_groups 16, n_codes 256, n_residuals 1..2, Hq / Hkv = 4,
+ *     dtype fp16 or fp32. Other values return COMMVQ_EUNSUPPORTED.
+ *   - No C++ exception crosses the ABI.
+ */
+#ifndef COMMVQ_H
+#define COMMVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { COMMVQ_F16 = 1, COMMVQ_F32 = 2 } commvq_dtype;
+
+typedef enum {
+  COMMVQ_OK = 0,
+  COMMVQ_EINVAL = -1,       /* null pointer, negative size, inconsistent shapes */
+  COMMVQ_EUNSUPPORTED = -2, /* valid but not implemented (head_dim, groups, codes, residuals, GQA) */
+  COMMVQ_EWORKSPACE = -3,   /* workspace (or table) smaller than the matching *_size() call asks */
+  COMMVQ_EHIP = -4          /* a HIP launch failed; the detail string holds HIP's message */
+} commvq_status;
+
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;     /* D (128) */
+  int32_t n_groups;     /* G (16): one code index per residual per group of W = D/G dims */
+  int32_t n_residuals;  /* R (1..2): residual codebooks; R bits per scalar at N = 256, W = 8 */
+  int32_t n_codes;      /* N (256) */
+  double rope_base;     /* RoPE base (e.g. 500000) */
+  float softmax_scale;  /* e.g. 1/sqrt(D) */
+  int32_t dtype;        /* commvq_dtype of q and both codebooks; outputs are fp32 */
+} commvq_dims;
+
+/* Static description of a status code. */
+const char* commvq_status_string(int status);
+/* Detail of the last failing call made by this thread ("" if none). */
+const char* commvq_last_error_detail(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * RoPE phase table: e^{i * t * theta_j} for positions t = 0 .. n_positions-1, stored as two levels,
+ * fine[f][j] = e^{i f theta_j} (f < 64) followed by coarse[c][j] = e^{i 64 c theta_j}
+ * (c < ceil(n_positions / 64)), complex fp32 (re, im) interleaved, each entry computed in fp64 and
+ * rounded once. The rotation of a key at position t is coarse[t >> 6][j] * fine[t & 63][j]
+ * ("pith.science verdict", key_machinery: the block-diagonal rotation R_m of each 2-D sub-vector).
+ * It depends only on rope_base, head_dim and the longest position, like a model's RoPE cache:
+ * build it once and pass it to every commvq_attn_decode call.
+ * ------------------------------------------------------------------------------------------- */
+size_t commvq_rope_table_size(const commvq_dims* d /* host */, int32_t n_positions);
+int commvq_rope_table(const commvq_dims* d /* host */, int32_t n_positions, void* table, size_t table_bytes,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Query x key-codebook table ("computed once and reused across all cached positions",
+ * pith.science verdict, key_machinery; summary page, Approach):
+ *   table[b][h][g][r][l][2u]   = q[b][h][2j] * a + q[b][h][2j+1] * b
+ *   table[b][h][g][r][l][2u+1] = q[b][h][2j] * b - q[b][h][2j+1] * a
+ * i.e. conj(q_j) * (a + i b) for pair j = 4g + u and codeword (a, b) = k_codebook[kv][g][r][l][2u..2u+1].
+ * Output [B][Hq][G][R][N][W] in dtype (fp16 results are rounded once from fp32).
+ * ------------------------------------------------------------------------------------------- */
+int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const void* k_codebook, void* table,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Decode-step attention over the compressed cache. For every (b, h):
+ *   s_t   = softmax_scale * sum_j Re( conj(q_j) * khat_{t,j} * e^{i t theta_j} ),  t < L_b
+ *   khat_{t,j} = sum_r k_codebook[kv][g][r][k_codes[kv][seq_start[b]+t][r][g]][2u..2u+1]   (j = 4g+u)
+ *   out[b][h] = sum_t softmax(s)_t * vhat_t,  vhat_t = sum_r v_codebook[kv][g][r][v_codes[..][r][g]]
+ * No key or value is dequantized to memory. Sequences with L_b = 0 produce zeros.
+ * rope_table: from commvq_rope_table with rope_positions >= max_len.
+ * max_len (host) must be >= every seq_len[b]; total_tokens (host) is T, the row count of the code
+ * arrays. workspace: at least commvq_attn_decode_workspace_size(d, max_len) bytes, caller owned;
+ * its contents need no initialisation and are scratch after the call.
+ * ------------------------------------------------------------------------------------------- */
+size_t commvq_attn_decode_workspace_size(const commvq_dims* d /* host */, int32_t max_len);
+int commvq_attn_decode(const commvq_dims* d /* host */, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
+                       const void* k_codebook, const void* v_codebook, const int64_t* seq_start,
+                       const int32_t* seq_len, int32_t max_len /* host */, int64_t total_tokens /* host */,
+                       const void* rope_table, int32_t rope_positions /* host */, void* workspace,
+                       size_t ws_bytes /* host */, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Value reduce with given weights, in the reordered form of the pages (pith.science verdict,
+ * forward_implications: the softmax weights multiply the value codes before the codebook product):
+ *   bins[g][r][l] = sum_{t < L_b} p[b][h][t] * [v_codes[kv][seq_start[b]+t][r][g] == l]
+ *   out[b][h][8g+w] = sum_r sum_l bins[g][r][l] * v_codebook[kv][g][r][l][w]
+ * p: [B][Hq][max_len] fp32, any finite real values, used as given (no renormalisation); entries at
+ * t >= L_b are ignored. workspace: commvq_value_reduce_workspace_size(d, max_len) bytes.
+ * ------------------------------------------------------------------------------------------- */
+size_t commvq_value_reduce_workspace_size(const commvq_dims* d /* host */, int32_t max_len);
+int commvq_value_reduce(const commvq_dims* d /* host */, const float* p, const uint8_t* v_codes,
+                        const void* v_codebook, const int64_t* seq_start, const int32_t* seq_len,
+                        int32_t max_len /* host */, int64_t total_tokens /* host */, void* workspace,
+                        size_t ws_bytes /* host */, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Code unpack exactly as the attention kernels read codes: out[kv][t][r][g] = index (int32).
+ * codes [Hkv][total_tokens][R][G] uint8. Used to test the unpack bit-exactly.
+ * ------------------------------------------------------------------------------------------- */
+int commvq_debug_unpack(const commvq_dims* d /* host */, const uint8_t* codes, int64_t total_tokens /* host */,
+                        int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMMVQ_H */

@@ -1,0 +1,97 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol, and rejects bad
+arguments on the host (these calls return before any HIP call, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import vector_quantized_kv_amd as vq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "commvq.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(commvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = vq.lib()
+    names = declared_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(vq.EXPORTED_SYMBOLS)
+
+
+def test_dims_struct_layout_matches_header():
+    # int32 x7, pad, double, float, int32 -> 48 bytes with 8-byte alignment
+    assert ctypes.sizeof(vq.Dims) == 48
+    assert vq.Dims.rope_base.offset == 32
+
+
+def test_status_strings():
+    assert vq.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert vq.status_string(s) != "unknown status"
+
+
+def _attn(d, **kw):
+    args = dict(q=None, kc=None, vc=None, kb=None, vb=None, ss=None, sl=None, max_len=0, total=0, rope=None,
+                rope_pos=0, ws=None, ws_bytes=0, out=None)
+    args.update(kw)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
+    conv = lambda v: fake if v == "p" else v
+    return vq.lib().commvq_attn_decode(ctypes.byref(d), *(conv(args[k]) for k in
+                                       ("q", "kc", "vc", "kb", "vb", "ss", "sl")), args["max_len"], args["total"],
+                                       conv(args["rope"]), args["rope_pos"], conv(args["ws"]), args["ws_bytes"],
+                                       conv(args["out"]), None)
+
+
+ALL = dict(q="p", kc="p", vc="p", kb="p", vb="p", ss="p", sl="p", rope="p", out="p", ws="p")
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_residuals", 3, vq.EUNSUPPORTED), ("n_residuals", 0, vq.EINVAL), ("head_dim", 64, vq.EUNSUPPORTED),
+    ("n_groups", 8, vq.EUNSUPPORTED), ("n_codes", 64, vq.EUNSUPPORTED), ("n_q_heads", 30, vq.EINVAL),
+    ("n_q_heads", 16, vq.EUNSUPPORTED), ("batch", 0, vq.EINVAL), ("dtype", 7, vq.EINVAL),
+    ("rope_base", 0.5, vq.EINVAL),
+])
+def test_bad_dims_rejected(field, value, status):
+    d = vq.make_dims(1, 32, 8, 2)
+    setattr(d, field, value)
+    assert _attn(d, **ALL, max_len=10, total=10, rope_pos=10, ws_bytes=1 << 30) == status
+    assert vq.last_error_detail() != ""
+
+
+def test_null_pointer_and_sizes_rejected():
+    d = vq.make_dims(1, 32, 8, 2)
+    base = dict(ALL, max_len=100, total=100, rope_pos=100, ws_bytes=1 << 30)
+    assert _attn(d, **dict(base, q=None)) == vq.EINVAL
+    assert _attn(d, **dict(base, max_len=-1)) == vq.EINVAL
+    assert _attn(d, **dict(base, total=-5)) == vq.EINVAL
+    assert _attn(d, **dict(base, rope_pos=50)) == vq.EINVAL
+    assert _attn(d, **dict(base, ws_bytes=16)) == vq.EWORKSPACE
+    assert "workspace" in vq.last_error_detail()
+    assert _attn(d, **dict(base, ws=None)) == vq.EWORKSPACE
+
+
+def test_misaligned_codes_rejected():
+    d = vq.make_dims(1, 32, 8, 2)
+    L = vq.lib()
+    p, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1001)
+    st = L.commvq_attn_decode(ctypes.byref(d), p, odd, p, p, p, p, p, 10, 10, p, 10, p, 1 << 30, p, None)
+    assert st == vq.EINVAL and "aligned" in vq.last_error_detail()
+
+
+def test_workspace_sizes():
+    d = vq.make_dims(2, 32, 8, 1)
+    # one partial of 132 floats per (sequence, q head, 1024-token split)
+    assert vq.attn_decode_workspace_size(d, 131072) == 2 * 32 * 128 * 132 * 4
+    assert vq.attn_decode_workspace_size(d, 1) == 2 * 32 * 1 * 132 * 4
+    assert vq.value_reduce_workspace_size(d, 2048) == 2 * 32 * 2 * 132 * 4
+    assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (64 + 2048) * 64 * 8
+    assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 0) == 0

@@ -1,0 +1,180 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: per (b, q head) output row, max_i |gpu - oracle| / max_i |oracle| <= 2e-3 for fp16 storage
+and 1e-5 for fp32 storage; the unpack is compared bit-exactly. Inputs come from workloads.make_inputs,
+shared by both sides; the oracle sees the same fp16/fp32 values converted exactly to fp64.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"float16": 2e-3, "float32": 1e-5}
+THREADS = 16
+
+
+@pytest.fixture(scope="module")
+def vq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vector_quantized_kv_amd as m
+    m.lib()
+    return m
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rowwise_rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    num = np.abs(got - ref).reshape(-1, ref.shape[-1]).max(-1)
+    den = np.abs(ref).reshape(-1, ref.shape[-1]).max(-1)
+    den = np.where(den == 0, 1.0, den)
+    return (num / den).max()
+
+
+def run_attn(vq, cfg, inp):
+    d = vq.dims_of(cfg)
+    layer = vq.Layer(d, inp)
+    out = layer.attn_decode()
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+CONFIG_NAMES = list(workloads.CONFIGS)
+
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_attn_decode_matches_oracle_full_configs(vq, name):
+    cfg = workloads.CONFIGS[name]
+    announce(f"attn_decode {name}")
+    inp = workloads.make_inputs(cfg)
+    got = run_attn(vq, cfg, inp)
+    ref = oracle.run_config(cfg, inp, n_threads=THREADS)
+    err = rowwise_rel_err(got, ref)
+    print(f"{name}: max row-relative error {err:.3e} (tol {TOL[cfg.dtype]})", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[cfg.dtype]
+
+
+EDGE = [
+    ("one_token_f32", 1, (1,), 2, "float32"),
+    ("ragged_tails_f32", 3, (1023, 1024, 1025), 1, "float32"),
+    ("ragged_small_f16", 4, (1, 64, 65, 3000), 2, "float16"),
+    ("empty_sequence_f16", 3, (700, 0, 2049), 2, "float16"),
+    ("split_boundary_r1_f16", 2, (2048, 4096), 1, "float16"),
+]
+
+
+@pytest.mark.parametrize("name,B,lengths,R,dtype", EDGE)
+def test_attn_decode_edge_cases(vq, name, B, lengths, R, dtype):
+    announce(f"attn_decode edge {name} lengths={lengths} R={R} {dtype}")
+    cfg = workloads.custom(name, B, 8, 2, lengths, R, dtype, 100 + len(name))
+    inp = workloads.make_inputs(cfg)
+    got = run_attn(vq, cfg, inp)
+    ref = oracle.run_config(cfg, inp, n_threads=THREADS)
+    for b, L in enumerate(lengths):
+        if L == 0:
+            assert np.all(got[b] == 0.0)
+    err = rowwise_rel_err(got, ref)
+    print(f"{name}: {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_1k_r2_f32", "llama8b_8k_r2", "llama8b_32k_r1", "ragged16_r2"])
+def test_unpack_bit_exact(vq, name):
+    cfg = workloads.CONFIGS[name]
+    announce(f"debug_unpack {name}")
+    inp = workloads.make_inputs(cfg)
+    d = vq.dims_of(cfg)
+    for key in ("k_codes", "v_codes"):
+        codes = torch.from_numpy(inp[key]).cuda()
+        got = vq.debug_unpack(d, codes, int(inp["total_tokens"]))
+        torch.cuda.synchronize()
+        ref = oracle.unpack(oracle.dims_of(cfg), inp[key], int(inp["total_tokens"]))
+        np.testing.assert_array_equal(got.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("dtype,R,tol", [("float32", 2, 1e-6), ("float16", 1, 1e-3), ("float16", 2, 1e-3)])
+def test_qcodebook_table_matches_oracle(vq, dtype, R, tol):
+    announce(f"qcodebook_table {dtype} R={R}")
+    cfg = workloads.custom("tab", 2, 8, 2, (5, 5), R, dtype, 21)
+    inp = workloads.make_inputs(cfg)
+    d = vq.dims_of(cfg)
+    dt = torch.float16 if dtype == "float16" else torch.float32
+    q = torch.from_numpy(inp["q"]).cuda().to(dt)
+    kcb = torch.from_numpy(inp["k_cb"]).cuda().to(dt)
+    got = vq.qcodebook_table(d, q, kcb)
+    torch.cuda.synchronize()
+    ref = oracle.table(oracle.dims_of(cfg), inp["q"], inp["k_cb"])
+    g = got.float().cpu().numpy().astype(np.float64)
+    for b in range(2):
+        for h in range(8):
+            err = np.abs(g[b, h] - ref[b, h]).max() / np.abs(ref[b, h]).max()
+            assert err <= tol, (b, h, err)
+
+
+@pytest.mark.parametrize("dtype,R,signed", [("float32", 2, False), ("float32", 1, True), ("float16", 2, False),
+                                            ("float16", 1, True)])
+def test_value_reduce_matches_oracle(vq, dtype, R, signed):
+    announce(f"value_reduce {dtype} R={R} signed={signed}")
+    cfg = workloads.custom("vr", 3, 8, 2, (2500, 1, 1024), R, dtype, 22)
+    inp = workloads.make_inputs(cfg)
+    L = int(inp["max_len"])
+    rng = np.random.default_rng(23)
+    p = rng.uniform(-1 if signed else 0, 1, size=(3, 8, L)).astype(np.float32)
+    d = vq.dims_of(cfg)
+    dt = torch.float16 if dtype == "float16" else torch.float32
+    got = vq.value_reduce(d, torch.from_numpy(p).cuda(), torch.from_numpy(inp["v_codes"]).cuda(),
+                          torch.from_numpy(inp["v_cb"]).cuda().to(dt), torch.from_numpy(inp["seq_start"]).cuda(),
+                          torch.from_numpy(inp["seq_len"]).cuda(), L, int(inp["total_tokens"]))
+    torch.cuda.synchronize()
+    ref = oracle.value_reduce(oracle.dims_of(cfg), p, inp["v_codes"], inp["v_cb"], inp["seq_start"], inp["seq_len"], L)
+    err = rowwise_rel_err(got.cpu().numpy(), ref)
+    print(f"value_reduce {dtype} R={R}: {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+def test_rope_table_matches_fp64(vq):
+    announce("rope_table")
+    d = vq.make_dims(1, 4, 1, 1)
+    n = 131072 + 5
+    t = vq.rope_table(d, n).cpu().numpy().view(np.complex64).reshape(-1, 64)
+    theta = 500000.0 ** (-np.arange(64) * 2.0 / 128)
+    fine = np.exp(1j * np.outer(np.arange(64), theta))
+    coarse = np.exp(1j * np.outer(64.0 * np.arange((n + 63) // 64), theta))
+    assert t.shape[0] == 64 + coarse.shape[0]
+    assert np.abs(t[:64] - fine).max() < 1e-7
+    assert np.abs(t[64:] - coarse).max() < 1e-7
+
+
+def test_workspace_too_small_is_rejected(vq):
+    announce("workspace too small")
+    cfg = workloads.custom("ws", 1, 8, 2, (3000,), 1, "float16", 24)
+    inp = workloads.make_inputs(cfg)
+    d = vq.dims_of(cfg)
+    layer = vq.Layer(d, inp)
+    small = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(vq.CommVQError) as ei:
+        vq.attn_decode(d, layer.q, layer.k_codes, layer.v_codes, layer.k_cb, layer.v_cb, layer.seq_start,
+                       layer.seq_len, layer.max_len, layer.total_tokens, layer.rope, layer.rope_positions, small)
+    assert ei.value.status == vq.EWORKSPACE
+
+
+def test_repeat_calls_are_consistent(vq):
+    announce("repeat calls")
+    cfg = workloads.CONFIGS["llama8b_8k_r2"]
+    inp = workloads.make_inputs(cfg)
+    layer = vq.Layer(vq.dims_of(cfg), inp)
+    a = layer.attn_decode().clone()
+    b = layer.attn_decode().clone()
+    torch.cuda.synchronize()
+    assert rowwise_rel_err(b.cpu().numpy(), a.cpu().numpy().astype(np.float64)) <= 1e-5

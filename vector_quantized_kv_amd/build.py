@@ -1,0 +1,41 @@
+"""Build libcommvq.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libcommvq.so")
+SOURCES = ["api.cpp", "kernels.hip"]
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+    # packed fp32 VALU ops are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    tmp = LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines() if "packed-fp32-ops" not in ln]
+    if proc.returncode != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError("hipcc failed building libcommvq.so")
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

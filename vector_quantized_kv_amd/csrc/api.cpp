@@ -1,0 +1,195 @@
+// C-ABI front end of libcommvq: host-side argument checks, workspace sizing and launches.
+// Every check runs before any HIP call, so a rejected call has no side effects.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "commvq_internal.h"
+
+using namespace commvq;
+
+namespace {
+
+thread_local std::string g_detail;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return status;
+}
+
+int ok() {
+  g_detail.clear();
+  return COMMVQ_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(COMMVQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every entry point.
+int check_dims(const commvq_dims* d) {
+  if (!d) return fail(COMMVQ_EINVAL, "dims is NULL");
+  if (d->batch < 1) return fail(COMMVQ_EINVAL, "batch = %d must be >= 1", d->batch);
+  if (d->n_kv_heads < 1 || d->n_q_heads < 1)
+    return fail(COMMVQ_EINVAL, "n_q_heads = %d and n_kv_heads = %d must be >= 1", d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(COMMVQ_EINVAL, "n_q_heads = %d is not a multiple of n_kv_heads = %d", d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads / d->n_kv_heads != kGqa)
+    return fail(COMMVQ_EUNSUPPORTED, "q heads per KV head = %d; only %d is implemented",
+                d->n_q_heads / d->n_kv_heads, kGqa);
+  if (d->head_dim != kHeadDim) return fail(COMMVQ_EUNSUPPORTED, "head_dim = %d; only %d is implemented", d->head_dim, kHeadDim);
+  if (d->n_groups != kGroups) return fail(COMMVQ_EUNSUPPORTED, "n_groups = %d; only %d is implemented", d->n_groups, kGroups);
+  if (d->n_codes != kCodes) return fail(COMMVQ_EUNSUPPORTED, "n_codes = %d; only %d is implemented", d->n_codes, kCodes);
+  if (d->n_residuals < 1) return fail(COMMVQ_EINVAL, "n_residuals = %d must be >= 1", d->n_residuals);
+  if (d->n_residuals > 2) return fail(COMMVQ_EUNSUPPORTED, "n_residuals = %d; only 1 and 2 are implemented", d->n_residuals);
+  if (d->dtype != COMMVQ_F16 && d->dtype != COMMVQ_F32) return fail(COMMVQ_EINVAL, "dtype = %d is not a commvq_dtype", d->dtype);
+  if (!(d->rope_base > 1.0)) return fail(COMMVQ_EINVAL, "rope_base = %g must be > 1", d->rope_base);
+  if (!(d->softmax_scale == d->softmax_scale) || d->softmax_scale == 0.f)
+    return fail(COMMVQ_EINVAL, "softmax_scale must be finite and non-zero");
+  return COMMVQ_OK;
+}
+
+size_t rope_bytes(int32_t n_positions) {
+  return static_cast<size_t>(kFineRows + rope_coarse_rows(n_positions)) * kPairs * sizeof(float2);
+}
+
+size_t part_bytes(const commvq_dims* d, int32_t max_len) {
+  return static_cast<size_t>(d->batch) * d->n_q_heads * n_splits_for(max_len) * kPartFloats * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* commvq_status_string(int status) {
+  switch (status) {
+    case COMMVQ_OK: return "ok";
+    case COMMVQ_EINVAL: return "invalid argument";
+    case COMMVQ_EUNSUPPORTED: return "unsupported configuration";
+    case COMMVQ_EWORKSPACE: return "workspace too small";
+    case COMMVQ_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* commvq_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t commvq_rope_table_size(const commvq_dims* d, int32_t n_positions) {
+  if (check_dims(d) != COMMVQ_OK || n_positions < 1) return 0;
+  return rope_bytes(n_positions);
+}
+
+int commvq_rope_table(const commvq_dims* d, int32_t n_positions, void* table, size_t table_bytes, void* stream) {
+  if (int st = check_dims(d)) return st;
+  if (n_positions < 1) return fail(COMMVQ_EINVAL, "n_positions = %d must be >= 1", n_positions);
+  if (!table) return fail(COMMVQ_EINVAL, "table is NULL");
+  if (table_bytes < rope_bytes(n_positions))
+    return fail(COMMVQ_EWORKSPACE, "table_bytes = %zu < %zu", table_bytes, rope_bytes(n_positions));
+  if (!aligned16(table)) return fail(COMMVQ_EINVAL, "table must be 16-byte aligned");
+  return hip_status(launch_rope_table(d->rope_base, n_positions, static_cast<float2*>(table),
+                                      static_cast<hipStream_t>(stream)),
+                    "rope_table launch");
+}
+
+int commvq_qcodebook_table(const commvq_dims* d, const void* q, const void* k_codebook, void* table, void* stream) {
+  if (int st = check_dims(d)) return st;
+  if (!q || !k_codebook || !table) return fail(COMMVQ_EINVAL, "q, k_codebook and table must be non-NULL");
+  return hip_status(launch_qtable(d->dtype, d->n_residuals, d->batch, d->n_q_heads, d->n_kv_heads, q, k_codebook,
+                                  table, static_cast<hipStream_t>(stream)),
+                    "qcodebook_table launch");
+}
+
+size_t commvq_attn_decode_workspace_size(const commvq_dims* d, int32_t max_len) {
+  if (check_dims(d) != COMMVQ_OK || max_len < 0) return 0;
+  return part_bytes(d, max_len);
+}
+
+int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
+                       const void* k_codebook, const void* v_codebook, const int64_t* seq_start,
+                       const int32_t* seq_len, int32_t max_len, int64_t total_tokens, const void* rope_table,
+                       int32_t rope_positions, void* workspace, size_t ws_bytes, float* out, void* stream) {
+  if (int st = check_dims(d)) return st;
+  if (!q || !k_codes || !v_codes || !k_codebook || !v_codebook || !seq_start || !seq_len || !rope_table || !out)
+    return fail(COMMVQ_EINVAL, "a required pointer is NULL");
+  if (max_len < 0) return fail(COMMVQ_EINVAL, "max_len = %d must be >= 0", max_len);
+  if (total_tokens < 0) return fail(COMMVQ_EINVAL, "total_tokens = %lld must be >= 0", (long long)total_tokens);
+  if (max_len > 0 && total_tokens < 1) return fail(COMMVQ_EINVAL, "total_tokens must be >= 1 when max_len > 0");
+  if (rope_positions < max_len)
+    return fail(COMMVQ_EINVAL, "rope_positions = %d < max_len = %d", rope_positions, max_len);
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(rope_table))
+    return fail(COMMVQ_EINVAL, "k_codes, v_codes and rope_table must be 16-byte aligned");
+  const size_t need = part_bytes(d, max_len);
+  if (!workspace || ws_bytes < need) return fail(COMMVQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  AttnArgs a;
+  a.q = q;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_cb = k_codebook;
+  a.v_cb = v_codebook;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.total_tokens = total_tokens;
+  a.rope = static_cast<const float2*>(rope_table);
+  a.n_splits = static_cast<int32_t>(n_splits_for(max_len));
+  a.n_q_heads = d->n_q_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.scale = d->softmax_scale;
+  a.part = static_cast<float*>(workspace);
+  return hip_status(launch_attn(d->dtype, d->n_residuals, d->batch, a, out, static_cast<hipStream_t>(stream)),
+                    "attn_decode launch");
+}
+
+size_t commvq_value_reduce_workspace_size(const commvq_dims* d, int32_t max_len) {
+  if (check_dims(d) != COMMVQ_OK || max_len < 0) return 0;
+  return part_bytes(d, max_len);
+}
+
+int commvq_value_reduce(const commvq_dims* d, const float* p, const uint8_t* v_codes, const void* v_codebook,
+                        const int64_t* seq_start, const int32_t* seq_len, int32_t max_len, int64_t total_tokens,
+                        void* workspace, size_t ws_bytes, float* out, void* stream) {
+  if (int st = check_dims(d)) return st;
+  if (!p || !v_codes || !v_codebook || !seq_start || !seq_len || !out)
+    return fail(COMMVQ_EINVAL, "a required pointer is NULL");
+  if (max_len < 0) return fail(COMMVQ_EINVAL, "max_len = %d must be >= 0", max_len);
+  if (total_tokens < 0) return fail(COMMVQ_EINVAL, "total_tokens = %lld must be >= 0", (long long)total_tokens);
+  if (max_len > 0 && total_tokens < 1) return fail(COMMVQ_EINVAL, "total_tokens must be >= 1 when max_len > 0");
+  if (!aligned16(v_codes)) return fail(COMMVQ_EINVAL, "v_codes must be 16-byte aligned");
+  const size_t need = part_bytes(d, max_len);
+  if (!workspace || ws_bytes < need) return fail(COMMVQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  ValueReduceArgs a;
+  a.p = p;
+  a.p_stride = max_len;
+  a.v_codes = v_codes;
+  a.v_cb = v_codebook;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.total_tokens = total_tokens;
+  a.n_splits = static_cast<int32_t>(n_splits_for(max_len));
+  a.n_q_heads = d->n_q_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.part = static_cast<float*>(workspace);
+  return hip_status(launch_value_reduce(d->dtype, d->n_residuals, d->batch, a, out, static_cast<hipStream_t>(stream)),
+                    "value_reduce launch");
+}
+
+int commvq_debug_unpack(const commvq_dims* d, const uint8_t* codes, int64_t total_tokens, int32_t* out, void* stream) {
+  if (int st = check_dims(d)) return st;
+  if (!codes || !out) return fail(COMMVQ_EINVAL, "codes and out must be non-NULL");
+  if (total_tokens < 0) return fail(COMMVQ_EINVAL, "total_tokens = %lld must be >= 0", (long long)total_tokens);
+  if (!aligned16(codes)) return fail(COMMVQ_EINVAL, "codes must be 16-byte aligned");
+  return hip_status(launch_debug_unpack(d->n_residuals, d->n_kv_heads, total_tokens, codes, out,
+                                        static_cast<hipStream_t>(stream)),
+                    "debug_unpack launch");
+}
+
+}  // extern "C"
