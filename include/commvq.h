@@ -79,9 +79,9 @@ const char* commvq_last_error_detail(void);
 
 /* ---------------------------------------------------------------------------------------------
  * RoPE phase table: e^{i * t * theta_j} for positions t = 0 .. n_positions-1, stored as two levels,
- * fine[f][j] = e^{i f theta_j} (f < 64) followed by coarse[c][j] = e^{i 64 c theta_j}
+ * fine[j][f] = e^{i f theta_j} (f < 64, pair-major) followed by coarse[c][j] = e^{i 64 c theta_j}
  * (c < ceil(n_positions / 64)), complex fp32 (re, im) interleaved, each entry computed in fp64 and
- * rounded once. The rotation of a key at position t is coarse[t >> 6][j] * fine[t & 63][j]
+ * rounded once. The rotation of a key at position t is coarse[t >> 6][j] * fine[j][t & 63]
  * ("pith.science verdict", key_machinery: the block-diagonal rotation R_m of each 2-D sub-vector).
  * It depends only on rope_base, head_dim and the longest position, like a model's RoPE cache:
  * build it once and pass it to every commvq_attn_decode call.
@@ -108,9 +108,13 @@ int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const
  *   out[b][h] = sum_t softmax(s)_t * vhat_t,  vhat_t = sum_r v_codebook[kv][g][r][v_codes[..][r][g]]
  * No key or value is dequantized to memory. Sequences with L_b = 0 produce zeros.
  * rope_table: from commvq_rope_table with rope_positions >= max_len.
- * max_len (host) must be >= every seq_len[b]; total_tokens (host) is T, the row count of the code
- * arrays. workspace: at least commvq_attn_decode_workspace_size(d, max_len) bytes, caller owned;
- * its contents need no initialisation and are scratch after the call.
+ * max_len (host) must be >= every seq_len[b], and seq_start[b] + seq_len[b] <= total_tokens (host),
+ * the row count of the code arrays. rope_table must hold at least rope_positions positions.
+ * workspace: at least commvq_attn_decode_workspace_size(d, max_len) bytes, caller owned, 256-byte
+ * aligned, and zero-filled before its first use: its head holds one arrival counter per (b, kv) that
+ * the last workgroup of each (b, kv) resets, so every completed call leaves it zero-filled again; the
+ * rest is scratch. Calls that share one workspace must not overlap in time.
+ * Codes, codebooks and rope_table must be 16-byte aligned.
  * ------------------------------------------------------------------------------------------- */
 size_t commvq_attn_decode_workspace_size(const commvq_dims* d /* host */, int32_t max_len);
 int commvq_attn_decode(const commvq_dims* d /* host */, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,

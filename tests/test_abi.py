@@ -89,9 +89,13 @@ def test_misaligned_codes_rejected():
 
 def test_workspace_sizes():
     d = vq.make_dims(2, 32, 8, 1)
-    # one partial of 132 floats per (sequence, q head, 1024-token split)
-    assert vq.attn_decode_workspace_size(d, 131072) == 2 * 32 * 128 * 132 * 4
-    assert vq.attn_decode_workspace_size(d, 1) == 2 * 32 * 1 * 132 * 4
+    # attention: 256 B of arrival counters, then one partial of 132 floats per (sequence, q head, split);
+    # the split is 256 x blocks-per-wave tokens (<= 2048), sized for about 512 work items
+    assert vq.attn_decode_workspace_size(d, 131072) == 256 + 2 * 32 * 64 * 132 * 4   # 2048-token splits
+    assert vq.attn_decode_workspace_size(d, 1) == 256 + 2 * 32 * 1 * 132 * 4
+    d1 = vq.make_dims(1, 32, 8, 2)
+    assert vq.attn_decode_workspace_size(d1, 8192) == 256 + 32 * 32 * 132 * 4          # 256-token splits
+    assert vq.attn_decode_workspace_size(d1, 131072) == 256 + 32 * 64 * 132 * 4       # 2048-token splits
     assert vq.value_reduce_workspace_size(d, 2048) == 2 * 32 * 2 * 132 * 4
     assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (64 + 2048) * 64 * 8
     assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 0) == 0

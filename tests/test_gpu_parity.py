@@ -152,7 +152,7 @@ def test_rope_table_matches_fp64(vq):
     fine = np.exp(1j * np.outer(np.arange(64), theta))
     coarse = np.exp(1j * np.outer(64.0 * np.arange((n + 63) // 64), theta))
     assert t.shape[0] == 64 + coarse.shape[0]
-    assert np.abs(t[:64] - fine).max() < 1e-7
+    assert np.abs(t[:64] - fine.T).max() < 1e-7  # fine part is pair-major: [j][f]
     assert np.abs(t[64:] - coarse).max() < 1e-7
 
 

@@ -135,6 +135,12 @@ def attn_decode_workspace_size(d: Dims, max_len: int) -> int:
     return int(lib().commvq_attn_decode_workspace_size(ctypes.byref(d), int(max_len)))
 
 
+def attn_workspace(d: Dims, max_len: int, device="cuda"):
+    """Zero-filled attention workspace (its arrival counters must start at zero; calls leave them zero)."""
+    import torch
+    return torch.zeros(max(attn_decode_workspace_size(d, max_len), 256), dtype=torch.uint8, device=device)
+
+
 def attn_decode(d: Dims, q, k_codes, v_codes, k_codebook, v_codebook, seq_start, seq_len, max_len: int,
                 total_tokens: int, rope, rope_positions: int, workspace=None, out=None, stream=None):
     """Decode-step attention; returns out [B][Hq][D] fp32 (see commvq_attn_decode)."""
@@ -142,7 +148,7 @@ def attn_decode(d: Dims, q, k_codes, v_codes, k_codebook, v_codebook, seq_start,
     if out is None:
         out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.empty(max(attn_decode_workspace_size(d, max_len), 16), dtype=torch.uint8, device=q.device)
+        workspace = attn_workspace(d, max_len, q.device)
     st = lib().commvq_attn_decode(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_codebook),
                                   _ptr(v_codebook), _ptr(seq_start), _ptr(seq_len), int(max_len), int(total_tokens),
                                   _ptr(rope), int(rope_positions), _ptr(workspace), workspace.numel() *
@@ -198,8 +204,7 @@ class Layer:
         self.total_tokens = int(inputs["total_tokens"])
         self.rope_positions = rope_positions if rope_positions is not None else max(self.max_len, 1)
         self.rope = rope if rope is not None else rope_table(d, self.rope_positions, device=device)
-        self.workspace = torch.empty(max(attn_decode_workspace_size(d, self.max_len), 16), dtype=torch.uint8,
-                                     device=device)
+        self.workspace = attn_workspace(d, self.max_len, device)
         self.out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=device)
 
     def attn_decode(self, stream=None):

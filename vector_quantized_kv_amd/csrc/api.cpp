@@ -67,6 +67,13 @@ size_t part_bytes(const commvq_dims* d, int32_t max_len) {
   return static_cast<size_t>(d->batch) * d->n_q_heads * n_splits_for(max_len) * kPartFloats * sizeof(float);
 }
 
+// attention workspace: [arrival counters, padded to 256 B][partials B x Hq x n_splits x kPartFloats]
+size_t attn_ws_bytes(const commvq_dims* d, int32_t max_len) {
+  const int32_t S = attn_split_tokens(max_len, d->batch, d->n_kv_heads);
+  return attn_counter_bytes(d->batch, d->n_kv_heads) +
+         static_cast<size_t>(d->batch) * d->n_q_heads * attn_n_splits(max_len, S) * kPartFloats * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,7 +118,7 @@ int commvq_qcodebook_table(const commvq_dims* d, const void* q, const void* k_co
 
 size_t commvq_attn_decode_workspace_size(const commvq_dims* d, int32_t max_len) {
   if (check_dims(d) != COMMVQ_OK || max_len < 0) return 0;
-  return part_bytes(d, max_len);
+  return attn_ws_bytes(d, max_len);
 }
 
 int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
@@ -126,10 +133,13 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
   if (max_len > 0 && total_tokens < 1) return fail(COMMVQ_EINVAL, "total_tokens must be >= 1 when max_len > 0");
   if (rope_positions < max_len)
     return fail(COMMVQ_EINVAL, "rope_positions = %d < max_len = %d", rope_positions, max_len);
-  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(rope_table))
-    return fail(COMMVQ_EINVAL, "k_codes, v_codes and rope_table must be 16-byte aligned");
-  const size_t need = part_bytes(d, max_len);
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(rope_table) || !aligned16(k_codebook) ||
+      !aligned16(v_codebook))
+    return fail(COMMVQ_EINVAL, "k_codes, v_codes, both codebooks and rope_table must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(COMMVQ_EINVAL, "workspace must be 256-byte aligned");
+  const size_t need = attn_ws_bytes(d, max_len);
   if (!workspace || ws_bytes < need) return fail(COMMVQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+  const int32_t split_tokens = attn_split_tokens(max_len, d->batch, d->n_kv_heads);
   AttnArgs a;
   a.q = q;
   a.k_codes = k_codes;
@@ -140,12 +150,16 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
   a.seq_len = seq_len;
   a.total_tokens = total_tokens;
   a.rope = static_cast<const float2*>(rope_table);
-  a.n_splits = static_cast<int32_t>(n_splits_for(max_len));
+  a.split_tokens = split_tokens;
+  a.n_splits = static_cast<int32_t>(attn_n_splits(max_len, split_tokens));
   a.n_q_heads = d->n_q_heads;
   a.n_kv_heads = d->n_kv_heads;
   a.scale = d->softmax_scale;
-  a.part = static_cast<float*>(workspace);
-  return hip_status(launch_attn(d->dtype, d->n_residuals, d->batch, a, out, static_cast<hipStream_t>(stream)),
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                    attn_counter_bytes(d->batch, d->n_kv_heads));
+  a.out = out;
+  return hip_status(launch_attn(d->dtype, d->n_residuals, d->batch, a, static_cast<hipStream_t>(stream)),
                     "attn_decode launch");
 }
 

@@ -14,13 +14,34 @@ constexpr int kGroups = 16;     // G: code indices per residual per vector
 constexpr int kGroupDim = 8;    // W: dims per group (4 RoPE pairs)
 constexpr int kCodes = 256;     // N: one byte per index
 constexpr int kGqa = 4;         // q heads per KV head
-constexpr int kSplitTokens = 1024;  // tokens per (sequence, KV head) work item
+constexpr int kSplitTokens = 1024;  // value_reduce: tokens per (sequence, KV head) work item
 constexpr int kPartFloats = 132;    // per (b, q head, split): m, l, 2 pad, o[128]
 constexpr int kFineRows = 64;       // RoPE table: fine rows e^{i f theta}, f < 64
+constexpr int kAttnThreads = 256;   // attention workgroup: 4 waves
+constexpr int kAttnMaxBlocksPerWave = 8;  // 64-token blocks per wave per split
+constexpr int kCounterBytes = 256;  // attention workspace head: per-(b, kv) arrival counters
 
 inline int64_t n_splits_for(int32_t max_len) {
   int64_t s = (static_cast<int64_t>(max_len) + kSplitTokens - 1) / kSplitTokens;
   return s > 0 ? s : 1;
+}
+
+// Attention split size: a multiple of 256 tokens (64 per wave-block, 4 waves), at most 2048, chosen so
+// that the grid holds about 512 (sequence, KV head, split) items: two workgroups per CU, all resident.
+inline int32_t attn_split_tokens(int32_t max_len, int32_t batch, int32_t n_kv_heads) {
+  const int64_t work = static_cast<int64_t>(max_len) * batch * n_kv_heads;
+  int64_t blocks_per_wave = (work + 512LL * kAttnThreads - 1) / (512LL * kAttnThreads);
+  if (blocks_per_wave < 1) blocks_per_wave = 1;
+  if (blocks_per_wave > kAttnMaxBlocksPerWave) blocks_per_wave = kAttnMaxBlocksPerWave;
+  return static_cast<int32_t>(blocks_per_wave * kAttnThreads);
+}
+inline int64_t attn_n_splits(int32_t max_len, int32_t split_tokens) {
+  int64_t s = (static_cast<int64_t>(max_len) + split_tokens - 1) / split_tokens;
+  return s > 0 ? s : 1;
+}
+inline size_t attn_counter_bytes(int32_t batch, int32_t n_kv_heads) {
+  size_t b = static_cast<size_t>(batch) * n_kv_heads * sizeof(uint32_t);
+  return (b + kCounterBytes - 1) / kCounterBytes * kCounterBytes;
 }
 inline int64_t rope_coarse_rows(int32_t n_positions) { return (static_cast<int64_t>(n_positions) + 63) / 64; }
 
@@ -35,10 +56,13 @@ struct AttnArgs {
   int64_t total_tokens;
   const float2* rope;
   int32_t n_splits;
+  int32_t split_tokens;
   int32_t n_q_heads;
   int32_t n_kv_heads;
   float scale;
-  float* part;
+  uint32_t* counters;  // [B][Hkv], zero between calls
+  float* part;         // [B][Hq][n_splits][kPartFloats]
+  float* out;
 };
 
 struct ValueReduceArgs {
@@ -58,7 +82,7 @@ struct ValueReduceArgs {
 hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hipStream_t s);
 hipError_t launch_qtable(int dtype, int R, int B, int Hq, int Hkv, const void* q, const void* kcb, void* out,
                          hipStream_t s);
-hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, float* out, hipStream_t s);
+hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, hipStream_t s);
 hipError_t launch_value_reduce(int dtype, int R, int B, const ValueReduceArgs& a, float* out, hipStream_t s);
 hipError_t launch_debug_unpack(int R, int Hkv, int64_t total_tokens, const uint8_t* codes, int32_t* out,
                                hipStream_t s);
