@@ -59,15 +59,12 @@ __device__ __forceinline__ h4 cat(h2 a, h2 b) { return (h4){a.x, a.y, b.x, b.y};
 __device__ __forceinline__ h4 to_h4(f4 x) { return (h4){(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]}; }
 
 // k * e^{i phi} for packed fp16 complex numbers (re in the low half, im in the high half), with
-// f = (cos, sin): t = (-k.im * sin, k.re * sin), then w = k * (cos, cos) + t. The half selection and the
-// negation fold into operand modifiers of the two packed instructions. The empty asm makes f opaque at
-// each use, so loop-invariant code motion cannot hoist a negated copy of every phase into registers.
+// f = (cos, sin): t = k.im * f = (k.im cos, k.im sin), then w = k.re * f + (-t.im, t.re). Every half
+// broadcast, swap and negation applies to k or t (values used once), so they fold into operand
+// modifiers of the two packed instructions and f is used as stored.
 __device__ __forceinline__ h2 crot(h2 k, h2 f) {
-  uint32_t fu = __builtin_bit_cast(uint32_t, f);
-  asm volatile("" : "+v"(fu));
-  const h2 g = __builtin_bit_cast(h2, fu);
-  const h2 t = (h2){k.y, k.x} * (h2){-g.y, g.y};
-  return k * (h2){g.x, g.x} + t;
+  const h2 t = (h2){k.y, k.y} * f;
+  return (h2){k.x, k.x} * f + (h2){-t.y, t.x};
 }
 
 struct Split2 {  // fp32 value as fp16 hi + lo
@@ -281,6 +278,18 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
 #pragma unroll
   for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
 
+  // Code records of the current phase live in code[]; as soon as a block has consumed its record, the
+  // record of the same token for the next phase is requested, so the next phase's codes stream in while
+  // this phase computes (phases: K residual 0..R-1, then V residual 0..R-1).
+  uint4 code[kMaxBlocks];
+  auto request_codes = [&](int ph, int i) {
+    const uint8_t* base = ph < R ? a.k_codes : a.v_codes;
+    code[i] = load_code_record(base, a.total_tokens, kv, token_row(i), R, ph % R);
+  };
+#pragma unroll
+  for (int i = 0; i < kMaxBlocks; ++i)
+    if (i < my_blocks) request_codes(0, i);
+
   // ------------------------------------------------------------------------------ key phases
   {
     h2 F[kPairs];
@@ -291,30 +300,16 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
         F[j] = (h2){(f16)f.x, (f16)f.y};
       }
     }
-    for (int r = 0; r < R; ++r) {
-      if (r > 0) __syncthreads();  // every wave is done with the previous table
-      load_table<T, R>(cb_k, r, lds, wave, lane);
-      // prefetch the phase's code records and coarse phases while the table streams in
-      uint4 code[kMaxBlocks];
-      float4 cph[kMaxBlocks][2];
+    // A operands: the query rotated by the conjugate coarse phase of each 64-token block,
+    // q'' = q * conj(C), in fp16 (fp32 inputs: hi and lo fp16 parts); the same for every key phase.
+    h4 Ah[kMaxBlocks][2], Al[kMaxBlocks][2];
 #pragma unroll
-      for (int i = 0; i < kMaxBlocks; ++i) {
-        if (i < my_blocks) {
-          code[i] = load_code_record(a.k_codes, a.total_tokens, kv, token_row(i), R, r);
-          const float2* cr = coarse + static_cast<int64_t>((t0 + (wave + kWaves * i) * 64) >> 6) * kPairs;
-          cph[i][0] = *reinterpret_cast<const float4*>(cr + 2 * quad);
-          cph[i][1] = *reinterpret_cast<const float4*>(cr + 32 + 2 * quad);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      // A operands: the query rotated by the conjugate coarse phase of each 64-token block,
-      // q'' = q * conj(C), in fp16 (fp32 inputs: hi and lo fp16 parts)
-      h4 Ah[kMaxBlocks][2], Al[kMaxBlocks][2];
-#pragma unroll
-      for (int i = 0; i < kMaxBlocks; ++i) {
+    for (int i = 0; i < kMaxBlocks; ++i) {
+      if (i < my_blocks) {
+        const float2* cr = coarse + static_cast<int64_t>((t0 + (wave + kWaves * i) * 64) >> 6) * kPairs;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const float4 c = cph[i][m];
+          const float4 c = *reinterpret_cast<const float4*>(cr + 32 * m + 2 * quad);
           const float2 q0 = qv[2 * m], q1 = qv[2 * m + 1];
           const float qq[4] = {q0.x * c.x + q0.y * c.y, q0.y * c.x - q0.x * c.y, q1.x * c.z + q1.y * c.w,
                                q1.y * c.z - q1.x * c.w};
@@ -326,6 +321,11 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
           }
         }
       }
+    }
+    for (int r = 0; r < R; ++r) {
+      if (r > 0) __syncthreads();  // every wave is done with the previous table
+      load_table<T, R>(cb_k, r, lds, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < kMaxBlocks; ++i) {
@@ -335,6 +335,7 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
           } else {
             key_groups<float>(std::make_integer_sequence<int, kGroups>{}, lds, code[i], fine, Ah[i], Al[i], sc[i]);
           }
+          request_codes(r + 1, i);
         }
       }
     }
@@ -411,16 +412,15 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
   for (int r = 0; r < R; ++r) {
     if (r > 0) __syncthreads();
     load_table<T, R>(cb_v, r, lds, wave, lane);
-    uint4 code[kMaxBlocks];
-#pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i)
-      if (i < my_blocks) code[i] = load_code_record(a.v_codes, a.total_tokens, kv, token_row(i), R, r);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i)
-      if (i < my_blocks)
+    for (int i = 0; i < kMaxBlocks; ++i) {
+      if (i < my_blocks) {
         value_groups<T>(std::make_integer_sequence<int, kGroups>{}, lds, code[i], ident, pth[i], ptl[i], O);
+        if (r + 1 < R) request_codes(R + r + 1, i);
+      }
+    }
   }
 
   // ------------------------------------------------------------------------ workgroup reduction
@@ -496,22 +496,27 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
     if (lane == 0) merge_den[wave] = den;
   }
   __syncthreads();
+  // each thread merges 2 outputs; the split loop issues 16 independent loads per step
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int o = tid + kAttnThreads * k;
     const int h = o >> 7, d = o & 127;
     const float* ph = pb + h * part_row + 4 + d;
     const float* wh = sw + h * a.n_splits;
-    float num0 = 0.f, num1 = 0.f, num2 = 0.f, num3 = 0.f;
-    int s2 = 0;
-    for (; s2 + 4 <= ns; s2 += 4) {
-      num0 = fmaf(wh[s2], ph[s2 * kPartFloats], num0);
-      num1 = fmaf(wh[s2 + 1], ph[(s2 + 1) * kPartFloats], num1);
-      num2 = fmaf(wh[s2 + 2], ph[(s2 + 2) * kPartFloats], num2);
-      num3 = fmaf(wh[s2 + 3], ph[(s2 + 3) * kPartFloats], num3);
+    float acc[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = s0 + u < ns ? ph[(s0 + u) * kPartFloats] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u] = fmaf(s0 + u < ns ? wh[s0 + u] : 0.f, v[u], acc[u]);
     }
-    for (; s2 < ns; ++s2) num0 = fmaf(wh[s2], ph[s2 * kPartFloats], num0);
-    out_bh[o] = ((num0 + num1) + (num2 + num3)) / merge_den[h];
+    float num = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) num += acc[u];
+    out_bh[o] = num / merge_den[h];
   }
   if (tid == 0) __hip_atomic_store(a.counters + b * a.n_kv_heads + kv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
