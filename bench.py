@@ -30,7 +30,10 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "vector_quantized_kv_amd", "csrc", f) for f in ("kernels.hip",)]
+# sources that determine the fused attention kernel's memory traffic (split sizing, layout, kernel body)
+KERNEL_SOURCES = [os.path.join(ROOT, "vector_quantized_kv_amd", "csrc", f)
+                  for f in ("attn.hip", "commvq_internal.h", "device_common.h", "api.cpp")]
+KERNEL_NAME = "attn_kernel"
 
 
 def kernel_source_hash() -> str:
@@ -87,6 +90,52 @@ def cpu_baseline(cfg, inp, budget_s: float = 12.0) -> dict:
     return {"value": d_tokens / per_run, "unit": "KV tokens/s per layer", "cores": threads, "kind": "oracle",
             "sample": f"{runs} full decode steps of one layer ({cfg.name}: {d_tokens} tokens x "
                       f"{cfg.n_kv_heads} KV heads), fp64, {threads} host threads; {per_run:.3f} s per step"}
+
+
+def read_stream_gbps(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Achievable HBM read rate on this machine: torch.sum over a 1 GiB fp32 tensor (one read pass each)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        x.sum()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del x
+    return nbytes / (ms * 1e-3) * 1e-9
+
+
+def profile_run(names, launches: int):
+    """Few launches per workload (for rocprofv3), plus a 1 GiB device copy whose FETCH_SIZE / WRITE_SIZE
+    calibrate the counters (it reads and writes exactly 1 GiB)."""
+    import torch
+    import vector_quantized_kv_amd as vq
+    for name in names:
+        cfg = workloads.CONFIGS[name]
+        d = vq.dims_of(cfg)
+        base = workloads.make_inputs(cfg)
+        per_layer = algorithmic_bytes(cfg, int(base["total_tokens"]))["total"]
+        layers = max(4, int(math.ceil((1 << 30) / per_layer)))
+        rope = vq.rope_table(d, int(base["max_len"]))
+        Ls = [vq.Layer(d, base if i == 0 else workloads.make_inputs(cfg, seed=cfg.seed + 1000 * i), rope=rope,
+                       rope_positions=int(base["max_len"])) for i in range(layers)]
+        for i in range(launches):
+            Ls[i % layers].attn_decode()
+        torch.cuda.synchronize()
+        print(f"profile: {name} {launches} launches over {layers} layer copies", flush=True)
+        del Ls
+        torch.cuda.empty_cache()
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("profile: 3 copies of 1 GiB (calibration)", flush=True)
 
 
 def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check: bool):
@@ -184,6 +233,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="compare layer 0 with the oracle")
+    ap.add_argument("--profile", action="store_true",
+                    help="no timing: a few launches of --config and --also workloads plus a 1 GiB copy, for rocprofv3")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -194,6 +245,10 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.profile:
+        names = [args.config] + [s for s in args.also.split(",") if s and s != args.config]
+        profile_run(names, max(args.steps, 1))
+        return
     cfg = workloads.CONFIGS[args.config]
     prim, base = run_config(cfg, args.steps, args.warmup, args.layers, not args.no_graph, args.check)
     variants = {cfg.name: prim}
@@ -217,9 +272,10 @@ def main():
                    "groups": cfg.n_groups, "codes": cfg.n_codes, "layers_rotated": prim["layers_rotated"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "commvq attention (split kernel + combine)",
+                     "kernel": f"{KERNEL_NAME} (fused decode attention, one launch per layer)",
                      "algorithmic_bytes_per_launch": prim["bytes"]["codes"]},
         "variants": variants,
+        "hbm_read_stream_GBps": read_stream_gbps(),
         "kernel_source_sha256_16": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

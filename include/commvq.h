@@ -19,8 +19,10 @@
  *   k_codebook [Hkv][G][R][N][W]   key codewords; per RoPE pair u of a group the two numbers (a, b) of
  *                                  the block [[a,-b],[b,a]] (dtype)
  *   v_codebook [Hkv][G][R][N][W]   value codewords (dtype)
- *   k_codes    [Hkv][T][R][G]      uint8 code indices (N = 256: one byte per index, no packing)
- *   v_codes    [Hkv][T][R][G]      uint8
+ *   k_codes    [Hkv][R][T][G]      uint8 code indices (N = 256: one byte per index, no packing); one
+ *                                  plane per residual codebook, so a token's 16 group indices of one
+ *                                  residual form one 16-byte record
+ *   v_codes    [Hkv][R][T][G]      uint8
  *   seq_start  [B] int64, seq_len [B] int32: sequence b owns token rows seq_start[b] ..
  *              seq_start[b] + seq_len[b] - 1 of every KV head; its keys sit at positions 0 .. L_b - 1.
  *   out        [B][Hq][D]          fp32
@@ -78,10 +80,12 @@ const char* commvq_status_string(int status);
 const char* commvq_last_error_detail(void);
 
 /* ---------------------------------------------------------------------------------------------
- * RoPE phase table: e^{i * t * theta_j} for positions t = 0 .. n_positions-1, stored as two levels,
- * fine[j][f] = e^{i f theta_j} (f < 64, pair-major) followed by coarse[c][j] = e^{i 64 c theta_j}
- * (c < ceil(n_positions / 64)), complex fp32 (re, im) interleaved, each entry computed in fp64 and
- * rounded once. The rotation of a key at position t is coarse[t >> 6][j] * fine[j][t & 63]
+ * RoPE phase table: e^{i * t * theta_j} for positions t = 0 .. n_positions-1, stored as two levels in
+ * three sections, each entry computed in fp64 and rounded once:
+ *   fine[j][f]   = e^{i f theta_j}, f < 64, pair-major, complex fp32 (re, im)        (32 KiB)
+ *   fine16[f][j] = the same phases, position-major, packed fp16 (re, im)            (16 KiB)
+ *   coarse[c][j] = e^{i 64 c theta_j}, c < ceil(n_positions / 64), complex fp32     (512 B per row)
+ * The rotation of a key at position t is coarse[t >> 6][j] * fine[j][t & 63]
  * ("pith.science verdict", key_machinery: the block-diagonal rotation R_m of each 2-D sub-vector).
  * It depends only on rope_base, head_dim and the longest position, like a model's RoPE cache:
  * build it once and pass it to every commvq_attn_decode call.
@@ -104,8 +108,8 @@ int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const
 /* ---------------------------------------------------------------------------------------------
  * Decode-step attention over the compressed cache. For every (b, h):
  *   s_t   = softmax_scale * sum_j Re( conj(q_j) * khat_{t,j} * e^{i t theta_j} ),  t < L_b
- *   khat_{t,j} = sum_r k_codebook[kv][g][r][k_codes[kv][seq_start[b]+t][r][g]][2u..2u+1]   (j = 4g+u)
- *   out[b][h] = sum_t softmax(s)_t * vhat_t,  vhat_t = sum_r v_codebook[kv][g][r][v_codes[..][r][g]]
+ *   khat_{t,j} = sum_r k_codebook[kv][g][r][k_codes[kv][r][seq_start[b]+t][g]][2u..2u+1]   (j = 4g+u)
+ *   out[b][h] = sum_t softmax(s)_t * vhat_t,  vhat_t = sum_r v_codebook[kv][g][r][v_codes[kv][r][..][g]]
  * No key or value is dequantized to memory. Sequences with L_b = 0 produce zeros.
  * rope_table: from commvq_rope_table with rope_positions >= max_len.
  * max_len (host) must be >= every seq_len[b], and seq_start[b] + seq_len[b] <= total_tokens (host),
@@ -138,8 +142,8 @@ int commvq_value_reduce(const commvq_dims* d /* host */, const float* p, const u
                         size_t ws_bytes /* host */, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Code unpack exactly as the attention kernels read codes: out[kv][t][r][g] = index (int32).
- * codes [Hkv][total_tokens][R][G] uint8. Used to test the unpack bit-exactly.
+ * Code unpack exactly as the attention kernels read codes: out[kv][r][t][g] = index (int32).
+ * codes [Hkv][R][total_tokens][G] uint8. Used to test the unpack bit-exactly.
  * ------------------------------------------------------------------------------------------- */
 int commvq_debug_unpack(const commvq_dims* d /* host */, const uint8_t* codes, int64_t total_tokens /* host */,
                         int32_t* out, void* stream);

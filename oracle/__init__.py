@@ -137,7 +137,7 @@ def attn_decode(d: Dims, q, k_codes, v_codes, k_cb, v_cb, seq_start, seq_len, ma
     kb, vb = _f64(k_cb), _f64(v_cb)
     ss = np.ascontiguousarray(seq_start, dtype=np.int64)
     sl = np.ascontiguousarray(seq_len, dtype=np.int32)
-    total = kc.shape[1]
+    total = kc.shape[2]
     if max_len is None:
         max_len = int(sl.max()) if sl.size else 0
     out = np.empty((d.batch, d.n_q_heads, d.head_dim), dtype=np.float64)
@@ -164,7 +164,7 @@ def scores_via_table(d: Dims, tab, k_codes, seq_start, seq_len, max_len: int) ->
     ss = np.ascontiguousarray(seq_start, dtype=np.int64)
     sl = np.ascontiguousarray(seq_len, dtype=np.int32)
     out = np.empty((d.batch, d.n_q_heads, max_len), dtype=np.float64)
-    lib().oracle_scores_via_table(ctypes.byref(d), _ptr(tt), _ptr(kc), _ptr(ss), _ptr(sl), kc.shape[1], int(max_len),
+    lib().oracle_scores_via_table(ctypes.byref(d), _ptr(tt), _ptr(kc), _ptr(ss), _ptr(sl), kc.shape[2], int(max_len),
                                   _ptr(out))
     return out
 
@@ -175,16 +175,16 @@ def value_reduce(d: Dims, p, v_codes, v_cb, seq_start, seq_len, max_len: int) ->
     ss = np.ascontiguousarray(seq_start, dtype=np.int64)
     sl = np.ascontiguousarray(seq_len, dtype=np.int32)
     out = np.empty((d.batch, d.n_q_heads, d.head_dim), dtype=np.float64)
-    lib().oracle_value_reduce(ctypes.byref(d), _ptr(pp), _ptr(vc), _ptr(vb), _ptr(ss), _ptr(sl), vc.shape[1],
+    lib().oracle_value_reduce(ctypes.byref(d), _ptr(pp), _ptr(vc), _ptr(vb), _ptr(ss), _ptr(sl), vc.shape[2],
                               int(max_len), _ptr(out))
     return out
 
 
 def encode_greedy(d: Dims, x, codebook, want_dist: bool = False):
-    """x [Hkv][n][D] in the codebook frame. Returns codes [Hkv][n][R][G] uint8 (and min distances)."""
+    """x [Hkv][n][D] in the codebook frame. Returns codes [Hkv][R][n][G] uint8 (and min distances)."""
     xx, cb = _f64(x), _f64(codebook)
     n = xx.shape[1]
-    codes = np.empty((d.n_kv_heads, n, d.n_residuals, d.n_groups), dtype=np.uint8)
+    codes = np.empty((d.n_kv_heads, d.n_residuals, n, d.n_groups), dtype=np.uint8)
     dist = np.empty(codes.shape, dtype=np.float64) if want_dist else None
     lib().oracle_encode_greedy(ctypes.byref(d), _ptr(xx), _ptr(cb), int(n), _ptr(codes),
                                _ptr(dist) if dist is not None else None)

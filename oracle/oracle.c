@@ -21,7 +21,8 @@
  * Every function is the plain definition, in fp64, with straight loops. Readings of points the
  * pages leave open (all listed in the design notes):
  *   - layout: head_dim D, G groups of W = D/G dims; a group holds W/2 RoPE pairs; pair j covers
- *     dims (2j, 2j+1); codes are bytes laid out [Hkv][T][R][G]; a codebook is [Hkv][G][R][N][W].
+ *     dims (2j, 2j+1); codes are bytes laid out [Hkv][R][T][G] (one plane of 16-byte token records per residual
+ *     codebook); a codebook is [Hkv][G][R][N][W].
  *   - a key codeword stores per pair the two numbers (a, b) of the block [[a,-b],[b,a]]; the
  *     decoded sub-vector is that block applied to e1, i.e. (a, b). [[x,y],[-y,x]] on [VER] is the
  *     same family with b = -y.
@@ -41,9 +42,9 @@ typedef struct {
   double rope_base, softmax_scale;
 } oracle_dims;
 
-/* index of code byte (kv, token, residual, group) in a [Hkv][T][R][G] byte array */
+/* index of code byte (kv, token, residual, group) in a [Hkv][R][T][G] byte array */
 static inline int64_t code_off(const oracle_dims* d, int64_t total_tokens, int kv, int64_t t, int r, int g) {
-  return (((int64_t)kv * total_tokens + t) * d->n_residuals + r) * d->n_groups + g;
+  return (((int64_t)kv * d->n_residuals + r) * total_tokens + t) * d->n_groups + g;
 }
 
 /* offset of codeword (kv, g, r, l) in a [Hkv][G][R][N][W] codebook */
@@ -52,7 +53,7 @@ static inline int64_t cw_off(const oracle_dims* d, int kv, int g, int r, int l) 
   return ((((int64_t)kv * d->n_groups + g) * d->n_residuals + r) * d->n_codes + l) * W;
 }
 
-/* Unpack: one byte per index (N = 256, 8 bits per index). out is int32 [Hkv][T][R][G]. */
+/* Unpack: one byte per index (N = 256, 8 bits per index). out is int32 [Hkv][R][T][G]. */
 void oracle_unpack(const oracle_dims* d, const uint8_t* codes, int64_t total_tokens, int32_t* out) {
   for (int kv = 0; kv < d->n_kv_heads; ++kv)
     for (int64_t t = 0; t < total_tokens; ++t)
@@ -337,7 +338,7 @@ void oracle_value_reduce(const oracle_dims* d, const double* p, const uint8_t* v
  * for each (kv, token, group), residual rounds r = 0..R-1 pick l* = argmin_l ||res - C[g][r][l]||^2
  * (ties to the lowest l) and subtract the chosen codeword ([VER] key_machinery: R residual rounds
  * refine the reconstruction). x [Hkv][T][D] (in the codebook's own frame, i.e. before RoPE);
- * codes_out [Hkv][T][R][G]; dist_out (optional) [Hkv][T][R][G] holds the minimum squared distance
+ * codes_out [Hkv][R][T][G]; dist_out (optional) [Hkv][R][T][G] holds the minimum squared distance
  * of each round. */
 void oracle_encode_greedy(const oracle_dims* d, const double* x, const double* codebook, int64_t n_tokens,
                           uint8_t* codes_out, double* dist_out) {

@@ -88,14 +88,21 @@ def test_misaligned_codes_rejected():
 
 
 def test_workspace_sizes():
+    # attention workspace: 256 B of arrival counters, then (m, l) per (sequence, q head, split) padded to
+    # 256 B, then o[128] fp32 per (sequence, q head, split). fp16 splits are 512 x blocks-per-wave tokens
+    # (8 waves x 64 tokens, blocks-per-wave 1..8), sized for about one work item per CU (256).
+    def attn_ws(B, Hq, splits):
+        items = B * Hq * splits
+        return 256 + (items * 8 + 255) // 256 * 256 + items * 128 * 4
     d = vq.make_dims(2, 32, 8, 1)
-    # attention: 256 B of arrival counters, then one partial of 132 floats per (sequence, q head, split);
-    # the split is 256 x blocks-per-wave tokens (<= 2048), sized for about 512 work items
-    assert vq.attn_decode_workspace_size(d, 131072) == 256 + 2 * 32 * 64 * 132 * 4   # 2048-token splits
-    assert vq.attn_decode_workspace_size(d, 1) == 256 + 2 * 32 * 1 * 132 * 4
+    assert vq.attn_decode_workspace_size(d, 131072) == attn_ws(2, 32, 32)   # 4096-token splits
+    assert vq.attn_decode_workspace_size(d, 1) == attn_ws(2, 32, 1)
     d1 = vq.make_dims(1, 32, 8, 2)
-    assert vq.attn_decode_workspace_size(d1, 8192) == 256 + 32 * 32 * 132 * 4          # 256-token splits
-    assert vq.attn_decode_workspace_size(d1, 131072) == 256 + 32 * 64 * 132 * 4       # 2048-token splits
+    assert vq.attn_decode_workspace_size(d1, 8192) == attn_ws(1, 32, 16)    # 512-token splits
+    assert vq.attn_decode_workspace_size(d1, 131072) == attn_ws(1, 32, 32)  # 4096-token splits
+    d32 = vq.make_dims(1, 4, 1, 2, dtype="float32")
+    assert vq.attn_decode_workspace_size(d32, 1024) == attn_ws(1, 4, 4)     # fp32: 4 waves, 256-token splits
     assert vq.value_reduce_workspace_size(d, 2048) == 2 * 32 * 2 * 132 * 4
-    assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (64 + 2048) * 64 * 8
+    # RoPE table: fine fp32 (64 x 64 x 8 B), fine fp16 (64 x 64 x 4 B), coarse (ceil(n/64) x 64 x 8 B)
+    assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (4096 + 2048 + 2048 * 64) * 8
     assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 0) == 0

@@ -147,13 +147,19 @@ def test_rope_table_matches_fp64(vq):
     announce("rope_table")
     d = vq.make_dims(1, 4, 1, 1)
     n = 131072 + 5
-    t = vq.rope_table(d, n).cpu().numpy().view(np.complex64).reshape(-1, 64)
+    raw = vq.rope_table(d, n).cpu().numpy()
     theta = 500000.0 ** (-np.arange(64) * 2.0 / 128)
-    fine = np.exp(1j * np.outer(np.arange(64), theta))
+    fine = np.exp(1j * np.outer(np.arange(64), theta))          # [f][j]
     coarse = np.exp(1j * np.outer(64.0 * np.arange((n + 63) // 64), theta))
-    assert t.shape[0] == 64 + coarse.shape[0]
-    assert np.abs(t[:64] - fine.T).max() < 1e-7  # fine part is pair-major: [j][f]
-    assert np.abs(t[64:] - coarse).max() < 1e-7
+    fine32 = raw[:8192].view(np.complex64).reshape(64, 64)       # pair-major [j][f]
+    fine16 = raw[8192:12288].view(np.float16).astype(np.float64).reshape(64, 64, 2)  # [f][j][re, im]
+    coarse32 = raw[12288:].view(np.complex64).reshape(-1, 64)
+    assert coarse32.shape[0] == coarse.shape[0]
+    assert np.abs(fine32 - fine.T).max() < 1e-7
+    assert np.abs(coarse32 - coarse).max() < 1e-7
+    # fp16 copy: each part rounded once from the fp64 phase (half an fp16 ulp at most)
+    assert np.all(np.abs(fine16[..., 0] - fine.real) <= 2.0 ** -12)
+    assert np.all(np.abs(fine16[..., 1] - fine.imag) <= 2.0 ** -12)
 
 
 def test_workspace_too_small_is_rejected(vq):

@@ -46,8 +46,8 @@ def small_inputs(B=1, Hq=4, Hkv=1, lengths=(37,), R=2, D=16, G=2, N=16, seed=0, 
     q = rng.standard_normal((B, Hq, D))
     kcb = rng.standard_normal((Hkv, G, R, N, W)) * 0.5
     vcb = rng.standard_normal((Hkv, G, R, N, W)) * 0.5
-    kc = rng.integers(0, N, size=(Hkv, T, R, G)).astype(np.uint8)
-    vc = rng.integers(0, N, size=(Hkv, T, R, G)).astype(np.uint8)
+    kc = rng.integers(0, N, size=(Hkv, R, T, G)).astype(np.uint8)
+    vc = rng.integers(0, N, size=(Hkv, R, T, G)).astype(np.uint8)
     return d, q, kcb, vcb, kc, vc, seq_start, seq_len
 
 
@@ -108,7 +108,7 @@ def test_rope_group_law_norm_identity_and_ladder(oracle_lib):
 def test_unpack_closed_form_pattern(oracle_lib):
     d = oracle.dims(1, 4, 3, 2)
     T = 70
-    kv, t, r, g = np.meshgrid(np.arange(3), np.arange(T), np.arange(2), np.arange(16), indexing="ij")
+    kv, r, t, g = np.meshgrid(np.arange(3), np.arange(2), np.arange(T), np.arange(16), indexing="ij")
     pat = ((kv * 7 + t * 3 + r * 5 + g * 11) % 256).astype(np.uint8)
     out = oracle.unpack(d, pat, T)
     assert out.dtype == np.int32
@@ -126,23 +126,23 @@ def test_decode_counting_codebook_reveals_indices(oracle_lib):
         cb[:, :, r, :, :] = (np.arange(N) * 256.0 ** r)[None, None, :, None]
     rng = np.random.default_rng(4)
     T = 33
-    codes = rng.integers(0, 256, size=(Hkv, T, R, G)).astype(np.uint8)
+    codes = rng.integers(0, 256, size=(Hkv, R, T, G)).astype(np.uint8)
     dec = oracle.decode(d, cb, codes, T)  # [Hkv][T][D]
     val = dec.reshape(Hkv, T, G, W)
     assert np.all(val == val[..., :1])
     v = val[..., 0].astype(np.int64)
-    np.testing.assert_array_equal(v % 256, codes[:, :, 0, :])
-    np.testing.assert_array_equal(v // 256, codes[:, :, 1, :])
+    np.testing.assert_array_equal(v % 256, codes[:, 0, :, :])
+    np.testing.assert_array_equal(v // 256, codes[:, 1, :, :])
 
 
 def test_decode_matches_numpy_gather(oracle_lib):
     d, q, kcb, vcb, kc, vc, ss, sl = small_inputs(Hkv=2, Hq=8, lengths=(41,), R=3)
-    T = kc.shape[1]
+    T = kc.shape[2]
     dec = oracle.decode(d, vcb, vc, T)
     Hkv, G, R, N, W = vcb.shape
     ref = np.zeros((Hkv, T, G, W))
     for r in range(R):
-        ref += vcb[np.arange(Hkv)[:, None, None], np.arange(G)[None, None, :], r, vc[:, :, r, :]]
+        ref += vcb[np.arange(Hkv)[:, None, None], np.arange(G)[None, None, :], r, vc[:, r, :, :]]
     np.testing.assert_allclose(dec, ref.reshape(Hkv, T, G * W), atol=1e-14)
 
 
@@ -203,7 +203,7 @@ def test_softmax_rows_sum_to_one_and_log_ratios(oracle_lib):
 def test_single_token_returns_its_decoded_value(oracle_lib):
     d, q, kcb, vcb, kc, vc, ss, sl = small_inputs(Hq=4, Hkv=1, lengths=(1,), R=2, D=128, G=16, N=256, seed=6)
     out = oracle.attn_decode(d, q, kc, vc, kcb, vcb, ss, sl)
-    v0 = sum(vcb[0, np.arange(16), r, vc[0, 0, r, :]] for r in range(2)).reshape(128)
+    v0 = sum(vcb[0, np.arange(16), r, vc[0, r, 0, :]] for r in range(2)).reshape(128)
     for h in range(4):
         np.testing.assert_allclose(out[0, h], v0, atol=1e-15)
 
@@ -216,7 +216,7 @@ def test_zero_query_gives_histogram_mean(oracle_lib):
     ref = np.zeros((16, 8))
     for g in range(16):
         for r in range(2):
-            cnt = np.bincount(vc[0, :, r, g], minlength=256)
+            cnt = np.bincount(vc[0, r, :, g], minlength=256)
             ref[g] += cnt @ vcb[0, g, r] / L
     for h in range(4):
         np.testing.assert_allclose(out[0, h], ref.reshape(128), atol=1e-14)
@@ -231,8 +231,8 @@ def test_hand_worked_two_token_example(oracle_lib):
     d = oracle.dims(1, 1, 1, 1, head_dim=4, n_groups=1, n_codes=2, rope_base=10000.0, softmax_scale=0.5)
     kcb = np.array([[1, 0, 0, 1], [0, 1, 1, 0]], dtype=np.float64).reshape(1, 1, 1, 2, 4)
     vcb = np.array([[1, 2, 3, 4], [5, 6, 7, 8]], dtype=np.float64).reshape(1, 1, 1, 2, 4)
-    kc = np.array([0, 1], dtype=np.uint8).reshape(1, 2, 1, 1)
-    vc = np.array([0, 1], dtype=np.uint8).reshape(1, 2, 1, 1)
+    kc = np.array([0, 1], dtype=np.uint8).reshape(1, 1, 2, 1)
+    vc = np.array([0, 1], dtype=np.uint8).reshape(1, 1, 2, 1)
     q = np.array([1, 0, 0, 0], dtype=np.float64).reshape(1, 1, 4)
     out = oracle.attn_decode(d, q, kc, vc, kcb, vcb, np.array([0]), np.array([2], dtype=np.int32))
     s0, s1 = 0.5, -math.sin(1.0) / 2
@@ -254,8 +254,8 @@ def test_matches_torch_sdpa_over_explicit_keys(oracle_lib):
     theta = cfg.rope_base ** (-np.arange(64) * 2.0 / 128)
     ph = np.exp(1j * np.outer(np.arange(L), theta))
     for kv in range(2):
-        K = sum(kcb[kv, np.arange(16)[None, :], r, kc[kv, :, r, :]] for r in range(2)).reshape(L, 128)
-        V = sum(vcb[kv, np.arange(16)[None, :], r, vc[kv, :, r, :]] for r in range(2)).reshape(L, 128)
+        K = sum(kcb[kv, np.arange(16)[None, :], r, kc[kv, r, :, :]] for r in range(2)).reshape(L, 128)
+        V = sum(vcb[kv, np.arange(16)[None, :], r, vc[kv, r, :, :]] for r in range(2)).reshape(L, 128)
         Kc = (K[:, 0::2] + 1j * K[:, 1::2]) * ph
         Kr = np.empty_like(K)
         Kr[:, 0::2], Kr[:, 1::2] = Kc.real, Kc.imag
@@ -285,8 +285,8 @@ def test_gqa_and_ragged_match_separate_runs(oracle_lib):
         s0, L = int(inp["seq_start"][b]), int(inp["seq_len"][b])
         for kv in range(2):
             d1 = oracle.dims(1, 4, 1, 2)
-            out = oracle.attn_decode(d1, inp["q"][b:b + 1, 4 * kv:4 * kv + 4], inp["k_codes"][kv:kv + 1, s0:s0 + L],
-                                     inp["v_codes"][kv:kv + 1, s0:s0 + L], inp["k_cb"][kv:kv + 1],
+            out = oracle.attn_decode(d1, inp["q"][b:b + 1, 4 * kv:4 * kv + 4], inp["k_codes"][kv:kv + 1, :, s0:s0 + L],
+                                     inp["v_codes"][kv:kv + 1, :, s0:s0 + L], inp["k_cb"][kv:kv + 1],
                                      inp["v_cb"][kv:kv + 1], np.array([0]), np.array([L], dtype=np.int32))
             np.testing.assert_array_equal(out[0], full[b, 4 * kv:4 * kv + 4])
 
@@ -303,7 +303,7 @@ def test_brute_force_loops_tiny(oracle_lib):
             for g in range(G):
                 for r in range(2):
                     for w in range(W):
-                        k[g * W + w] += kcb[0, g, r, kc[0, t, r, g], w]
+                        k[g * W + w] += kcb[0, g, r, kc[0, r, t, g], w]
             acc = 0.0
             for j in range(D // 2):
                 ang = t * 100.0 ** (-2.0 * j / D)
@@ -319,7 +319,7 @@ def test_brute_force_loops_tiny(oracle_lib):
             for g in range(G):
                 for r in range(2):
                     for w in range(W):
-                        o[g * W + w] += e[t] / z * vcb[0, g, r, vc[0, t, r, g], w]
+                        o[g * W + w] += e[t] / z * vcb[0, g, r, vc[0, r, t, g], w]
         np.testing.assert_allclose(out[0, h], o, atol=1e-14)
 
 
@@ -357,7 +357,7 @@ def test_encode_recovers_exact_codewords(oracle_lib):
     rng = np.random.default_rng(18)
     d = oracle.dims(1, 4, 2, 1)
     cb = rng.standard_normal((2, 16, 1, 256, 8))
-    codes = rng.integers(0, 256, size=(2, 40, 1, 16)).astype(np.uint8)
+    codes = rng.integers(0, 256, size=(2, 1, 40, 16)).astype(np.uint8)
     x = oracle.decode(d, cb, codes, 40)
     got, dist = oracle.encode_greedy(d, x, cb, want_dist=True)
     np.testing.assert_array_equal(got, codes)
@@ -375,8 +375,8 @@ def test_encode_brute_force_and_ties(oracle_lib):
     for t in range(30):
         for g in range(16):
             dd = ((x[0, t, g * 8:(g + 1) * 8][None, :] - cb[0, g, 0]) ** 2).sum(-1)
-            assert got[0, t, 0, g] == int(np.argmin(dd))
-            assert dist[0, t, 0, g] == pytest.approx(dd.min(), rel=1e-12, abs=1e-15)
+            assert got[0, 0, t, g] == int(np.argmin(dd))
+            assert dist[0, 0, t, g] == pytest.approx(dd.min(), rel=1e-12, abs=1e-15)
     assert got[0, 0, 0, 3] == 17
 
 
@@ -386,11 +386,11 @@ def test_encode_residual_rounds_do_not_increase_error(oracle_lib):
     cb = rng.standard_normal((1, 16, 3, 256, 8)) * np.array([0.5, 0.25, 0.125])[None, None, :, None, None]
     x = rng.standard_normal((1, 25, 128)) * 0.5
     codes, dist = oracle.encode_greedy(d, x, cb, want_dist=True)
-    assert np.all(np.diff(dist, axis=2) <= 1e-15)
+    assert np.all(np.diff(dist, axis=1) <= 1e-15)
     # the last round's distance is the squared error of the decoded reconstruction
     rec = oracle.decode(d, cb, codes, 25)
     err = ((x - rec) ** 2).reshape(1, 25, 16, 8).sum(-1)
-    np.testing.assert_allclose(dist[:, :, 2, :], err, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(dist[:, 2, :, :], err, rtol=1e-10, atol=1e-14)
 
 
 # ------------------------------------------------------------------------------------ page figures

@@ -179,7 +179,7 @@ def value_reduce(d: Dims, p, v_codes, v_codebook, seq_start, seq_len, max_len: i
 def debug_unpack(d: Dims, codes, total_tokens: int, out=None, stream=None):
     import torch
     if out is None:
-        out = torch.empty((d.n_kv_heads, int(total_tokens), d.n_residuals, d.n_groups), dtype=torch.int32,
+        out = torch.empty((d.n_kv_heads, d.n_residuals, int(total_tokens), d.n_groups), dtype=torch.int32,
                           device=codes.device)
     _check(lib().commvq_debug_unpack(ctypes.byref(d), _ptr(codes), int(total_tokens), _ptr(out), _stream(stream)),
            "debug_unpack")

@@ -60,19 +60,29 @@ int check_dims(const commvq_dims* d) {
 }
 
 size_t rope_bytes(int32_t n_positions) {
-  return static_cast<size_t>(kFineRows + rope_coarse_rows(n_positions)) * kPairs * sizeof(float2);
+  return (static_cast<size_t>(kRopeCoarseOffset) + static_cast<size_t>(rope_coarse_rows(n_positions)) * kPairs) *
+         sizeof(float2);
 }
 
 size_t part_bytes(const commvq_dims* d, int32_t max_len) {
   return static_cast<size_t>(d->batch) * d->n_q_heads * n_splits_for(max_len) * kPartFloats * sizeof(float);
 }
 
-// attention workspace: [arrival counters, padded to 256 B][partials B x Hq x n_splits x kPartFloats]
-size_t attn_ws_bytes(const commvq_dims* d, int32_t max_len) {
-  const int32_t S = attn_split_tokens(max_len, d->batch, d->n_kv_heads);
-  return attn_counter_bytes(d->batch, d->n_kv_heads) +
-         static_cast<size_t>(d->batch) * d->n_q_heads * attn_n_splits(max_len, S) * kPartFloats * sizeof(float);
+// attention workspace: [arrival counters, padded to 256 B][(m, l) per (b, q head, split), padded to 256 B]
+// [o[D] per (b, q head, split)]
+struct AttnWs {
+  size_t ml_offset, o_offset, bytes;
+};
+AttnWs attn_ws(const commvq_dims* d, int32_t max_len) {
+  const int32_t S = attn_split_tokens(d->dtype, max_len, d->batch, d->n_kv_heads);
+  const size_t items = static_cast<size_t>(d->batch) * d->n_q_heads * attn_n_splits(max_len, S);
+  AttnWs w;
+  w.ml_offset = attn_counter_bytes(d->batch, d->n_kv_heads);
+  w.o_offset = w.ml_offset + (items * sizeof(float2) + 255) / 256 * 256;
+  w.bytes = w.o_offset + items * kHeadDim * sizeof(float);
+  return w;
 }
+size_t attn_ws_bytes(const commvq_dims* d, int32_t max_len) { return attn_ws(d, max_len).bytes; }
 
 }  // namespace
 
@@ -139,7 +149,11 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(COMMVQ_EINVAL, "workspace must be 256-byte aligned");
   const size_t need = attn_ws_bytes(d, max_len);
   if (!workspace || ws_bytes < need) return fail(COMMVQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
-  const int32_t split_tokens = attn_split_tokens(max_len, d->batch, d->n_kv_heads);
+  const int32_t split_tokens = attn_split_tokens(d->dtype, max_len, d->batch, d->n_kv_heads);
+  if (attn_n_splits(max_len, split_tokens) > kAttnMaxSplits)
+    return fail(COMMVQ_EUNSUPPORTED, "max_len = %d needs more than %d splits of %d tokens", max_len, kAttnMaxSplits,
+                split_tokens);
+  const AttnWs w = attn_ws(d, max_len);
   AttnArgs a;
   a.q = q;
   a.k_codes = k_codes;
@@ -156,8 +170,8 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
   a.n_kv_heads = d->n_kv_heads;
   a.scale = d->softmax_scale;
   a.counters = static_cast<uint32_t*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
-                                    attn_counter_bytes(d->batch, d->n_kv_heads));
+  a.part_ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + w.ml_offset);
+  a.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + w.o_offset);
   a.out = out;
   return hip_status(launch_attn(d->dtype, d->n_residuals, d->batch, a, static_cast<hipStream_t>(stream)),
                     "attn_decode launch");

@@ -9,27 +9,30 @@
 // rotation, the rotation by position can be split freely between the query side and the key side; the
 // kernel puts the per-64-token part on the query (once per block) and the per-lane part on the keys.
 //
-// Work item: one workgroup (4 waves) per (sequence b, KV head, split of `split_tokens` tokens). Each wave
-// owns 64-token blocks; lane = token within the block, so the fine RoPE phase e^{i (t mod 64) theta_j}
-// is a per-lane constant held in registers (64 packed fp16 pairs).
+// Work item: one workgroup per (sequence b, KV head, split of `split_tokens` tokens), one workgroup per
+// CU (it owns the CU's LDS). Each wave owns 64-token blocks; lane = token within the block, so the fine
+// RoPE phase e^{i (t mod 64) theta_j} is a per-lane constant held in registers (64 packed fp16 pairs).
 //
-// Phases (K residual 0..R-1, then V residual 0..R-1), each over the whole split with the residual's 64 KiB
-// codebook in LDS, filled by direct global->LDS loads that overlap the phase's prefetch of code records
-// and coarse phases (two workgroups per CU, so one computes while the other waits on its loads):
+// Phases K residual 0..R-1, then V residual 0..R-1, each a pass over the split's blocks with that
+// residual's codebook (16 groups x 256 codes x 8 values) in LDS. fp16 storage keeps two 64 KiB codebook
+// slots: while a phase runs on one slot, the next phase's codebook streams into the other by direct
+// global->LDS loads, and the next phase's 16-byte code records stream into registers, so a phase
+// boundary is one workgroup barrier. fp32 storage uses one 128 KiB slot and loads between phases.
 //   K phase: gather the token's 16 codewords (one ds_read_b128 each), rotate them by the fine phase
 //            (2 packed-fp16 ops per pair), and form the 4 GQA head scores with v_mfma_f32_4x4x4_16b_f16:
 //            B = the token's rotated key (4 dims per step), A = the query rotated by the conjugate coarse
 //            phase of the block, broadcast from one 4-lane block (CBSZ/ABID) so each lane supplies only
 //            4 of the 64 query pairs. Scores accumulate across residuals in the MFMA accumulator.
-//   softmax: split max / sum over the workgroup; weights p = e^{s - m} in registers.
+//   softmax: per wave, m_w = max and l_w = sum of p = e^{s - m_w} over the wave's tokens; no barrier.
 //   V phase: gather value codewords, transpose each 4x4 (token x dim) tile of a lane quad with an
 //            identity-B MFMA, and accumulate p^T x v with the same 4x4x4 MFMA (the reduction over tokens
 //            runs inside each quad; the 16 quads are summed once at the end).
-// The workgroup writes (m, l, o[128]) per q head; the last workgroup of each (b, kv) (arrival counter in
-// the workspace, reset to zero by that workgroup) merges the splits and writes out.
+// The workgroup then combines its waves (rescaling wave w by e^{m_w - M}), writes (M, L, o[128]) per q
+// head, and the last workgroup of each (b, kv) (arrival counter in the workspace, reset to zero by that
+// workgroup) merges the splits and writes out.
 //
 // fp32 storage uses the same structure with each fp32 operand split into fp16 hi + lo parts (three MFMA
-// products per step), the fine phase read from the table, and a 128 KiB codebook buffer.
+// products per step) and the fine phase read from the fp32 table.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -46,7 +49,23 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = kAttnThreads / 64;
+// Per storage type: waves per workgroup and codebook slots in LDS.
+template <typename T>
+struct Shape;
+template <>
+struct Shape<f16> {
+  static constexpr int kWaves = 8, kSlots = 2;
+};
+template <>
+struct Shape<float> {
+  static constexpr int kWaves = 4, kSlots = 1;
+};
+
+constexpr int kMaxBlocks = kAttnMaxBlocksPerWave;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of this wave are outstanding
+// (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_at_most(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
 template <int ABID>
 __device__ __forceinline__ f4 mfma_bcast(h4 a, h4 b, f4 c) {
@@ -75,6 +94,33 @@ __device__ __forceinline__ Split2 split2(float x) {
   return {h, (f16)(x - (float)h)};
 }
 
+// s_waitcnt immediate that waits for all of this wave's LDS operations (lgkmcnt = 0) and nothing else.
+constexpr int kLgkmcnt0 = 0xf | (0x3 << 14) | (0x7 << 4);
+
+// Workgroup barriers that leave this wave's global loads in flight. __syncthreads() releases memory at
+// workgroup scope, which on this target waits for every outstanding vector-memory load of the wave,
+// including code records prefetched for later blocks (and a release that only covers LDS still waits
+// for them while a direct-to-LDS load is pending).
+// lds_barrier: LDS writes before it are visible to every wave after it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// slot_barrier: codebook slot hand-over. Each wave has already waited (vmcnt) for its own direct-to-LDS
+// loads into the slot being published; lgkmcnt(0) retires this wave's reads of the slot about to be
+// refilled. Nothing is written to LDS by ordinary stores across it, so no release is needed.
+__device__ __forceinline__ void slot_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// This lane's index in its wave, computed afresh rather than kept in a register since the kernel began.
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
 // Identity B operand: lane 4b+j holds e_j, so D_b = A_b (a quad transpose of A).
 __device__ __forceinline__ h4 identity_b(int lane) {
   const int j = lane & 3;
@@ -83,19 +129,20 @@ __device__ __forceinline__ h4 identity_b(int lane) {
 
 // ---------------------------------------------------------------------------------- per-group steps
 // Key step for group G of one 64-token block: gather, rotate, two MFMA steps (4 dims each).
+// F[G] holds the lane's fine phases of pairs 4G..4G+3 (packed fp16 (cos, sin) per pair).
 template <int G, typename T>
 struct KeyGroup;
 
 template <int G>
 struct KeyGroup<G, f16> {
-  __device__ __forceinline__ static void run(const unsigned char* tab, const uint4& code, const h2 (&F)[kPairs],
+  __device__ __forceinline__ static void run(const unsigned char* tab, const uint4& code, const uint4 (&F)[kGroups],
                                              const h4& A0, const h4& A1, f4& acc) {
     const uint32_t idx = code_index(code, G);
     const uint4 row = *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + idx * 16);
-    const h2 w0 = crot(as_h2(row.x), F[4 * G + 0]);
-    const h2 w1 = crot(as_h2(row.y), F[4 * G + 1]);
-    const h2 w2 = crot(as_h2(row.z), F[4 * G + 2]);
-    const h2 w3 = crot(as_h2(row.w), F[4 * G + 3]);
+    const h2 w0 = crot(as_h2(row.x), as_h2(F[G].x));
+    const h2 w1 = crot(as_h2(row.y), as_h2(F[G].y));
+    const h2 w2 = crot(as_h2(row.z), as_h2(F[G].z));
+    const h2 w3 = crot(as_h2(row.w), as_h2(F[G].w));
     const h4 A = (G < 8) ? A0 : A1;
     acc = mfma_bcast<(2 * G) & 15>(A, cat(w0, w1), acc);
     acc = mfma_bcast<(2 * G + 1) & 15>(A, cat(w2, w3), acc);
@@ -186,24 +233,38 @@ struct ValueGroup<G, float> {
   }
 };
 
-template <typename T, typename... Args, int... Gs>
-__device__ __forceinline__ void key_groups(std::integer_sequence<int, Gs...>, Args&&... args) {
-  (KeyGroup<Gs, T>::run(args...), ...);
+// A block's 16 groups run as two halves of 8 with a scheduling barrier between them, so at most 8
+// gathered rows (32 VGPRs) are in flight; the other wave on the SIMD covers the LDS latency at the seam.
+template <typename T, int Base, typename... Args, int... Gs>
+__device__ __forceinline__ void key_half(std::integer_sequence<int, Gs...>, Args&&... args) {
+  (KeyGroup<Base + Gs, T>::run(args...), ...);
 }
-template <typename T, typename... Args, int... Gs>
-__device__ __forceinline__ void value_groups(std::integer_sequence<int, Gs...>, Args&&... args) {
-  (ValueGroup<Gs, T>::run(args...), ...);
+template <typename T, int Base, typename... Args, int... Gs>
+__device__ __forceinline__ void value_half(std::integer_sequence<int, Gs...>, Args&&... args) {
+  (ValueGroup<Base + Gs, T>::run(args...), ...);
+}
+template <typename T, typename... Args>
+__device__ __forceinline__ void key_groups(Args&&... args) {
+  key_half<T, 0>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
+  __builtin_amdgcn_sched_barrier(0);
+  key_half<T, kGroups / 2>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
+}
+template <typename T, typename... Args>
+__device__ __forceinline__ void value_groups(Args&&... args) {
+  value_half<T, 0>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
+  __builtin_amdgcn_sched_barrier(0);
+  value_half<T, kGroups / 2>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
 }
 
-// Fill one phase's codebook table (16 groups x 256 codes, row = W values of T) in LDS with direct
-// global->LDS 16-byte loads; each wave moves its quarter. cb_kv points at codebook [kv][0][0][0][0].
-template <typename T, int R>
+// Fill one codebook slot (16 groups x 256 codes, row = 8 values of T) with direct global->LDS 16-byte
+// loads; each wave moves its share. cb_kv points at codebook [kv][0][0][0][0]; r selects the residual.
+template <typename T, int R, int kW>
 __device__ __forceinline__ void load_table(const T* cb_kv, int r, unsigned char* dst, int wave, int lane) {
   constexpr int kRowBytes = kGroupDim * sizeof(T);
   constexpr int kChunksPerRow = kRowBytes / 16;
   constexpr int kChunks = kGroups * kCodes * kChunksPerRow;
-  constexpr int kPerWave = kChunks / kWaves;
-#pragma unroll 4
+  constexpr int kPerWave = kChunks / kW;
+#pragma unroll
   for (int i = 0; i < kPerWave / 64; ++i) {
     const int c = wave * kPerWave + i * 64 + lane;
     const int rowi = c / kChunksPerRow, part = c % kChunksPerRow;
@@ -215,170 +276,270 @@ __device__ __forceinline__ void load_table(const T* cb_kv, int r, unsigned char*
   }
 }
 
-// row_ror DPP: lane l of each 16-lane row reads lane (l + n) mod 16 of the same row.
-template <int N>
-__device__ __forceinline__ float row_ror(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf,
-                                                               false));
-}
-
-constexpr int kMaxBlocks = kAttnMaxBlocksPerWave;
-
 template <typename T, int R>
-__global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ? 1 : 2))
-    attn_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnArgs a) {
   constexpr bool kF32 = std::is_same<T, float>::value;
-  constexpr int kRowBytes = kGroupDim * sizeof(T);
-  constexpr int kTableBytes = kGroups * kCodes * kRowBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kTableBytes];
-  __shared__ float red[2][kWaves][kGqa];
+  constexpr int kW = Shape<T>::kWaves;
+  constexpr int kThreads = kW * 64;
+  constexpr int kSlots = Shape<T>::kSlots;
+  constexpr int kTab = kGroups * kCodes * kGroupDim * static_cast<int>(sizeof(T));
+  constexpr int kPhases = 2 * R;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kSlots * kTab];
+  __shared__ float wave_ml[2][kW][kGqa];  // per wave and head: softmax max m_w and sum l_w
+  __shared__ float merge_den[kGqa];
   __shared__ int is_last;
 
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave values scalar
   const int L = a.seq_len[b];
   const int S = a.split_tokens;
   const int t0 = split * S;
   const int h0 = kv * kGqa;
-  float* out_bh = a.out + (static_cast<int64_t>(b) * a.n_q_heads + h0) * kHeadDim;
+  const int64_t bh0 = static_cast<int64_t>(b) * a.n_q_heads + h0;
+  float* out_bh = a.out + bh0 * kHeadDim;
   if (t0 >= L) {
     if (split == 0)  // empty sequence: the output is zero
-      for (int i = tid; i < kGqa * kHeadDim; i += kAttnThreads) out_bh[i] = 0.f;
+      for (int i = tid; i < kGqa * kHeadDim; i += kThreads) out_bh[i] = 0.f;
     return;
   }
   const int nvalid = min(S, L - t0);
   const int nblocks = (nvalid + 63) >> 6;
-  const int my_blocks = (nblocks - wave + kWaves - 1) / kWaves;  // blocks wave, wave+4, ...
+  const int my_blocks = (nblocks - wave + kW - 1) / kW;  // this wave owns blocks wave, wave + kW, ...
   const int64_t row_base = a.seq_start[b] + t0;
   const int64_t cb_stride = static_cast<int64_t>(kGroups) * R * kCodes * kGroupDim;
   const T* cb_k = static_cast<const T*>(a.k_cb) + kv * cb_stride;
   const T* cb_v = static_cast<const T*>(a.v_cb) + kv * cb_stride;
+  auto table_src = [&](int p) { return p < R ? cb_k : cb_v; };
 
-  // token row of block i for this lane, clamped into the split so every prefetch is in bounds
+  // token row of block i for this lane, clamped into the split so every load is in bounds
   auto token_row = [&](int i) -> int64_t {
-    const int tl = (wave + kWaves * i) * 64 + lane;
+    const int tl = (wave + kW * i) * 64 + lane;
     return row_base + min(tl, nvalid - 1);
   };
 
-  // query pairs this lane supplies to the broadcast A operand: head qi, pairs 2*quad + {0,1} (+32)
+  // ---------------------------------------------------------------------------------- prologue
+  // (1) register operands the first block needs: query pairs, coarse phases of every block, fine phases.
+  // Query pairs this lane supplies to the broadcast A operand: head qi, pairs 2*quad + {0,1} (+32).
   const int quad = lane >> 2, qi = lane & 3;
-  const T* qp = static_cast<const T*>(a.q) + (static_cast<int64_t>(b) * a.n_q_heads + h0 + qi) * kHeadDim;
-  float2 qv[4];
+  const T* qp = static_cast<const T*>(a.q) + (bh0 + qi) * kHeadDim;
+  // raw query pairs (converted after the prologue barrier): index 2m + e is pair 32m + 2 quad + e
+  typedef typename std::conditional<kF32, float2, uint32_t>::type QPair;
+  QPair qraw[4];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int j = 32 * m + 2 * quad + e;
-      qv[2 * m + e] = make_float2(static_cast<float>(qp[2 * j]), static_cast<float>(qp[2 * j + 1]));
-    }
-  const float2* coarse = a.rope + kFineRows * kPairs;
-  const float2* fine = a.rope + lane;  // fine[j * 64 + (t mod 64)], t mod 64 = lane: stride kFineRows per pair
-
-  f4 sc[kMaxBlocks];
+    for (int e = 0; e < 2; ++e) qraw[2 * m + e] = *reinterpret_cast<const QPair*>(qp + 2 * (32 * m + 2 * quad + e));
+  const float2* coarse = a.rope + kRopeCoarseOffset;
+  // Coarse phases of this lane's 4 query pairs (index 2m + e: pair 32m + 2 quad + e). fp32 storage: one
+  // row per block. fp16 storage: the row of the wave's first block and row 1 (e^{i 64 theta}), from
+  // which the per-block rotation steps follow (below).
+  constexpr int kCoarseRows = kF32 ? kMaxBlocks : 2;
+  float4 cphase[kCoarseRows][2];
 #pragma unroll
-  for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
-
-  // Code records of the current phase live in code[]; as soon as a block has consumed its record, the
-  // record of the same token for the next phase is requested, so the next phase's codes stream in while
-  // this phase computes (phases: K residual 0..R-1, then V residual 0..R-1).
+  for (int i = 0; i < kCoarseRows; ++i) {
+    // clamped rows: never past the sequence, so always inside the table
+    const int row = kF32 ? (t0 >> 6) + min(wave + kW * i, nblocks - 1) : (i == 0 ? (t0 >> 6) + wave : min(1, (L - 1) >> 6));
+    const float2* cr = coarse + static_cast<int64_t>(kF32 || i == 1 ? row : min(row, (L - 1) >> 6)) * kPairs;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) cphase[i][m] = *reinterpret_cast<const float4*>(cr + 32 * m + 2 * quad);
+  }
+  uint4 F[kGroups];  // fp16 storage: fine phases of pairs 4g..4g+3 at this lane's t mod 64 = lane
+  if constexpr (!kF32) {
+    const uint4* f16row = reinterpret_cast<const uint4*>(a.rope + kRopeFine16Offset) + lane * kGroups;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) F[g] = f16row[g];
+  }
+  const float2* fine = a.rope + lane;  // fp32 storage: fine[j * 64 + lane], read per group
+  __builtin_amdgcn_sched_barrier(0);
+  // (2) codebooks of the first phases, straight into LDS
+#pragma unroll
+  for (int p = 0; p < (kSlots < kPhases ? kSlots : kPhases); ++p)
+    load_table<T, R, kW>(table_src(p), p % R, lds + p * kTab, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+  // (3) code records of phase 0. Code records of the current phase live in code[]; once a block has
+  // consumed its record, the record of the same token for the next phase is requested. Every phase
+  // issues exactly kMaxBlocks record loads per wave (clamped rows), so a fixed vmcnt finds the codebook
+  // loads issued before them.
   uint4 code[kMaxBlocks];
   auto request_codes = [&](int ph, int i) {
     const uint8_t* base = ph < R ? a.k_codes : a.v_codes;
     code[i] = load_code_record(base, a.total_tokens, kv, token_row(i), R, ph % R);
   };
 #pragma unroll
-  for (int i = 0; i < kMaxBlocks; ++i)
-    if (i < my_blocks) request_codes(0, i);
+  for (int i = 0; i < kMaxBlocks; ++i) request_codes(0, i);
 
-  // ------------------------------------------------------------------------------ key phases
-  {
-    h2 F[kPairs];
-    if constexpr (!kF32) {
-#pragma unroll
-      for (int j = 0; j < kPairs; ++j) {
-        const float2 f = fine[j * kFineRows];
-        F[j] = (h2){(f16)f.x, (f16)f.y};
-      }
+  // Codebooks of phases 2 and 3 (fp16, R = 2) cannot be loaded up front (both slots are busy), so during
+  // phase p the codebook of phase p + 1 is staged through registers into the slot phase p - 1 used: one
+  // 16-byte row per thread per block, written to LDS one block later. (A direct global->LDS load here
+  // would make the compiler wait for it before every LDS read of the other slot.)
+  auto slot_of = [&](int p) { return lds + (p % kSlots) * kTab; };
+  auto staged = [](int p) { return kSlots == 2 && p >= 1 && p + 1 < kPhases; };
+  uint4 stage;
+  auto stage_load = [&](int pn, int i) {  // row i * kThreads + tid of phase pn's codebook
+    const int row = i * kThreads + tid, g = row >> 8, l = row & (kCodes - 1);
+    stage = *reinterpret_cast<const uint4*>(table_src(pn) + ((static_cast<int64_t>(g) * R + pn % R) * kCodes + l) *
+                                                                kGroupDim);
+  };
+  auto stage_store = [&](int pn, int i) {
+    *reinterpret_cast<uint4*>(slot_of(pn) + (i * kThreads + tid) * 16) = stage;
+  };
+  static_assert(kSlots == 1 || kTab / 16 == kMaxBlocks * kThreads, "one staged codebook row per thread per block");
+
+  // End of phase p: make the codebook of phase p + 1 resident and visible.
+  auto next_phase = [&](int p) {
+    if constexpr (kSlots == 2) {
+      if (staged(p)) stage_store(p + 1, kMaxBlocks - 1);
+      lds_barrier();  // codebook p+1 complete (prologue load or staged rows); every wave is done with slot p % 2
+    } else {
+      slot_barrier();  // every wave is done with the slot
+      load_table<T, R, kW>(table_src(p + 1), (p + 1) % R, lds, wave, lane);
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+      slot_barrier();
     }
-    // A operands: the query rotated by the conjugate coarse phase of each 64-token block,
-    // q'' = q * conj(C), in fp16 (fp32 inputs: hi and lo fp16 parts); the same for every key phase.
-    h4 Ah[kMaxBlocks][2], Al[kMaxBlocks][2];
+  };
+  // The first codebooks were issued before the kMaxBlocks code records, which the barrier keeps last.
+  // Nothing may wait on a loaded register between the codebook loads and this point: while a direct-to-
+  // LDS load is outstanding the compiler can only wait with vmcnt(0), which would include the records.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kMaxBlocks));
+  slot_barrier();
+  // Pin the query and coarse-phase registers here, so the arithmetic on them (and its wait for their
+  // loads) cannot be hoisted above the codebook loads.
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i) {
-      if (i < my_blocks) {
-        const float2* cr = coarse + static_cast<int64_t>((t0 + (wave + kWaves * i) * 64) >> 6) * kPairs;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const float4 c = *reinterpret_cast<const float4*>(cr + 32 * m + 2 * quad);
-          const float2 q0 = qv[2 * m], q1 = qv[2 * m + 1];
-          const float qq[4] = {q0.x * c.x + q0.y * c.y, q0.y * c.x - q0.x * c.y, q1.x * c.z + q1.y * c.w,
-                               q1.y * c.z - q1.x * c.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const Split2 sp = split2(qq[e]);
-            Ah[i][m][e] = sp.hi;
-            Al[i][m][e] = sp.lo;
-          }
-        }
-      }
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (kF32) {
+      asm volatile("" : "+v"(qraw[k].x), "+v"(qraw[k].y));
+    } else {
+      asm volatile("" : "+v"(qraw[k]));
     }
-    for (int r = 0; r < R; ++r) {
-      if (r > 0) __syncthreads();  // every wave is done with the previous table
-      load_table<T, R>(cb_k, r, lds, wave, lane);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+  }
 #pragma unroll
-      for (int i = 0; i < kMaxBlocks; ++i) {
-        if (i < my_blocks) {
-          if constexpr (!kF32) {
-            key_groups<f16>(std::make_integer_sequence<int, kGroups>{}, lds, code[i], F, Ah[i][0], Ah[i][1], sc[i]);
-          } else {
-            key_groups<float>(std::make_integer_sequence<int, kGroups>{}, lds, code[i], fine, Ah[i], Al[i], sc[i]);
-          }
-          request_codes(r + 1, i);
-        }
-      }
+  for (int i = 0; i < kCoarseRows; ++i)
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      asm volatile("" : "+v"(cphase[i][m].x), "+v"(cphase[i][m].y), "+v"(cphase[i][m].z), "+v"(cphase[i][m].w));
+  float2 qv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if constexpr (kF32) {
+      qv[k] = qraw[k];
+    } else {
+      const h2 hq = as_h2(qraw[k]);
+      qv[k] = make_float2(static_cast<float>(hq.x), static_cast<float>(hq.y));
     }
   }
 
-  // ------------------------------------------------------------------------------ split softmax
-  float m_h[kGqa], l_h[kGqa];
-  {
-    float mx[kGqa] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  // A operands: the query rotated by the conjugate coarse phase of each 64-token block,
+  // q'' = q * conj(C), in fp16 (fp32 inputs: hi and lo fp16 parts); the same for every key phase.
+  // fp32 storage computes all of them here. fp16 storage keeps q''_0 of the wave's first block and the
+  // step E = e^{i 64 kW theta} (row 1 squared log2(kW) times): the wave's blocks are kW rows apart, so
+  // q''_{i+1} = q''_i * conj(E). Seven fp32 steps stay far below the fp16 rounding of the operand.
+  h4 Ah[kF32 ? kMaxBlocks : 1][2], Al[kF32 ? kMaxBlocks : 1][2];
+  float2 qc0[4], stepE[4];
+  auto cmul_conj = [](float2 x, float2 c) { return make_float2(x.x * c.x + x.y * c.y, x.y * c.x - x.x * c.y); };
+  if constexpr (kF32) {
 #pragma unroll
     for (int i = 0; i < kMaxBlocks; ++i) {
-      const bool ok = i < my_blocks && (wave + kWaves * i) * 64 + lane < nvalid;
 #pragma unroll
-      for (int h = 0; h < kGqa; ++h) {
-        sc[i][h] = ok ? sc[i][h] * a.scale : -INFINITY;
-        mx[h] = fmaxf(mx[h], sc[i][h]);
+      for (int m = 0; m < 2; ++m) {
+        const float4 c = cphase[i][m];
+        const float2 u0 = cmul_conj(qv[2 * m], make_float2(c.x, c.y));
+        const float2 u1 = cmul_conj(qv[2 * m + 1], make_float2(c.z, c.w));
+        const float qq[4] = {u0.x, u0.y, u1.x, u1.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const Split2 sp = split2(qq[e]);
+          Ah[i][m][e] = sp.hi;
+          Al[i][m][e] = sp.lo;
+        }
       }
     }
+  } else {
+    static_assert((kW & (kW - 1)) == 0, "blocks of a wave are a power-of-two number of rows apart");
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) {
-      mx[h] = wave_max(mx[h]);
-      if (lane == 0) red[0][wave][h] = mx[h];
+    for (int m = 0; m < 2; ++m) {
+      const float4 c0 = cphase[0][m], c1 = cphase[1][m];
+      qc0[2 * m] = cmul_conj(qv[2 * m], make_float2(c0.x, c0.y));
+      qc0[2 * m + 1] = cmul_conj(qv[2 * m + 1], make_float2(c0.z, c0.w));
+      stepE[2 * m] = make_float2(c1.x, c1.y);
+      stepE[2 * m + 1] = make_float2(c1.z, c1.w);
     }
-    __syncthreads();
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h)
-      m_h[h] = fmaxf(fmaxf(red[0][0][h], red[0][1][h]), fmaxf(red[0][2][h], red[0][3][h]));
-    float sm[kGqa] = {0.f, 0.f, 0.f, 0.f};
+    for (int sq = 1; sq < kW; sq *= 2)
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i)
-#pragma unroll
-      for (int h = 0; h < kGqa; ++h) {
-        sc[i][h] = __expf(sc[i][h] - m_h[h]);  // masked tokens: exp(-inf) = 0
-        sm[h] += sc[i][h];
+      for (int k = 0; k < 4; ++k) {
+        const float2 e = stepE[k];
+        stepE[k] = make_float2(e.x * e.x - e.y * e.y, 2.f * e.x * e.y);
       }
+  }
+
+
+  // ------------------------------------------------------------------------------ key phases
+  f4 sc[kMaxBlocks];
+#pragma unroll
+  for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
+  // Residual phases are instantiated with compile-time r (straight-line code), so that every wait for a
+  // prefetched record is an exact vmcnt rather than a conservative one at a loop header.
+  auto key_phase = [&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    const unsigned char* tab = slot_of(r);
+    float2 cur[4];  // fp16 storage: q'' of the current block
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cur[k] = qc0[k];
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks; ++i) {
+      if constexpr (staged(r)) {
+        if (i > 0) stage_store(r + 1, i - 1);
+        stage_load(r + 1, i);
+      }
+      if (i < my_blocks) {
+        if constexpr (!kF32) {
+          const h4 A0 = {(f16)cur[0].x, (f16)cur[0].y, (f16)cur[1].x, (f16)cur[1].y};
+          const h4 A1 = {(f16)cur[2].x, (f16)cur[2].y, (f16)cur[3].x, (f16)cur[3].y};
+          key_groups<f16>(tab, code[i], F, A0, A1, sc[i]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
+        } else {
+          key_groups<float>(tab, code[i], fine, Ah[i], Al[i], sc[i]);
+        }
+      }
+      request_codes(r + 1, i);  // phase r + 1 always exists (the value phases follow)
+    }
+    if constexpr (r + 1 < R) next_phase(r);
+  };
+  key_phase(std::integral_constant<int, 0>{});
+  if constexpr (R > 1) key_phase(std::integral_constant<int, 1>{});
+
+  // ------------------------------------------------------------------------------ wave softmax
+  // m_w = max over the wave's valid tokens, p = e^{s - m_w}, l_w = sum p. A wave with no valid token
+  // has m_w = -inf, p = 0, l_w = 0, and weight e^{m_w - M} = 0 in the workgroup combine.
+  float m_w[kGqa], l_w[kGqa];
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks; ++i) {
+      const bool ok = i < my_blocks && (wave + kW * i) * 64 + lane < nvalid;
+      sc[i][h] = ok ? sc[i][h] * a.scale : -INFINITY;
+      mx = fmaxf(mx, sc[i][h]);
+    }
+    m_w[h] = wave_max(mx);
+    const float msafe = m_w[h] == -INFINITY ? 0.f : m_w[h];
+    float sm = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks; ++i) {
+      sc[i][h] = __expf(sc[i][h] - msafe);  // masked tokens: exp(-inf) = 0
+      sm += sc[i][h];
+    }
+    l_w[h] = wave_sum(sm);
+  }
+  if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) {
-      sm[h] = wave_sum(sm[h]);
-      if (lane == 0) red[1][wave][h] = sm[h];
+      wave_ml[0][wave][h] = m_w[h];
+      wave_ml[1][wave][h] = l_w[h];
     }
-    __syncthreads();  // also: every wave is done with the last key table
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h) l_h[h] = (red[1][0][h] + red[1][1][h]) + (red[1][2][h] + red[1][3][h]);
   }
 
   // p^T operands: lane 4b+j holds head j's weights for the 4 tokens of its quad (quad transpose)
@@ -404,29 +565,34 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
       }
     }
   }
+  next_phase(R - 1);
 
   // ------------------------------------------------------------------------------ value phases
   f4 O[2 * kGroups];
 #pragma unroll
   for (int c = 0; c < 2 * kGroups; ++c) O[c] = (f4){0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < R; ++r) {
-    if (r > 0) __syncthreads();
-    load_table<T, R>(cb_v, r, lds, wave, lane);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  auto value_phase = [&](auto rc) {
+    constexpr int r = decltype(rc)::value;
+    constexpr int p = R + r;
+    const unsigned char* tab = slot_of(p);
 #pragma unroll
     for (int i = 0; i < kMaxBlocks; ++i) {
-      if (i < my_blocks) {
-        value_groups<T>(std::make_integer_sequence<int, kGroups>{}, lds, code[i], ident, pth[i], ptl[i], O);
-        if (r + 1 < R) request_codes(R + r + 1, i);
+      if constexpr (staged(p)) {
+        if (i > 0) stage_store(p + 1, i - 1);
+        stage_load(p + 1, i);
       }
+      if (i < my_blocks)
+        value_groups<T>(tab, code[i], ident, pth[i], ptl[i], O);
+      if constexpr (r + 1 < R) request_codes(p + 1, i);
     }
-  }
+    if constexpr (r + 1 < R) next_phase(p);
+  };
+  value_phase(std::integral_constant<int, 0>{});
+  if constexpr (R > 1) value_phase(std::integral_constant<int, 1>{});
 
-  // ------------------------------------------------------------------------ workgroup reduction
-  // O[c] in lane 16*rho + 4*b' + j, register h: head h, dim 4c + j, summed over the tokens of quad b'.
-  // Sum the 4 quads of each 16-lane row with DPP, then the 4 rows and 4 waves through LDS.
-  __syncthreads();  // every wave is done with the value table; its space is reused below
+  auto epilogue = [&](const int lane, const int tid, f4 (&O)[2 * kGroups], const float (&m_w)[kGqa]) {
+  lds_barrier();  // every wave is done with the value codebooks; their space is reused below
+
   float* red_o = reinterpret_cast<float*>(lds);  // [wave][rho][j][c*4 + h]
 #pragma unroll
   for (int c = 0; c < 2 * kGroups; ++c)
@@ -443,25 +609,36 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
 #pragma unroll
     for (int c = 0; c < 2 * kGroups; ++c) *reinterpret_cast<f4*>(dst + c * 4) = O[c];
   }
-  __syncthreads();
-  const int64_t part_row = static_cast<int64_t>(a.n_splits) * kPartFloats;
-  float* part = a.part + ((static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits + split) * kPartFloats;
+  lds_barrier();
   // Partials are written with device-scope (agent) atomic stores, which write through to the device
   // coherence point, so no workgroup needs a device-wide release fence (on this chip that fence writes
   // back the whole L2 and costs far more than the stores). Once the stores have completed (vmcnt), the
   // arrival counter is bumped; the last workgroup to arrive merges.
+  const int64_t ns_alloc = a.n_splits;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int o = tid + kAttnThreads * k;  // (h, d)
+  for (int k = 0; k < kGqa * kHeadDim / kThreads; ++k) {
+    const int o = tid + kThreads * k;  // (h, d)
     const int h = o >> 7, d = o & 127, c = d >> 2, j = d & 3;
-    float acc = 0.f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int wr = 0; wr < 16; ++wr) acc += red_o[(wr * 4 + j) * (2 * kGroups * kGqa) + c * 4 + h];
-    __hip_atomic_store(part + h * part_row + 4 + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (tid < kGqa) {
-    __hip_atomic_store(part + tid * part_row + 0, m_h[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(part + tid * part_row + 1, l_h[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, wave_ml[0][w][h]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const float f = __expf(wave_ml[0][w][h] - M);  // 0 for a wave without tokens
+      float s = 0.f;
+#pragma unroll
+      for (int rho = 0; rho < 4; ++rho) s += red_o[((w * 4 + rho) * 4 + j) * (2 * kGroups * kGqa) + c * 4 + h];
+      acc = fmaf(f, s, acc);
+      lsum = fmaf(f, wave_ml[1][w][h], lsum);
+    }
+    const int64_t item = (bh0 + h) * ns_alloc + split;
+    __hip_atomic_store(a.part_o + item * kHeadDim + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      float* ml = reinterpret_cast<float*>(a.part_ml + item);
+      __hip_atomic_store(ml, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ml + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // ------------------------------------------------------------------------ last workgroup merges
@@ -476,40 +653,45 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
   __syncthreads();
   if (!is_last) return;
   // Only the merging workgroup pays for an acquire: drop any stale cached copy of the partials.
-  __threadfence();
-  const float* pb = a.part + (static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits * kPartFloats;
-  float* sw = reinterpret_cast<float*>(lds);  // [kGqa][n_splits] split weights e^{m_s - M}
-  __shared__ float merge_den[kGqa];
-  // one wave per head: max over splits, weights, denominator
-  {
-    const float* ph = pb + wave * part_row;
-    float mx = -INFINITY;
-    for (int s2 = lane; s2 < ns; s2 += 64) mx = fmaxf(mx, ph[s2 * kPartFloats]);
-    mx = wave_max(mx);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  float* sw = reinterpret_cast<float*>(lds);  // [kGqa][ns] split weights e^{m_s - M}
+  // waves 0..3, one per head: max over splits, weights, denominator
+  if (wave < kGqa) {
+    const float2* mlh = a.part_ml + (bh0 + wave) * ns_alloc;
+    const float2 ml0 = lane < ns ? mlh[lane] : make_float2(-INFINITY, 0.f);
+    float mx = ml0.x;
+    for (int s2 = lane + 64; s2 < ns; s2 += 64) mx = fmaxf(mx, mlh[s2].x);
+    mx = wave_max(mx);  // finite: split 0 of a non-empty sequence always has tokens
     float den = 0.f;
-    for (int s2 = lane; s2 < ns; s2 += 64) {
-      const float w = __expf(ph[s2 * kPartFloats] - mx);
-      sw[wave * a.n_splits + s2] = w;
-      den = fmaf(w, ph[s2 * kPartFloats + 1], den);
+    if (lane < ns) {
+      const float w = __expf(ml0.x - mx);
+      sw[wave * ns + lane] = w;
+      den = w * ml0.y;
+    }
+    for (int s2 = lane + 64; s2 < ns; s2 += 64) {
+      const float2 ml = mlh[s2];
+      const float w = __expf(ml.x - mx);
+      sw[wave * ns + s2] = w;
+      den = fmaf(w, ml.y, den);
     }
     den = wave_sum(den);
     if (lane == 0) merge_den[wave] = den;
   }
   __syncthreads();
-  // each thread merges 2 outputs; the split loop issues 16 independent loads per step
+  // each output sums over the splits; 16 independent loads per step
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int o = tid + kAttnThreads * k;
+  for (int k = 0; k < kGqa * kHeadDim / kThreads; ++k) {
+    const int o = tid + kThreads * k;
     const int h = o >> 7, d = o & 127;
-    const float* ph = pb + h * part_row + 4 + d;
-    const float* wh = sw + h * a.n_splits;
+    const float* ph = a.part_o + (bh0 + h) * ns_alloc * kHeadDim + d;
+    const float* wh = sw + h * ns;
     float acc[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u) acc[u] = 0.f;
     for (int s0 = 0; s0 < ns; s0 += 16) {
       float v[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = s0 + u < ns ? ph[(s0 + u) * kPartFloats] : 0.f;
+      for (int u = 0; u < 16; ++u) v[u] = s0 + u < ns ? ph[static_cast<int64_t>(s0 + u) * kHeadDim] : 0.f;
 #pragma unroll
       for (int u = 0; u < 16; ++u) acc[u] = fmaf(s0 + u < ns ? wh[s0 + u] : 0.f, v[u], acc[u]);
     }
@@ -519,6 +701,12 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
     out_bh[o] = num / merge_den[h];
   }
   if (tid == 0) __hip_atomic_store(a.counters + b * a.n_kv_heads + kv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // ------------------------------------------------------------------------ workgroup reduction
+  // O[c] in lane 16*rho + 4*b' + j, register h: head h, dim 4c + j, summed over the tokens of quad b'.
+  // Sum the 4 quads of each 16-lane row with DPP, then the 4 rows and the waves through LDS.
+  // (Lane and thread indices are recomputed here so that no index register lives across the phases.)
+  epilogue(lane_id(), wave * 64 + lane_id(), O, m_w);
 }
 
 }  // namespace
@@ -526,11 +714,13 @@ __global__ void __launch_bounds__(kAttnThreads, (std::is_same<T, float>::value ?
 hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv_heads, B);
   if (dtype == COMMVQ_F16) {
-    if (R == 1) attn_kernel<f16, 1><<<grid, kAttnThreads, 0, s>>>(a);
-    else attn_kernel<f16, 2><<<grid, kAttnThreads, 0, s>>>(a);
+    constexpr int kThreads = Shape<f16>::kWaves * 64;
+    if (R == 1) attn_kernel<f16, 1><<<grid, kThreads, 0, s>>>(a);
+    else attn_kernel<f16, 2><<<grid, kThreads, 0, s>>>(a);
   } else {
-    if (R == 1) attn_kernel<float, 1><<<grid, kAttnThreads, 0, s>>>(a);
-    else attn_kernel<float, 2><<<grid, kAttnThreads, 0, s>>>(a);
+    constexpr int kThreads = Shape<float>::kWaves * 64;
+    if (R == 1) attn_kernel<float, 1><<<grid, kThreads, 0, s>>>(a);
+    else attn_kernel<float, 2><<<grid, kThreads, 0, s>>>(a);
   }
   return hipGetLastError();
 }

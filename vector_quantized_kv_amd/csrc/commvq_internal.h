@@ -17,23 +17,33 @@ constexpr int kGqa = 4;         // q heads per KV head
 constexpr int kSplitTokens = 1024;  // value_reduce: tokens per (sequence, KV head) work item
 constexpr int kPartFloats = 132;    // per (b, q head, split): m, l, 2 pad, o[128]
 constexpr int kFineRows = 64;       // RoPE table: fine rows e^{i f theta}, f < 64
-constexpr int kAttnThreads = 256;   // attention workgroup: 4 waves
+// RoPE table sections, in float2 units: fine fp32 [j][f], fine packed fp16 [f][j] (4 bytes per entry),
+// coarse fp32 [c][j]
+constexpr int kRopeFine16Offset = kFineRows * kPairs;
+constexpr int kRopeCoarseOffset = kRopeFine16Offset + kFineRows * kPairs / 2;
 constexpr int kAttnMaxBlocksPerWave = 8;  // 64-token blocks per wave per split
 constexpr int kCounterBytes = 256;  // attention workspace head: per-(b, kv) arrival counters
+constexpr int kAttnMaxSplits = 8192;  // splits per sequence the last-workgroup merge can hold in LDS
+constexpr int kCUs = 256;             // compute units the split sizing aims to fill (one workgroup each)
+
+// Attention workgroup: fp16 storage runs 8 waves (two per SIMD) over two 64 KiB codebook slots; fp32
+// storage runs 4 waves over one 128 KiB slot. Either way one workgroup owns a CU's LDS.
+inline int attn_waves(int dtype) { return dtype == COMMVQ_F16 ? 8 : 4; }
 
 inline int64_t n_splits_for(int32_t max_len) {
   int64_t s = (static_cast<int64_t>(max_len) + kSplitTokens - 1) / kSplitTokens;
   return s > 0 ? s : 1;
 }
 
-// Attention split size: a multiple of 256 tokens (64 per wave-block, 4 waves), at most 2048, chosen so
-// that the grid holds about 512 (sequence, KV head, split) items: two workgroups per CU, all resident.
-inline int32_t attn_split_tokens(int32_t max_len, int32_t batch, int32_t n_kv_heads) {
+// Attention split size: waves x 64 tokens x blocks-per-wave (1..8), chosen so that the grid holds
+// about one (sequence, KV head, split) item per CU.
+inline int32_t attn_split_tokens(int dtype, int32_t max_len, int32_t batch, int32_t n_kv_heads) {
+  const int64_t wg_tokens = 64LL * attn_waves(dtype);
   const int64_t work = static_cast<int64_t>(max_len) * batch * n_kv_heads;
-  int64_t blocks_per_wave = (work + 512LL * kAttnThreads - 1) / (512LL * kAttnThreads);
+  int64_t blocks_per_wave = (work + kCUs * wg_tokens - 1) / (kCUs * wg_tokens);
   if (blocks_per_wave < 1) blocks_per_wave = 1;
   if (blocks_per_wave > kAttnMaxBlocksPerWave) blocks_per_wave = kAttnMaxBlocksPerWave;
-  return static_cast<int32_t>(blocks_per_wave * kAttnThreads);
+  return static_cast<int32_t>(blocks_per_wave * wg_tokens);
 }
 inline int64_t attn_n_splits(int32_t max_len, int32_t split_tokens) {
   int64_t s = (static_cast<int64_t>(max_len) + split_tokens - 1) / split_tokens;
@@ -61,7 +71,8 @@ struct AttnArgs {
   int32_t n_kv_heads;
   float scale;
   uint32_t* counters;  // [B][Hkv], zero between calls
-  float* part;         // [B][Hq][n_splits][kPartFloats]
+  float2* part_ml;     // [B][Hq][n_splits]: (m, l) of each split
+  float* part_o;       // [B][Hq][n_splits][D]: unnormalised output of each split
   float* out;
 };
 

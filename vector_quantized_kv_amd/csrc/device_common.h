@@ -15,22 +15,38 @@ __device__ __forceinline__ uint32_t code_index(const uint4& w, int g) {
   return (word >> ((g & 3) * 8)) & 0xffu;
 }
 
-// 16-byte code record of (kv head, token row, residual r) in a [Hkv][T][R][G] byte array.
+// 16-byte code record of (kv head, token row, residual r) in a [Hkv][R][T][G] byte array.
 __device__ __forceinline__ uint4 load_code_record(const uint8_t* codes, int64_t total_tokens, int kv, int64_t row,
                                                   int R, int r) {
-  return *reinterpret_cast<const uint4*>(codes + ((static_cast<int64_t>(kv) * total_tokens + row) * R + r) * 16);
+  return *reinterpret_cast<const uint4*>(codes + ((static_cast<int64_t>(kv) * R + r) * total_tokens + row) * 16);
 }
 
+// row_ror DPP: lane l of each 16-lane row reads lane (l + n) mod 16 of the same row.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf,
+                                                               false));
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Wave-wide reductions (all 64 lanes active): four row_ror DPP steps leave each 16-lane row's result in
+// every lane of the row; the four row results are then read as scalars. The result is wave-uniform.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<1>(v));
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 }  // namespace commvq

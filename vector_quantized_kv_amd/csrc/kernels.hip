@@ -23,25 +23,42 @@ __device__ __forceinline__ float ld(const T* p) {
 }
 
 // ------------------------------------------------------------------------------------ RoPE table
-__global__ void rope_table_kernel(double base, int64_t n_rows, float2* out) {
+// One thread per entry, over three sections: fine fp32 pair-major (entry j * 64 + f = e^{i f theta_j}),
+// fine packed fp16 position-major (entry f * 64 + j, (cos, sin) rounded once from fp64), coarse fp32
+// position-major (entry c * 64 + j = e^{i 64 c theta_j}).
+__global__ void rope_table_kernel(double base, int64_t n_coarse, float2* out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= n_rows * kPairs) return;
-  // fine part (first kFineRows * kPairs entries) is pair-major: entry j * 64 + f = e^{i f theta_j};
-  // coarse part is position-major: entry 64 * 64 + c * 64 + j = e^{i 64 c theta_j}
-  const bool fine_part = idx < static_cast<int64_t>(kFineRows) * kPairs;
-  const int64_t row = fine_part ? idx % kFineRows : idx / kPairs;
-  const int j = static_cast<int>(fine_part ? idx / kFineRows : idx % kPairs);
-  const double pos = fine_part ? static_cast<double>(row) : 64.0 * static_cast<double>(row - kFineRows);
+  constexpr int64_t kFine = static_cast<int64_t>(kFineRows) * kPairs;
+  if (idx >= 2 * kFine + n_coarse * kPairs) return;
+  int j;
+  double pos;
+  if (idx < kFine) {
+    j = static_cast<int>(idx / kFineRows);
+    pos = static_cast<double>(idx % kFineRows);
+  } else if (idx < 2 * kFine) {
+    j = static_cast<int>((idx - kFine) % kPairs);
+    pos = static_cast<double>((idx - kFine) / kPairs);
+  } else {
+    j = static_cast<int>((idx - 2 * kFine) % kPairs);
+    pos = 64.0 * static_cast<double>((idx - 2 * kFine) / kPairs);
+  }
   const double theta = pow(base, -2.0 * j / static_cast<double>(kHeadDim));
   double s, c;
   sincos(pos * theta, &s, &c);
-  out[idx] = make_float2(static_cast<float>(c), static_cast<float>(s));
+  if (idx < kFine) {
+    out[idx] = make_float2(static_cast<float>(c), static_cast<float>(s));
+  } else if (idx < 2 * kFine) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    reinterpret_cast<h2*>(out + kRopeFine16Offset)[idx - kFine] = (h2){static_cast<f16>(c), static_cast<f16>(s)};
+  } else {
+    out[kRopeCoarseOffset + (idx - 2 * kFine)] = make_float2(static_cast<float>(c), static_cast<float>(s));
+  }
 }
 
 hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hipStream_t s) {
-  const int64_t rows = kFineRows + rope_coarse_rows(n_positions);
-  const int64_t n = rows * kPairs;
-  rope_table_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(base, rows, table);
+  const int64_t n_coarse = rope_coarse_rows(n_positions);
+  const int64_t n = 2LL * kFineRows * kPairs + n_coarse * kPairs;
+  rope_table_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(base, n_coarse, table);
   return hipGetLastError();
 }
 

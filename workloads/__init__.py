@@ -7,8 +7,8 @@ Layouts (shared by every consumer):
   q        [B][Hq][D]              post-RoPE query, dtype = cfg.dtype (float16 or float32)
   k_cb     [Hkv][G][R][N][W]       key codebook: per RoPE pair of the group the block numbers (a, b)
   v_cb     [Hkv][G][R][N][W]       value codebook
-  k_codes  [Hkv][T][R][G] uint8    one byte per code index (N = 256)
-  v_codes  [Hkv][T][R][G] uint8
+  k_codes  [Hkv][R][T][G] uint8    one byte per code index (N = 256); one plane per residual
+  v_codes  [Hkv][R][T][G] uint8
   seq_start[B] int64, seq_len[B] int32: sequence b owns token rows seq_start[b] .. +seq_len[b]-1
 with D = head_dim, G = n_groups, W = D / G, R = n_residuals, N = n_codes, T = total tokens.
 
@@ -98,10 +98,10 @@ def make_inputs(cfg: Config, seed: Optional[int] = None) -> Dict[str, np.ndarray
     k_cb = (rng.standard_normal((Hkv, G, R, N, W), dtype=np.float32) * np.float32(0.5)).astype(dt)
     v_cb = (rng.standard_normal((Hkv, G, R, N, W), dtype=np.float32) * np.float32(0.5)).astype(dt)
     q = rng.standard_normal((B, Hq, D), dtype=np.float32).astype(dt)
-    k_codes = rng.integers(0, N, size=(Hkv, total, R, G), dtype=np.uint8) if N == 256 else \
-        rng.integers(0, N, size=(Hkv, total, R, G)).astype(np.uint8)
-    v_codes = rng.integers(0, N, size=(Hkv, total, R, G), dtype=np.uint8) if N == 256 else \
-        rng.integers(0, N, size=(Hkv, total, R, G)).astype(np.uint8)
+    k_codes = rng.integers(0, N, size=(Hkv, R, total, G), dtype=np.uint8) if N == 256 else \
+        rng.integers(0, N, size=(Hkv, R, total, G)).astype(np.uint8)
+    v_codes = rng.integers(0, N, size=(Hkv, R, total, G), dtype=np.uint8) if N == 256 else \
+        rng.integers(0, N, size=(Hkv, R, total, G)).astype(np.uint8)
     return dict(q=q, k_cb=k_cb, v_cb=v_cb, k_codes=k_codes, v_codes=v_codes, seq_start=seq_start,
                 seq_len=seq_len, total_tokens=np.int64(total), max_len=np.int32(max(lengths) if lengths else 0))
 
