@@ -152,7 +152,8 @@ def test_rope_table_matches_fp64(vq):
     fine = np.exp(1j * np.outer(np.arange(64), theta))          # [f][j]
     coarse = np.exp(1j * np.outer(64.0 * np.arange((n + 63) // 64), theta))
     fine32 = raw[:8192].view(np.complex64).reshape(64, 64)       # pair-major [j][f]
-    fine16 = raw[8192:12288].view(np.float16).astype(np.float64).reshape(64, 64, 2)  # [f][j][re, im]
+    f16 = raw[8192:12288].view(np.float16).astype(np.float64).reshape(16, 64, 4, 2)  # [g][f][u][re, im]
+    fine16 = f16.transpose(1, 0, 2, 3).reshape(64, 64, 2)                         # [f][j = 4g + u][re, im]
     coarse32 = raw[12288:].view(np.complex64).reshape(-1, 64)
     assert coarse32.shape[0] == coarse.shape[0]
     assert np.abs(fine32 - fine.T).max() < 1e-7

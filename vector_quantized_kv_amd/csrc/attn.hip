@@ -136,7 +136,8 @@ struct KeyGroup;
 template <int G>
 struct KeyGroup<G, f16> {
   __device__ __forceinline__ static void run(const unsigned char* tab, const uint4& code, const uint4 (&F)[kGroups],
-                                             const h4& A0, const h4& A1, f4& acc) {
+                                             const h4& A0, const h4& A1, f4& acc_even, f4& acc_odd) {
+    f4& acc = (G & 1) ? acc_odd : acc_even;  // two independent MFMA accumulation chains
     const uint32_t idx = code_index(code, G);
     const uint4 row = *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + idx * 16);
     const h2 w0 = crot(as_h2(row.x), as_h2(F[G].x));
@@ -285,8 +286,8 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   constexpr int kTab = kGroups * kCodes * kGroupDim * static_cast<int>(sizeof(T));
   constexpr int kPhases = 2 * R;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kSlots * kTab];
+  __shared__ __attribute__((aligned(16))) uint4 fine_lds[kF32 ? 1 : kGroups * kFineRows];  // fp16 fine phases
   __shared__ float wave_ml[2][kW][kGqa];  // per wave and head: softmax max m_w and sum l_w
-  __shared__ float merge_den[kGqa];
   __shared__ int is_last;
 
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
@@ -344,14 +345,20 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 #pragma unroll
     for (int m = 0; m < 2; ++m) cphase[i][m] = *reinterpret_cast<const float4*>(cr + 32 * m + 2 * quad);
   }
-  uint4 F[kGroups];  // fp16 storage: fine phases of pairs 4g..4g+3 at this lane's t mod 64 = lane
-  if constexpr (!kF32) {
-    const uint4* f16row = reinterpret_cast<const uint4*>(a.rope + kRopeFine16Offset) + lane * kGroups;
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) F[g] = f16row[g];
-  }
   const float2* fine = a.rope + lane;  // fp32 storage: fine[j * 64 + lane], read per group
   __builtin_amdgcn_sched_barrier(0);
+  // (2a) fp16 storage: the group-major packed-fp16 fine phases (16 KiB) once per workgroup into LDS;
+  // every wave then reads its lane's 64 phases from there (instead of 8 waves loading the same table)
+  if constexpr (!kF32) {
+    constexpr int kFineChunks = kGroups * kFineRows;  // 16-byte entries
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine16Offset);
+#pragma unroll
+    for (int i = 0; i < kFineChunks / kThreads; ++i) {
+      const int c = (wave * (kFineChunks / kThreads) + i) * 64;
+      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, reinterpret_cast<unsigned char*>(fine_lds) + c * 16, 16,
+                                       0, 0);
+    }
+  }
   // (2) codebooks of the first phases, straight into LDS
 #pragma unroll
   for (int p = 0; p < (kSlots < kPhases ? kSlots : kPhases); ++p)
@@ -390,6 +397,9 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   auto next_phase = [&](int p) {
     if constexpr (kSlots == 2) {
       if (staged(p)) stage_store(p + 1, kMaxBlocks - 1);
+      // Codebook p+1 came with the prologue and slot p % 2 is never refilled (R = 1): each wave moves on
+      // without waiting for the others.
+      if (p + 1 < kSlots && p + 2 >= kPhases) return;
       lds_barrier();  // codebook p+1 complete (prologue load or staged rows); every wave is done with slot p % 2
     } else {
       slot_barrier();  // every wave is done with the slot
@@ -404,6 +414,11 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kMaxBlocks));
   slot_barrier();
+  uint4 F[kGroups];  // fp16 storage: fine phases of pairs 4g..4g+3 at this lane's t mod 64 = lane
+  if constexpr (!kF32) {
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) F[g] = fine_lds[g * kFineRows + lane];
+  }
   // Pin the query and coarse-phase registers here, so the arithmetic on them (and its wait for their
   // loads) cannot be hoisted above the codebook loads.
 #pragma unroll
@@ -497,7 +512,9 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
         if constexpr (!kF32) {
           const h4 A0 = {(f16)cur[0].x, (f16)cur[0].y, (f16)cur[1].x, (f16)cur[1].y};
           const h4 A1 = {(f16)cur[2].x, (f16)cur[2].y, (f16)cur[3].x, (f16)cur[3].y};
-          key_groups<f16>(tab, code[i], F, A0, A1, sc[i]);
+          f4 odd = {0.f, 0.f, 0.f, 0.f};
+          key_groups<f16>(tab, code[i], F, A0, A1, sc[i], odd);
+          sc[i] += odd;
 #pragma unroll
           for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
         } else {
@@ -593,21 +610,23 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   auto epilogue = [&](const int lane, const int tid, f4 (&O)[2 * kGroups], const float (&m_w)[kGqa]) {
   lds_barrier();  // every wave is done with the value codebooks; their space is reused below
 
-  float* red_o = reinterpret_cast<float*>(lds);  // [wave][rho][j][c*4 + h]
+  // red_o [wave][rho][d = 4c + j][h]: the 4 writing lanes of each 16-lane group store adjacent 16-byte
+  // entries, and the readers (one (h, d) each) walk consecutive entries, so neither side has bank conflicts.
+  float* red_o = reinterpret_cast<float*>(lds);
+  // two full passes, so every DPP source was written long before and each step is one v_add_f32_dpp
 #pragma unroll
   for (int c = 0; c < 2 * kGroups; ++c)
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) {
-      float v = O[c][h];
-      v += row_ror<8>(v);
-      v += row_ror<4>(v);
-      O[c][h] = v;
-    }
+    for (int h = 0; h < kGqa; ++h) O[c][h] += row_ror<8>(O[c][h]);
+#pragma unroll
+  for (int c = 0; c < 2 * kGroups; ++c)
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) O[c][h] += row_ror<4>(O[c][h]);
   if ((lane & 15) < 4) {
     const int rho = lane >> 4, j = lane & 3;
-    float* dst = red_o + ((wave * 4 + rho) * 4 + j) * (2 * kGroups * kGqa);
+    f4* dst = reinterpret_cast<f4*>(red_o) + (wave * 4 + rho) * kHeadDim + j;
 #pragma unroll
-    for (int c = 0; c < 2 * kGroups; ++c) *reinterpret_cast<f4*>(dst + c * 4) = O[c];
+    for (int c = 0; c < 2 * kGroups; ++c) dst[4 * c] = O[c];
   }
   lds_barrier();
   // Partials are written with device-scope (agent) atomic stores, which write through to the device
@@ -618,7 +637,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 #pragma unroll
   for (int k = 0; k < kGqa * kHeadDim / kThreads; ++k) {
     const int o = tid + kThreads * k;  // (h, d)
-    const int h = o >> 7, d = o & 127, c = d >> 2, j = d & 3;
+    const int h = o >> 7, d = o & 127;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kW; ++w) M = fmaxf(M, wave_ml[0][w][h]);
@@ -628,7 +647,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
       const float f = __expf(wave_ml[0][w][h] - M);  // 0 for a wave without tokens
       float s = 0.f;
 #pragma unroll
-      for (int rho = 0; rho < 4; ++rho) s += red_o[((w * 4 + rho) * 4 + j) * (2 * kGroups * kGqa) + c * 4 + h];
+      for (int rho = 0; rho < 4; ++rho) s += red_o[((w * 4 + rho) * kHeadDim + d) * kGqa + h];
       acc = fmaf(f, s, acc);
       lsum = fmaf(f, wave_ml[1][w][h], lsum);
     }
@@ -652,53 +671,50 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   }
   __syncthreads();
   if (!is_last) return;
-  // Only the merging workgroup pays for an acquire: drop any stale cached copy of the partials.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  float* sw = reinterpret_cast<float*>(lds);  // [kGqa][ns] split weights e^{m_s - M}
-  // waves 0..3, one per head: max over splits, weights, denominator
-  if (wave < kGqa) {
-    const float2* mlh = a.part_ml + (bh0 + wave) * ns_alloc;
-    const float2 ml0 = lane < ns ? mlh[lane] : make_float2(-INFINITY, 0.f);
-    float mx = ml0.x;
-    for (int s2 = lane + 64; s2 < ns; s2 += 64) mx = fmaxf(mx, mlh[s2].x);
-    mx = wave_max(mx);  // finite: split 0 of a non-empty sequence always has tokens
-    float den = 0.f;
-    if (lane < ns) {
-      const float w = __expf(ml0.x - mx);
-      sw[wave * ns + lane] = w;
-      den = w * ml0.y;
-    }
-    for (int s2 = lane + 64; s2 < ns; s2 += 64) {
-      const float2 ml = mlh[s2];
-      const float w = __expf(ml.x - mx);
-      sw[wave * ns + s2] = w;
-      den = fmaf(w, ml.y, den);
-    }
-    den = wave_sum(den);
-    if (lane == 0) merge_den[wave] = den;
-  }
-  __syncthreads();
-  // each output sums over the splits; 16 independent loads per step
+  // The partials are read with device-scope (agent) loads, which read through to the coherence point the
+  // partial stores wrote through to; this replaces an acquire fence, which on this chip invalidates the
+  // whole L2.
+  // Each thread owns outputs (h, d) and combines the splits itself: per chunk of splits it issues every
+  // load at once (its partial o_s[d] and the head's (m_s, l_s)), so a chunk costs one memory round trip;
+  // a running maximum rescales earlier chunks (one chunk covers up to 32 splits, 128K tokens).
+  constexpr int kChunk = 32;
+  constexpr int kOut = kGqa * kHeadDim / kThreads;
 #pragma unroll
-  for (int k = 0; k < kGqa * kHeadDim / kThreads; ++k) {
+  for (int k = 0; k < kOut; ++k) {
     const int o = tid + kThreads * k;
     const int h = o >> 7, d = o & 127;
-    const float* ph = a.part_o + (bh0 + h) * ns_alloc * kHeadDim + d;
-    const float* wh = sw + h * ns;
-    float acc[16];
+    const float* po = a.part_o + (bh0 + h) * ns_alloc * kHeadDim + d;
+    const float2* pml = a.part_ml + (bh0 + h) * ns_alloc;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += kChunk) {
+      float v[kChunk];
+      float2 ml[kChunk];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 16) {
-      float v[16];
+      for (int u = 0; u < kChunk; ++u) {
+        const bool ok = s0 + u < ns;
+        const float* pm = reinterpret_cast<const float*>(pml + s0 + u);
+        v[u] = ok ? __hip_atomic_load(po + static_cast<int64_t>(s0 + u) * kHeadDim, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT)
+                  : 0.f;
+        ml[u] = ok ? make_float2(__hip_atomic_load(pm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                 __hip_atomic_load(pm + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                   : make_float2(-INFINITY, 0.f);
+      }
+      float mc = M;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = s0 + u < ns ? ph[static_cast<int64_t>(s0 + u) * kHeadDim] : 0.f;
+      for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, ml[u].x);  // finite: split 0 always has tokens
+      const float r = __expf(M - mc);  // 0 on the first chunk
+      num *= r;
+      den *= r;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) acc[u] = fmaf(s0 + u < ns ? wh[s0 + u] : 0.f, v[u], acc[u]);
+      for (int u = 0; u < kChunk; ++u) {
+        const float w = __expf(ml[u].x - mc);  // 0 past the last split
+        num = fmaf(w, v[u], num);
+        den = fmaf(w, ml[u].y, den);
+      }
+      M = mc;
     }
-    float num = 0.f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) num += acc[u];
-    out_bh[o] = num / merge_den[h];
+    out_bh[o] = num / den;
   }
   if (tid == 0) __hip_atomic_store(a.counters + b * a.n_kv_heads + kv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };

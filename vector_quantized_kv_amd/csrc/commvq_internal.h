@@ -17,7 +17,8 @@ constexpr int kGqa = 4;         // q heads per KV head
 constexpr int kSplitTokens = 1024;  // value_reduce: tokens per (sequence, KV head) work item
 constexpr int kPartFloats = 132;    // per (b, q head, split): m, l, 2 pad, o[128]
 constexpr int kFineRows = 64;       // RoPE table: fine rows e^{i f theta}, f < 64
-// RoPE table sections, in float2 units: fine fp32 [j][f], fine packed fp16 [f][j] (4 bytes per entry),
+// RoPE table sections, in float2 units: fine fp32 [j][f], fine packed fp16 [g][f][u] with j = 4g + u
+// (4 bytes per entry),
 // coarse fp32 [c][j]
 constexpr int kRopeFine16Offset = kFineRows * kPairs;
 constexpr int kRopeCoarseOffset = kRopeFine16Offset + kFineRows * kPairs / 2;

@@ -21,11 +21,13 @@ __device__ __forceinline__ uint4 load_code_record(const uint8_t* codes, int64_t 
   return *reinterpret_cast<const uint4*>(codes + ((static_cast<int64_t>(kv) * R + r) * total_tokens + row) * 16);
 }
 
-// row_ror DPP: lane l of each 16-lane row reads lane (l + n) mod 16 of the same row.
+// row_ror DPP: lane l of each 16-lane row reads lane (l + n) mod 16 of the same row. Every source lane
+// exists, so bound_ctrl is irrelevant to the result; setting it lets the compiler fold the move into the
+// consuming add or max.
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf,
-                                                               false));
+                                                               true));
 }
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));

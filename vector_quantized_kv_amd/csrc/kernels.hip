@@ -24,8 +24,8 @@ __device__ __forceinline__ float ld(const T* p) {
 
 // ------------------------------------------------------------------------------------ RoPE table
 // One thread per entry, over three sections: fine fp32 pair-major (entry j * 64 + f = e^{i f theta_j}),
-// fine packed fp16 position-major (entry f * 64 + j, (cos, sin) rounded once from fp64), coarse fp32
-// position-major (entry c * 64 + j = e^{i 64 c theta_j}).
+// fine packed fp16 group-major (entry (g * 64 + f) * 4 + u for pair j = 4g + u, (cos, sin) rounded once
+// from fp64), coarse fp32 position-major (entry c * 64 + j = e^{i 64 c theta_j}).
 __global__ void rope_table_kernel(double base, int64_t n_coarse, float2* out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   constexpr int64_t kFine = static_cast<int64_t>(kFineRows) * kPairs;
@@ -36,8 +36,9 @@ __global__ void rope_table_kernel(double base, int64_t n_coarse, float2* out) {
     j = static_cast<int>(idx / kFineRows);
     pos = static_cast<double>(idx % kFineRows);
   } else if (idx < 2 * kFine) {
-    j = static_cast<int>((idx - kFine) % kPairs);
-    pos = static_cast<double>((idx - kFine) / kPairs);
+    const int k = static_cast<int>(idx - kFine);
+    j = 4 * (k >> 8) + (k & 3);
+    pos = static_cast<double>((k >> 2) & 63);
   } else {
     j = static_cast<int>((idx - 2 * kFine) % kPairs);
     pos = 64.0 * static_cast<double>((idx - 2 * kFine) / kPairs);
