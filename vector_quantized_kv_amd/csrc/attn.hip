@@ -121,6 +121,16 @@ __device__ __forceinline__ void slot_barrier() {
 // This lane's index in its wave, computed afresh rather than kept in a register since the kernel began.
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
+// Transposing LDS read (ds_read_b64_tr_b16): every lane names 8 bytes (4 fp16 values) of LDS; within each
+// 16-lane group, lane 4a + e receives value e of the loads named by lanes a, a + 4, a + 8 and a + 12 (in
+// that order). For MFMA block b = 4g + a of the 4x4x4 instruction, that is a 4x4 transpose: B_b[k][e]
+// is value e of source lane 16g + 4k + a.
+__device__ __forceinline__ h4 lds_read_tr(const void* p) {
+  typedef short s4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s4 lds_s4;
+  return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p)));
+}
+
 // Identity B operand: lane 4b+j holds e_j, so D_b = A_b (a quad transpose of A).
 __device__ __forceinline__ h4 identity_b(int lane) {
   const int j = lane & 3;
@@ -234,27 +244,110 @@ struct ValueGroup<G, float> {
   }
 };
 
-// A block's 16 groups run as two halves of 8 with a scheduling barrier between them, so at most 8
-// gathered rows (32 VGPRs) are in flight; the other wave on the SIMD covers the LDS latency at the seam.
+// ------------------------------------------------------- fp16: explicitly pipelined block processing
+// A block's 16 groups are processed in quarters of 4. The 4 codeword gathers of the next quarter (or of
+// the next block's first quarter) are issued in a scheduling region ahead of the current quarter's
+// arithmetic, so each wave keeps 4 LDS reads in flight while it rotates and multiplies.
+template <int G>
+__device__ __forceinline__ uint4 gather_row(const unsigned char* tab, const uint4& code) {
+  return *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + code_index(code, G) * 16);
+}
+template <int Q>
+__device__ __forceinline__ void gather_quarter(const unsigned char* tab, const uint4& code, uint4 (&buf)[4]) {
+  buf[0] = gather_row<4 * Q + 0>(tab, code);
+  buf[1] = gather_row<4 * Q + 1>(tab, code);
+  buf[2] = gather_row<4 * Q + 2>(tab, code);
+  buf[3] = gather_row<4 * Q + 3>(tab, code);
+}
+// key step of group G from its gathered row: rotate by the fine phase, two MFMA steps
+template <int G>
+__device__ __forceinline__ void key_step(const uint4& row, const uint4 (&F)[kGroups], const h4& A0, const h4& A1,
+                                         f4& acc) {
+  const h2 w0 = crot(as_h2(row.x), as_h2(F[G].x));
+  const h2 w1 = crot(as_h2(row.y), as_h2(F[G].y));
+  const h2 w2 = crot(as_h2(row.z), as_h2(F[G].z));
+  const h2 w3 = crot(as_h2(row.w), as_h2(F[G].w));
+  const h4 A = (G < 8) ? A0 : A1;
+  acc = mfma_bcast<(2 * G) & 15>(A, cat(w0, w1), acc);
+  acc = mfma_bcast<(2 * G + 1) & 15>(A, cat(w2, w3), acc);
+}
+template <int Q>
+__device__ __forceinline__ void key_quarter(const uint4 (&buf)[4], const uint4 (&F)[kGroups], const h4& A0,
+                                            const h4& A1, f4& acc_even, f4& acc_odd) {
+  key_step<4 * Q + 0>(buf[0], F, A0, A1, acc_even);  // two independent MFMA accumulation chains
+  key_step<4 * Q + 1>(buf[1], F, A0, A1, acc_odd);
+  key_step<4 * Q + 2>(buf[2], F, A0, A1, acc_even);
+  key_step<4 * Q + 3>(buf[3], F, A0, A1, acc_odd);
+}
+// Value path: each group's codeword row (8 dims) is gathered as two transposing 8-byte reads, which
+// deliver the B operands of p^T x v directly: lane 4b + e gets dim e (and 4 + e) of the 4 tokens of
+// MFMA block b (the tokens of lanes 16g + 4k + a). The p^T operand uses the same token grouping.
+template <int Q>
+__device__ __forceinline__ void gather_quarter_tr(const unsigned char* tab, const uint4& code, uint4 (&buf)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const unsigned char* row = tab + (4 * Q + u) * kCodes * 16 + code_index(code, 4 * Q + u) * 16;
+    const h4 lo = lds_read_tr(row), hi = lds_read_tr(row + 8);
+    buf[u] = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                        __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+  }
+}
+template <int G>
+__device__ __forceinline__ void value_step(const uint4& tv, const h4& pt, f4 (&O)[2 * kGroups]) {
+  O[2 * G] = mfma(pt, cat(as_h2(tv.x), as_h2(tv.y)), O[2 * G]);
+  O[2 * G + 1] = mfma(pt, cat(as_h2(tv.z), as_h2(tv.w)), O[2 * G + 1]);
+}
+template <int Q>
+__device__ __forceinline__ void value_quarter(const uint4 (&buf)[4], const h4& pt, f4 (&O)[2 * kGroups]) {
+  value_step<4 * Q + 0>(buf[0], pt, O);
+  value_step<4 * Q + 1>(buf[1], pt, O);
+  value_step<4 * Q + 2>(buf[2], pt, O);
+  value_step<4 * Q + 3>(buf[3], pt, O);
+}
+
+// A block's 16 groups are scheduled as a software pipeline: kPipeDepth codeword gathers are issued ahead,
+// then each group's VALU work and MFMA steps are followed by the gather kPipeDepth groups later, so
+// several LDS reads per wave are in flight while the rotation and products run.
+constexpr int kPipeDepth = 4;
 template <typename T, int Base, typename... Args, int... Gs>
-__device__ __forceinline__ void key_half(std::integer_sequence<int, Gs...>, Args&&... args) {
+__device__ __forceinline__ void key_seq(std::integer_sequence<int, Gs...>, Args&&... args) {
   (KeyGroup<Base + Gs, T>::run(args...), ...);
 }
 template <typename T, int Base, typename... Args, int... Gs>
-__device__ __forceinline__ void value_half(std::integer_sequence<int, Gs...>, Args&&... args) {
+__device__ __forceinline__ void value_seq(std::integer_sequence<int, Gs...>, Args&&... args) {
   (ValueGroup<Base + Gs, T>::run(args...), ...);
+}
+// sched_group_barrier masks: 0x2 VALU, 0x8 MFMA, 0x100 LDS read
+template <int kValu, int kMfmaBefore, int kMfmaAfter>
+__device__ __forceinline__ void pipeline_schedule() {
+  __builtin_amdgcn_sched_group_barrier(0x100, kPipeDepth, 0);
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    if (kMfmaBefore > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMfmaBefore, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaAfter, 0);
+    if (g + kPipeDepth < kGroups) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
 }
 template <typename T, typename... Args>
 __device__ __forceinline__ void key_groups(Args&&... args) {
-  key_half<T, 0>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
-  __builtin_amdgcn_sched_barrier(0);
-  key_half<T, kGroups / 2>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
+  key_seq<T, 0>(std::make_integer_sequence<int, kGroups>{}, args...);
+  if constexpr (std::is_same<T, f16>::value) pipeline_schedule<9, 0, 2>();
 }
 template <typename T, typename... Args>
 __device__ __forceinline__ void value_groups(Args&&... args) {
-  value_half<T, 0>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
-  __builtin_amdgcn_sched_barrier(0);
-  value_half<T, kGroups / 2>(std::make_integer_sequence<int, kGroups / 2>{}, args...);
+  value_seq<T, 0>(std::make_integer_sequence<int, kGroups>{}, args...);
+  if constexpr (std::is_same<T, f16>::value) pipeline_schedule<5, 2, 2>();
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time unrolled).
+template <int... Is, typename Fn>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, Fn&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
 // Fill one codebook slot (16 groups x 256 codes, row = 8 values of T) with direct global->LDS 16-byte
@@ -288,6 +381,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   __shared__ __attribute__((aligned(16))) unsigned char lds[kSlots * kTab];
   __shared__ __attribute__((aligned(16))) uint4 fine_lds[kF32 ? 1 : kGroups * kFineRows];  // fp16 fine phases
   __shared__ float wave_ml[2][kW][kGqa];  // per wave and head: softmax max m_w and sum l_w
+  __shared__ __attribute__((aligned(16))) uint2 p_scratch[kF32 ? 1 : kW][64];  // fp16: p^T transposes
   __shared__ int is_last;
 
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
@@ -502,8 +596,12 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     float2 cur[4];  // fp16 storage: q'' of the current block
 #pragma unroll
     for (int k = 0; k < 4; ++k) cur[k] = qc0[k];
-#pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i) {
+    uint4 rows[2][4];  // fp16: gathered rows of the current and the next quarter
+    if constexpr (!kF32) {
+      if (my_blocks > 0) gather_quarter<0>(tab, code[0], rows[0]);
+    }
+    auto key_block = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       if constexpr (staged(r)) {
         if (i > 0) stage_store(r + 1, i - 1);
         stage_load(r + 1, i);
@@ -513,7 +611,25 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
           const h4 A0 = {(f16)cur[0].x, (f16)cur[0].y, (f16)cur[1].x, (f16)cur[1].y};
           const h4 A1 = {(f16)cur[2].x, (f16)cur[2].y, (f16)cur[3].x, (f16)cur[3].y};
           f4 odd = {0.f, 0.f, 0.f, 0.f};
-          key_groups<f16>(tab, code[i], F, A0, A1, sc[i], odd);
+          // quarter q uses rows[q % 2]; the gathers of quarter q + 1 go out before its arithmetic
+          __builtin_amdgcn_sched_barrier(0);
+          gather_quarter<1>(tab, code[i], rows[1]);
+          __builtin_amdgcn_sched_barrier(0);
+          key_quarter<0>(rows[0], F, A0, A1, sc[i], odd);
+          __builtin_amdgcn_sched_barrier(0);
+          gather_quarter<2>(tab, code[i], rows[0]);
+          __builtin_amdgcn_sched_barrier(0);
+          key_quarter<1>(rows[1], F, A0, A1, sc[i], odd);
+          __builtin_amdgcn_sched_barrier(0);
+          gather_quarter<3>(tab, code[i], rows[1]);
+          __builtin_amdgcn_sched_barrier(0);
+          key_quarter<2>(rows[0], F, A0, A1, sc[i], odd);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (i + 1 < kMaxBlocks) {
+            if (i + 1 < my_blocks) gather_quarter<0>(tab, code[i + 1], rows[0]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          key_quarter<3>(rows[1], F, A0, A1, sc[i], odd);
           sc[i] += odd;
 #pragma unroll
           for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
@@ -522,7 +638,8 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
         }
       }
       request_codes(r + 1, i);  // phase r + 1 always exists (the value phases follow)
-    }
+    };
+    static_for<kMaxBlocks>(key_block);
     if constexpr (r + 1 < R) next_phase(r);
   };
   key_phase(std::integral_constant<int, 0>{});
@@ -567,7 +684,10 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 #pragma unroll
     for (int i = 0; i < kMaxBlocks; ++i) {
       if constexpr (!kF32) {
-        pth[i] = to_h4(mfma(to_h4(sc[i]), ident, z));
+        // lane writes its token's 4 head weights (fp16); the transposing read returns, in lane 4b + e,
+        // head e's weights of the 4 tokens of MFMA block b, matching the value operands
+        p_scratch[wave][lane] = __builtin_bit_cast(uint2, to_h4(sc[i]));
+        pth[i] = lds_read_tr(&p_scratch[wave][lane]);
         ptl[i] = pth[i];
       } else {
         h4 ph_, pl_;
@@ -592,16 +712,43 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     constexpr int r = decltype(rc)::value;
     constexpr int p = R + r;
     const unsigned char* tab = slot_of(p);
-#pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i) {
+    uint4 rows[2][4];  // fp16: gathered rows of the current and the next quarter
+    if constexpr (!kF32) {
+      if (my_blocks > 0) gather_quarter_tr<0>(tab, code[0], rows[0]);
+    }
+    auto value_block = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       if constexpr (staged(p)) {
         if (i > 0) stage_store(p + 1, i - 1);
         stage_load(p + 1, i);
       }
-      if (i < my_blocks)
-        value_groups<T>(tab, code[i], ident, pth[i], ptl[i], O);
+      if (i < my_blocks) {
+        if constexpr (!kF32) {
+          __builtin_amdgcn_sched_barrier(0);
+          gather_quarter_tr<1>(tab, code[i], rows[1]);
+          __builtin_amdgcn_sched_barrier(0);
+          value_quarter<0>(rows[0], pth[i], O);
+          __builtin_amdgcn_sched_barrier(0);
+          gather_quarter_tr<2>(tab, code[i], rows[0]);
+          __builtin_amdgcn_sched_barrier(0);
+          value_quarter<1>(rows[1], pth[i], O);
+          __builtin_amdgcn_sched_barrier(0);
+          gather_quarter_tr<3>(tab, code[i], rows[1]);
+          __builtin_amdgcn_sched_barrier(0);
+          value_quarter<2>(rows[0], pth[i], O);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (i + 1 < kMaxBlocks) {
+            if (i + 1 < my_blocks) gather_quarter_tr<0>(tab, code[i + 1], rows[0]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          value_quarter<3>(rows[1], pth[i], O);
+        } else {
+          value_groups<T>(tab, code[i], ident, pth[i], ptl[i], O);
+        }
+      }
       if constexpr (r + 1 < R) request_codes(p + 1, i);
-    }
+    };
+    static_for<kMaxBlocks>(value_block);
     if constexpr (r + 1 < R) next_phase(p);
   };
   value_phase(std::integral_constant<int, 0>{});
