@@ -384,7 +384,9 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   __shared__ __attribute__((aligned(16))) uint2 p_scratch[kF32 ? 1 : kW][64];  // fp16: p^T transposes
   __shared__ int is_last;
 
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  // XCD-aware work order: the KV head is the fastest grid index. Workgroups are dealt to the 8 XCDs in
+  // turn, so with 8 KV heads each XCD serves one head and its L2 fetches only that head's codebooks.
+  const int kv = blockIdx.x % a.n_kv_heads, split = blockIdx.x / a.n_kv_heads, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave values scalar
   const int L = a.seq_len[b];
@@ -875,7 +877,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 }  // namespace
 
 hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, hipStream_t s) {
-  dim3 grid(a.n_splits, a.n_kv_heads, B);
+  dim3 grid(a.n_splits * a.n_kv_heads, B);
   if (dtype == COMMVQ_F16) {
     constexpr int kThreads = Shape<f16>::kWaves * 64;
     if (R == 1) attn_kernel<f16, 1><<<grid, kThreads, 0, s>>>(a);
