@@ -142,6 +142,24 @@ int commvq_value_reduce(const commvq_dims* d /* host */, const float* p, const u
                         size_t ws_bytes /* host */, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Greedy residual encoder: writes the code indices of n_tokens new keys or values into a code array
+ * ("1-bit quantization" tag page, CommVQ abstract: vectors are encoded into indices of an additive
+ * codebook; pith.science verdict for arXiv 2506.18879, key_machinery: R residual rounds). It stands in
+ * for the pages' learned encoder, whose weights are not available: per (KV head, token, group), round
+ * r = 0..R-1 picks l* = argmin_l ||res - C[kv][g][r][l]||^2 (distances in fp32; the first minimum in index
+ * order) and subtracts that codeword from res (res starts as the group's 8 values of x).
+ *   x         [Hkv][n_tokens][D] in dims->dtype, in the codebook's own frame (keys before RoPE)
+ *   codebook  [Hkv][G][R][N][W] in dims->dtype
+ *   codes     a [Hkv][R][total_rows][G] uint8 code array; token t is written to row first_row + t, other
+ *             rows are untouched (so new tokens can be appended to a cache in place)
+ * Returns COMMVQ_EINVAL unless 0 <= first_row and first_row + n_tokens <= total_rows; n_tokens = 0 is a
+ * no-op.
+ * ------------------------------------------------------------------------------------------- */
+int commvq_encode_greedy(const commvq_dims* d /* host */, const void* x, const void* codebook,
+                         int64_t n_tokens /* host */, uint8_t* codes, int64_t total_rows /* host */,
+                         int64_t first_row /* host */, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Code unpack exactly as the attention kernels read codes: out[kv][r][t][g] = index (int32).
  * codes [Hkv][R][total_tokens][G] uint8. Used to test the unpack bit-exactly.
  * ------------------------------------------------------------------------------------------- */

@@ -60,9 +60,10 @@ def lib():
         L.oracle_scores_via_table.argtypes = [D, P, P, P, P, i64, i32, P]
         L.oracle_value_reduce.argtypes = [D, P, P, P, P, P, i64, i32, P]
         L.oracle_encode_greedy.argtypes = [D, P, P, i64, P, P]
+        L.oracle_encode_eval.argtypes = [D, P, P, i64, P, P, P, P]
         for f in ("oracle_unpack", "oracle_decode", "oracle_rope", "oracle_key_block", "oracle_rotation",
                   "oracle_attn_decode", "oracle_table", "oracle_scores_via_table", "oracle_value_reduce",
-                  "oracle_encode_greedy"):
+                  "oracle_encode_greedy", "oracle_encode_eval"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -189,6 +190,17 @@ def encode_greedy(d: Dims, x, codebook, want_dist: bool = False):
     lib().oracle_encode_greedy(ctypes.byref(d), _ptr(xx), _ptr(cb), int(n), _ptr(codes),
                                _ptr(dist) if dist is not None else None)
     return (codes, dist) if want_dist else codes
+
+
+def encode_eval(d: Dims, x, codebook, codes):
+    """Replay the greedy residual rounds with the given codes [Hkv][R][n][G]; returns (chosen, best, second)
+    squared distances per round, each [Hkv][R][n][G] float64."""
+    xx, cb, cc = _f64(x), _f64(codebook), _u8(codes)
+    n = xx.shape[1]
+    assert cc.shape == (d.n_kv_heads, d.n_residuals, n, d.n_groups)
+    outs = [np.empty(cc.shape, dtype=np.float64) for _ in range(3)]
+    lib().oracle_encode_eval(ctypes.byref(d), _ptr(xx), _ptr(cb), int(n), _ptr(cc), *(_ptr(o) for o in outs))
+    return tuple(outs)
 
 
 def run_config(cfg, inputs, n_threads: int = 1):

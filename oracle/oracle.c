@@ -367,3 +367,39 @@ void oracle_encode_greedy(const oracle_dims* d, const double* x, const double* c
       }
   free(res);
 }
+
+/* Evaluation of given codes under the greedy residual rule, for checking an encoder whose distances are
+ * computed in another precision: for each (kv, token, group) the residual rounds are replayed with the
+ * GIVEN indices; round r reports the squared distance of the given codeword to the current residual
+ * (chosen_out), the minimum over all codewords (best_out) and the second smallest (second_out). A given
+ * code is a valid greedy choice when chosen == best; when best and second are far apart the argmin is
+ * unique. codes [Hkv][R][T][G]; the three outputs [Hkv][R][T][G]. */
+void oracle_encode_eval(const oracle_dims* d, const double* x, const double* codebook, int64_t n_tokens,
+                        const uint8_t* codes, double* chosen_out, double* best_out, double* second_out) {
+  int D = d->head_dim, G = d->n_groups, W = D / G, R = d->n_residuals, N = d->n_codes;
+  double* res = (double*)malloc(sizeof(double) * W);
+  for (int kv = 0; kv < d->n_kv_heads; ++kv)
+    for (int64_t t = 0; t < n_tokens; ++t)
+      for (int g = 0; g < G; ++g) {
+        const double* xv = x + ((int64_t)kv * n_tokens + t) * D + g * W;
+        for (int w = 0; w < W; ++w) res[w] = xv[w];
+        for (int r = 0; r < R; ++r) {
+          int64_t o = code_off(d, n_tokens, kv, t, r, g);
+          int given = codes[o];
+          double b1 = INFINITY, b2 = INFINITY, dg = 0.0;
+          for (int l = 0; l < N; ++l) {
+            const double* c = codebook + cw_off(d, kv, g, r, l);
+            double dd = 0.0;
+            for (int w = 0; w < W; ++w) { double e = res[w] - c[w]; dd += e * e; }
+            if (l == given) dg = dd;
+            if (dd < b1) { b2 = b1; b1 = dd; } else if (dd < b2) { b2 = dd; }
+          }
+          chosen_out[o] = dg;
+          best_out[o] = b1;
+          second_out[o] = b2;
+          const double* c = codebook + cw_off(d, kv, g, r, given);
+          for (int w = 0; w < W; ++w) res[w] -= c[w];
+        }
+      }
+  free(res);
+}

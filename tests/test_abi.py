@@ -106,3 +106,16 @@ def test_workspace_sizes():
     # RoPE table: fine fp32 (64 x 64 x 8 B), fine fp16 (64 x 64 x 4 B), coarse (ceil(n/64) x 64 x 8 B)
     assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (4096 + 2048 + 2048 * 64) * 8
     assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 0) == 0
+
+
+def test_encode_greedy_rejects_bad_arguments_on_host():
+    d = vq.make_dims(1, 32, 8, 2)
+    L = vq.lib()
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation or is a no-op
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, -1, p, 10, 0, None) == vq.EINVAL
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, 6, None) == vq.EINVAL   # rows 6..10 > 10
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, -1, None) == vq.EINVAL
+    assert L.commvq_encode_greedy(ctypes.byref(d), None, p, 5, p, 10, 0, None) == vq.EINVAL
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 0, p, 0, 0, None) == vq.OK         # nothing to do
+    d.n_residuals = 3
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, 0, None) == vq.EUNSUPPORTED

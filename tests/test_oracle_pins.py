@@ -21,6 +21,8 @@ Which pin covers which oracle function:
                       selects one decoded value
   oracle_encode_greedy: exact codewords are recovered; brute force over all codes for R = 1;
                       ties go to the lowest index; residual rounds never increase the error
+  oracle_encode_eval: numpy brute force of the replayed rounds for arbitrary given codes; on the
+                      greedy encoder's own codes the chosen distance is the minimum
 Page figures (tests/golden/page_figures.json): bit-rate and memory arithmetic of the layouts.
 """
 import json
@@ -391,6 +393,32 @@ def test_encode_residual_rounds_do_not_increase_error(oracle_lib):
     rec = oracle.decode(d, cb, codes, 25)
     err = ((x - rec) ** 2).reshape(1, 25, 16, 8).sum(-1)
     np.testing.assert_allclose(dist[:, 2, :, :], err, rtol=1e-10, atol=1e-14)
+
+
+def test_encode_eval_brute_force_and_greedy_consistency(oracle_lib):
+    rng = np.random.default_rng(21)
+    Hkv, R, n, G, N, W = 2, 2, 9, 16, 256, 8
+    d = oracle.dims(1, 4, Hkv, R)
+    cb = rng.standard_normal((Hkv, G, R, N, W)) * 0.5
+    x = rng.standard_normal((Hkv, n, G * W)) * 0.7
+    given = rng.integers(0, N, size=(Hkv, R, n, G)).astype(np.uint8)
+    chosen, best, second = oracle.encode_eval(d, x, cb, given)
+    for kv in range(Hkv):
+        for t in range(n):
+            for g in range(G):
+                res = x[kv, t, g * W:(g + 1) * W].copy()
+                for r in range(R):
+                    dd = ((res[None, :] - cb[kv, g, r]) ** 2).sum(-1)
+                    srt = np.sort(dd)
+                    l = given[kv, r, t, g]
+                    assert chosen[kv, r, t, g] == pytest.approx(dd[l], rel=1e-13)
+                    assert best[kv, r, t, g] == pytest.approx(srt[0], rel=1e-13)
+                    assert second[kv, r, t, g] == pytest.approx(srt[1], rel=1e-13)
+                    res -= cb[kv, g, r, l]
+    codes, dist = oracle.encode_greedy(d, x, cb, want_dist=True)
+    chosen, best, _ = oracle.encode_eval(d, x, cb, codes)
+    np.testing.assert_array_equal(chosen, best)
+    np.testing.assert_array_equal(best, dist)
 
 
 # ------------------------------------------------------------------------------------ page figures

@@ -20,7 +20,7 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 EXPORTED_SYMBOLS = (
     "commvq_status_string", "commvq_last_error_detail", "commvq_rope_table_size", "commvq_rope_table",
     "commvq_qcodebook_table", "commvq_attn_decode_workspace_size", "commvq_attn_decode",
-    "commvq_value_reduce_workspace_size", "commvq_value_reduce", "commvq_debug_unpack",
+    "commvq_value_reduce_workspace_size", "commvq_value_reduce", "commvq_encode_greedy", "commvq_debug_unpack",
 )
 
 
@@ -76,6 +76,8 @@ def lib():
         L.commvq_value_reduce_workspace_size.argtypes, L.commvq_value_reduce_workspace_size.restype = [D, i32], sz
         L.commvq_value_reduce.argtypes = [D, P, P, P, P, P, i32, i64, P, sz, P, P]
         L.commvq_value_reduce.restype = ctypes.c_int
+        L.commvq_encode_greedy.argtypes = [D, P, P, i64, P, i64, i64, P]
+        L.commvq_encode_greedy.restype = ctypes.c_int
         L.commvq_debug_unpack.argtypes, L.commvq_debug_unpack.restype = [D, P, i64, P, P], ctypes.c_int
         _lib = L
     return _lib
@@ -174,6 +176,18 @@ def value_reduce(d: Dims, p, v_codes, v_codebook, seq_start, seq_len, max_len: i
                                    workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
     _check(st, "value_reduce")
     return out
+
+
+def encode_greedy(d: Dims, x, codebook, codes=None, first_row: int = 0, stream=None):
+    """Greedy residual codes of x [Hkv][n][D] (see commvq_encode_greedy). With codes=None a new
+    [Hkv][R][n][G] array is returned; otherwise the tokens are written to rows first_row.. of codes."""
+    import torch
+    n = int(x.shape[1])
+    if codes is None:
+        codes = torch.zeros((d.n_kv_heads, d.n_residuals, n, d.n_groups), dtype=torch.uint8, device=x.device)
+    _check(lib().commvq_encode_greedy(ctypes.byref(d), _ptr(x), _ptr(codebook), n, _ptr(codes), int(codes.shape[2]),
+                                      int(first_row), _stream(stream)), "encode_greedy")
+    return codes
 
 
 def debug_unpack(d: Dims, codes, total_tokens: int, out=None, stream=None):

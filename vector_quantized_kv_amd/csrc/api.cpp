@@ -210,6 +210,22 @@ int commvq_value_reduce(const commvq_dims* d, const float* p, const uint8_t* v_c
                     "value_reduce launch");
 }
 
+int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebook, int64_t n_tokens, uint8_t* codes,
+                         int64_t total_rows, int64_t first_row, void* stream) {
+  if (int st = check_dims(d)) return st;
+  if (n_tokens < 0) return fail(COMMVQ_EINVAL, "n_tokens = %lld must be >= 0", (long long)n_tokens);
+  if (first_row < 0 || total_rows < 0 || first_row + n_tokens > total_rows)
+    return fail(COMMVQ_EINVAL, "rows [%lld, %lld) do not fit total_rows = %lld", (long long)first_row,
+                (long long)(first_row + n_tokens), (long long)total_rows);
+  if (n_tokens == 0) return COMMVQ_OK;
+  if (!x || !codebook || !codes) return fail(COMMVQ_EINVAL, "x, codebook and codes must be non-NULL");
+  if ((n_tokens + 255) / 256 > 0x7fffffffLL) return fail(COMMVQ_EUNSUPPORTED, "n_tokens = %lld is too large",
+                                                          (long long)n_tokens);
+  return hip_status(launch_encode_greedy(d->dtype, d->n_residuals, d->n_kv_heads, x, codebook, n_tokens, codes,
+                                         total_rows, first_row, static_cast<hipStream_t>(stream)),
+                    "encode_greedy launch");
+}
+
 int commvq_debug_unpack(const commvq_dims* d, const uint8_t* codes, int64_t total_tokens, int32_t* out, void* stream) {
   if (int st = check_dims(d)) return st;
   if (!codes || !out) return fail(COMMVQ_EINVAL, "codes and out must be non-NULL");
