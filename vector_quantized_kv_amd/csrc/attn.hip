@@ -759,23 +759,38 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   auto epilogue = [&](const int lane, const int tid, f4 (&O)[2 * kGroups], const float (&m_w)[kGqa]) {
   lds_barrier();  // every wave is done with the value codebooks; their space is reused below
 
-  // red_o [wave][rho][d = 4c + j][h]: the 4 writing lanes of each 16-lane group store adjacent 16-byte
-  // entries, and the readers (one (h, d) each) walk consecutive entries, so neither side has bank conflicts.
+  // O[c][h] sits in lane 16*rho + 4*b' + j (head h, dim 4c + j, one token quad per (rho, b')); each output
+  // is the sum over the 16 lanes that share j. Two half-wave swap steps first fold the rows: each step pairs
+  // two registers and halves the register count, so for every q the four rows of W[q] end up holding dims
+  // 4c + j of c = 4q + rho, each summed over its 4 rows. DPP then sums the 4 quads of every row.
+  float W[2 * kGroups / 4][kGqa];
+#pragma unroll
+  for (int q = 0; q < 2 * kGroups / 4; ++q)
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      const float z0 = swap32_add(O[4 * q][h], O[4 * q + 2][h]);      // rows 0,1: c = 4q;     rows 2,3: c = 4q + 2
+      const float z1 = swap32_add(O[4 * q + 1][h], O[4 * q + 3][h]);  // rows 0,1: c = 4q + 1; rows 2,3: c = 4q + 3
+      W[q][h] = swap16_add(z0, z1);                                    // row rho: c = 4q + rho
+    }
+#pragma unroll
+  for (int q = 0; q < 2 * kGroups / 4; ++q)
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) W[q][h] += row_ror<8>(W[q][h]);
+#pragma unroll
+  for (int q = 0; q < 2 * kGroups / 4; ++q)
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      W[q][h] += row_ror<4>(W[q][h]);
+      asm("" : "+v"(W[q][h]));  // keeps the add beside its DPP move (one v_add_f32_dpp), not in the store branch
+    }
+  // red_o [wave][d][h]: lanes 16*rho + j (j < 4) store dims d = 16q + 4rho + j, so each store instruction
+  // covers 256 contiguous bytes; the readers (one (h, d) each) walk consecutive entries.
   float* red_o = reinterpret_cast<float*>(lds);
-  // two full passes, so every DPP source was written long before and each step is one v_add_f32_dpp
-#pragma unroll
-  for (int c = 0; c < 2 * kGroups; ++c)
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h) O[c][h] += row_ror<8>(O[c][h]);
-#pragma unroll
-  for (int c = 0; c < 2 * kGroups; ++c)
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h) O[c][h] += row_ror<4>(O[c][h]);
   if ((lane & 15) < 4) {
     const int rho = lane >> 4, j = lane & 3;
-    f4* dst = reinterpret_cast<f4*>(red_o) + (wave * 4 + rho) * kHeadDim + j;
+    f4* dst = reinterpret_cast<f4*>(red_o) + wave * kHeadDim + 4 * rho + j;
 #pragma unroll
-    for (int c = 0; c < 2 * kGroups; ++c) dst[4 * c] = O[c];
+    for (int q = 0; q < 2 * kGroups / 4; ++q) dst[16 * q] = (f4){W[q][0], W[q][1], W[q][2], W[q][3]};
   }
   lds_barrier();
   // Partials are written with device-scope (agent) atomic stores, which write through to the device
@@ -794,10 +809,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 #pragma unroll
     for (int w = 0; w < kW; ++w) {
       const float f = __expf(wave_ml[0][w][h] - M);  // 0 for a wave without tokens
-      float s = 0.f;
-#pragma unroll
-      for (int rho = 0; rho < 4; ++rho) s += red_o[((w * 4 + rho) * kHeadDim + d) * kGqa + h];
-      acc = fmaf(f, s, acc);
+      acc = fmaf(f, red_o[(w * kHeadDim + d) * kGqa + h], acc);
       lsum = fmaf(f, wave_ml[1][w][h], lsum);
     }
     const int64_t item = (bh0 + h) * ns_alloc + split;
@@ -868,8 +880,6 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   if (tid == 0) __hip_atomic_store(a.counters + b * a.n_kv_heads + kv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   // ------------------------------------------------------------------------ workgroup reduction
-  // O[c] in lane 16*rho + 4*b' + j, register h: head h, dim 4c + j, summed over the tokens of quad b'.
-  // Sum the 4 quads of each 16-lane row with DPP, then the 4 rows and the waves through LDS.
   // (Lane and thread indices are recomputed here so that no index register lives across the phases.)
   epilogue(lane_id(), wave * 64 + lane_id(), O, m_w);
 }

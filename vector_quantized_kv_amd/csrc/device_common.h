@@ -29,6 +29,22 @@ __device__ __forceinline__ float row_ror(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf,
                                                                true));
 }
+// Half-wave swap reductions of two registers x, y into one.
+// swap32_add: lanes 0..31 get x[l] + x[l + 32], lanes 32..63 get y[l - 32] + y[l].
+// swap16_add: per 16-lane row, row 0 gets x row 0 + x row 1, row 1 gets y rows 0 + 1, row 2 gets
+// x rows 2 + 3, row 3 gets y rows 2 + 3 (lane offsets within the row are kept).
+__device__ __forceinline__ float swap32_add(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  const unsigned s0 = s[0], s1 = s[1];  // (bit-casting a vector element directly reads element 0)
+  return __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+}
+__device__ __forceinline__ float swap16_add(float x, float y) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, y),
+                                                  false, false);
+  const unsigned s0 = s[0], s1 = s[1];  // (bit-casting a vector element directly reads element 0)
+  return __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+}
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
