@@ -628,7 +628,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
           key_quarter<2>(rows[0], F, A0, A1, sc[i], odd);
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (i + 1 < kMaxBlocks) {
-            if (i + 1 < my_blocks) gather_quarter<0>(tab, code[i + 1], rows[0]);
+            gather_quarter<0>(tab, code[i + 1], rows[0]);  // clamped record: always in bounds
           }
           __builtin_amdgcn_sched_barrier(0);
           key_quarter<3>(rows[1], F, A0, A1, sc[i], odd);
@@ -740,7 +740,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
           value_quarter<2>(rows[0], pth[i], O);
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (i + 1 < kMaxBlocks) {
-            if (i + 1 < my_blocks) gather_quarter_tr<0>(tab, code[i + 1], rows[0]);
+            gather_quarter_tr<0>(tab, code[i + 1], rows[0]);  // clamped record: always in bounds
           }
           __builtin_amdgcn_sched_barrier(0);
           value_quarter<3>(rows[1], pth[i], O);
