@@ -279,6 +279,32 @@ __device__ __forceinline__ void key_quarter(const uint4 (&buf)[4], const uint4 (
   key_step<4 * Q + 2>(buf[2], F, A0, A1, acc_even);
   key_step<4 * Q + 3>(buf[3], F, A0, A1, acc_odd);
 }
+// fp16 block loops are software pipelines over units (a quarter or a pair of groups): the gathers of unit
+// n + kAhead go out before the arithmetic of unit n, rotating through kAhead + 1 register buffers.
+constexpr int kAhead = 2;
+constexpr int kBufs = kAhead + 1;
+
+// Fused residual key path (fp16, R = 2, both key codebooks resident): a block's groups go in pairs. Each
+// group's two residual rows are gathered and summed in fp16; the rotation is linear, so the sum is rotated
+// and multiplied once instead of once per residual.
+template <int P>
+__device__ __forceinline__ void gather_pair2(const unsigned char* tab0, const unsigned char* tab1, const uint4& c0,
+                                             const uint4& c1, uint4 (&buf)[2][2]) {
+  buf[0][0] = gather_row<2 * P>(tab0, c0);
+  buf[0][1] = gather_row<2 * P>(tab1, c1);
+  buf[1][0] = gather_row<2 * P + 1>(tab0, c0);
+  buf[1][1] = gather_row<2 * P + 1>(tab1, c1);
+}
+__device__ __forceinline__ uint32_t add_h2(uint32_t x, uint32_t y) { return __builtin_bit_cast(uint32_t, as_h2(x) + as_h2(y)); }
+__device__ __forceinline__ uint4 add_rows(const uint4& x, const uint4& y) {
+  return make_uint4(add_h2(x.x, y.x), add_h2(x.y, y.y), add_h2(x.z, y.z), add_h2(x.w, y.w));
+}
+template <int P>
+__device__ __forceinline__ void key_pair2(const uint4 (&buf)[2][2], const uint4 (&F)[kGroups], const h4& A0,
+                                          const h4& A1, f4& acc_even, f4& acc_odd) {
+  key_step<2 * P>(add_rows(buf[0][0], buf[0][1]), F, A0, A1, acc_even);
+  key_step<2 * P + 1>(add_rows(buf[1][0], buf[1][1]), F, A0, A1, acc_odd);
+}
 // Value path: each group's codeword row (8 dims) is gathered as two transposing 8-byte reads, which
 // deliver the B operands of p^T x v directly: lane 4b + e gets dim e (and 4 + e) of the 4 tokens of
 // MFMA block b (the tokens of lanes 16g + 4k + a). The p^T operand uses the same token grouping.
@@ -411,7 +437,8 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 
   // token row of block i for this lane, clamped into the split so every load is in bounds
   auto token_row = [&](int i) -> int64_t {
-    const int tl = (wave + kW * i) * 64 + lane;
+    int tl = (wave + kW * i) * 64 + lane;
+    asm volatile("" : "+v"(tl));  // recomputed at every use: 8 blocks' row offsets kept live would take 16 VGPRs
     return row_base + min(tl, nvalid - 1);
   };
 
@@ -469,8 +496,21 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     const uint8_t* base = ph < R ? a.k_codes : a.v_codes;
     code[i] = load_code_record(base, a.total_tokens, kv, token_row(i), R, ph % R);
   };
+  // fp16, R = 2: both key codebooks are resident from the start, so both residuals' key records of a
+  // block are consumed together by one fused key pass (code[] holds residual 0, code1[] residual 1)
+  constexpr bool kFusedKey = !kF32 && R == 2;
+  uint4 code1[kMaxBlocks];
+  // The prologue requests the records of the first kLeadBlocks blocks only (a wave's full share would
+  // queue a large part of the whole code stream ahead of the codebook loads); block i of the first phase
+  // requests block i + kLeadBlocks.
+  constexpr int kLeadBlocks = kMaxBlocks < 3 ? kMaxBlocks : 3;
+  auto request_key_records = [&](int i) {
+    request_codes(0, i);
+    if constexpr (kFusedKey) code1[i] = load_code_record(a.k_codes, a.total_tokens, kv, token_row(i), R, 1);
+  };
 #pragma unroll
-  for (int i = 0; i < kMaxBlocks; ++i) request_codes(0, i);
+  for (int i = 0; i < kLeadBlocks; ++i) request_key_records(i);
+  constexpr int kPrologueRecords = (kFusedKey ? 2 : 1) * kLeadBlocks;
 
   // Codebooks of phases 2 and 3 (fp16, R = 2) cannot be loaded up front (both slots are busy), so during
   // phase p the codebook of phase p + 1 is staged through registers into the slot phase p - 1 used: one
@@ -504,11 +544,11 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
       slot_barrier();
     }
   };
-  // The first codebooks were issued before the kMaxBlocks code records, which the barrier keeps last.
-  // Nothing may wait on a loaded register between the codebook loads and this point: while a direct-to-
-  // LDS load is outstanding the compiler can only wait with vmcnt(0), which would include the records.
+  // The first codebooks were issued before the code records, which the barrier keeps last. Nothing may
+  // wait on a loaded register between the codebook loads and this point: while a direct-to-LDS load is
+  // outstanding the compiler can only wait with vmcnt(0), which would include the records.
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kMaxBlocks));
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kPrologueRecords));
   slot_barrier();
   uint4 F[kGroups];  // fp16 storage: fine phases of pairs 4g..4g+3 at this lane's t mod 64 = lane
   if constexpr (!kF32) {
@@ -598,12 +638,17 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     float2 cur[4];  // fp16 storage: q'' of the current block
 #pragma unroll
     for (int k = 0; k < 4; ++k) cur[k] = qc0[k];
-    uint4 rows[2][4];  // fp16: gathered rows of the current and the next quarter
+    uint4 rows[kBufs][4];  // fp16: gathered rows of quarters n .. n + kAhead
+    auto issue = [&](auto mc) {  // gathers of quarter m = 4 * block + q (clamped records: always in bounds)
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 4 * kMaxBlocks) gather_quarter<m % 4>(tab, code[m / 4], rows[m % kBufs]);
+    };
     if constexpr (!kF32) {
-      if (my_blocks > 0) gather_quarter<0>(tab, code[0], rows[0]);
+      if (my_blocks > 0) static_for<kAhead>(issue);
     }
     auto key_block = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      if constexpr (r == 0 && i + kLeadBlocks < kMaxBlocks) request_key_records(i + kLeadBlocks);
       if constexpr (staged(r)) {
         if (i > 0) stage_store(r + 1, i - 1);
         stage_load(r + 1, i);
@@ -613,25 +658,14 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
           const h4 A0 = {(f16)cur[0].x, (f16)cur[0].y, (f16)cur[1].x, (f16)cur[1].y};
           const h4 A1 = {(f16)cur[2].x, (f16)cur[2].y, (f16)cur[3].x, (f16)cur[3].y};
           f4 odd = {0.f, 0.f, 0.f, 0.f};
-          // quarter q uses rows[q % 2]; the gathers of quarter q + 1 go out before its arithmetic
-          __builtin_amdgcn_sched_barrier(0);
-          gather_quarter<1>(tab, code[i], rows[1]);
-          __builtin_amdgcn_sched_barrier(0);
-          key_quarter<0>(rows[0], F, A0, A1, sc[i], odd);
-          __builtin_amdgcn_sched_barrier(0);
-          gather_quarter<2>(tab, code[i], rows[0]);
-          __builtin_amdgcn_sched_barrier(0);
-          key_quarter<1>(rows[1], F, A0, A1, sc[i], odd);
-          __builtin_amdgcn_sched_barrier(0);
-          gather_quarter<3>(tab, code[i], rows[1]);
-          __builtin_amdgcn_sched_barrier(0);
-          key_quarter<2>(rows[0], F, A0, A1, sc[i], odd);
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (i + 1 < kMaxBlocks) {
-            gather_quarter<0>(tab, code[i + 1], rows[0]);  // clamped record: always in bounds
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          key_quarter<3>(rows[1], F, A0, A1, sc[i], odd);
+          auto quarter = [&](auto qc) {
+            constexpr int n = 4 * i + decltype(qc)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            issue(std::integral_constant<int, n + kAhead>{});
+            __builtin_amdgcn_sched_barrier(0);
+            key_quarter<n % 4>(rows[n % kBufs], F, A0, A1, sc[i], odd);
+          };
+          static_for<4>(quarter);
           sc[i] += odd;
 #pragma unroll
           for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
@@ -644,8 +678,63 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     static_for<kMaxBlocks>(key_block);
     if constexpr (r + 1 < R) next_phase(r);
   };
-  key_phase(std::integral_constant<int, 0>{});
-  if constexpr (R > 1) key_phase(std::integral_constant<int, 1>{});
+  // Fused pass (fp16, R = 2): per group pair, the four rows of both residuals go out ahead of the previous
+  // pair's arithmetic; the records of the first value phase follow each block.
+  auto fused_key_pass = [&]() {
+    const unsigned char* tab0 = slot_of(0);
+    const unsigned char* tab1 = slot_of(1);
+    float2 cur[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cur[k] = qc0[k];
+    uint4 rows[kBufs][2][2];  // [buffer][group of the pair][residual]
+    auto issue = [&](auto mc) {  // gathers of pair m = 8 * block + pair (clamped records: always in bounds)
+      constexpr int m = decltype(mc)::value;
+      constexpr int kPairs = kGroups / 2;
+      if constexpr (m < kPairs * kMaxBlocks)
+        gather_pair2<m % kPairs>(tab0, tab1, code[m / kPairs], code1[m / kPairs], rows[m % kBufs]);
+    };
+    if (my_blocks > 0) static_for<kAhead>(issue);
+    auto key_block = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + kLeadBlocks < kMaxBlocks) request_key_records(i + kLeadBlocks);
+      if (i < my_blocks) {
+        const h4 A0 = {(f16)cur[0].x, (f16)cur[0].y, (f16)cur[1].x, (f16)cur[1].y};
+        const h4 A1 = {(f16)cur[2].x, (f16)cur[2].y, (f16)cur[3].x, (f16)cur[3].y};
+        f4 odd = {0.f, 0.f, 0.f, 0.f};
+        auto pair_step = [&](auto pc) {
+          constexpr int n = (kGroups / 2) * i + decltype(pc)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          issue(std::integral_constant<int, n + kAhead>{});
+          __builtin_amdgcn_sched_barrier(0);
+          key_pair2<n % (kGroups / 2)>(rows[n % kBufs], F, A0, A1, sc[i], odd);
+        };
+        static_for<kGroups / 2>(pair_step);
+        sc[i] += odd;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
+      }
+      request_codes(R, i);
+    };
+    static_for<kMaxBlocks>(key_block);
+  };
+  if constexpr (kFusedKey) {
+    fused_key_pass();
+  } else {
+    key_phase(std::integral_constant<int, 0>{});
+    if constexpr (R > 1) key_phase(std::integral_constant<int, 1>{});
+  }
+  // Fused key pass: both slots held key codebooks, so the first value codebook could not be staged during
+  // it. Each thread fetches its 8 rows now; they are written once every wave is done with the key slots.
+  constexpr int kRowsPerThread = kTab / 16 / kThreads;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // (a plain vector type keeps the rows in VGPRs)
+  u32x4 vrows[kRowsPerThread];
+  if constexpr (kFusedKey) {
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) {
+      const int row = k * kThreads + tid, g = row >> 8, l = row & (kCodes - 1);
+      vrows[k] = *reinterpret_cast<const u32x4*>(cb_v + (static_cast<int64_t>(g) * R * kCodes + l) * kGroupDim);
+    }
+  }
 
   // ------------------------------------------------------------------------------ wave softmax
   // m_w = max over the wave's valid tokens, p = e^{s - m_w}, l_w = sum p. A wave with no valid token
@@ -704,7 +793,14 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
       }
     }
   }
-  next_phase(R - 1);
+  if constexpr (kFusedKey) {
+    lds_barrier();  // every wave is done with both key codebooks
+#pragma unroll
+    for (int k = 0; k < kRowsPerThread; ++k) *reinterpret_cast<u32x4*>(slot_of(R) + (k * kThreads + tid) * 16) = vrows[k];
+    lds_barrier();  // first value codebook complete
+  } else {
+    next_phase(R - 1);
+  }
 
   // ------------------------------------------------------------------------------ value phases
   f4 O[2 * kGroups];
@@ -714,9 +810,13 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     constexpr int r = decltype(rc)::value;
     constexpr int p = R + r;
     const unsigned char* tab = slot_of(p);
-    uint4 rows[2][4];  // fp16: gathered rows of the current and the next quarter
+    uint4 rows[kBufs][4];  // fp16: gathered rows of quarters n .. n + kAhead
+    auto issue = [&](auto mc) {  // gathers of quarter m = 4 * block + q (clamped records: always in bounds)
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 4 * kMaxBlocks) gather_quarter_tr<m % 4>(tab, code[m / 4], rows[m % kBufs]);
+    };
     if constexpr (!kF32) {
-      if (my_blocks > 0) gather_quarter_tr<0>(tab, code[0], rows[0]);
+      if (my_blocks > 0) static_for<kAhead>(issue);
     }
     auto value_block = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -726,24 +826,14 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
       }
       if (i < my_blocks) {
         if constexpr (!kF32) {
-          __builtin_amdgcn_sched_barrier(0);
-          gather_quarter_tr<1>(tab, code[i], rows[1]);
-          __builtin_amdgcn_sched_barrier(0);
-          value_quarter<0>(rows[0], pth[i], O);
-          __builtin_amdgcn_sched_barrier(0);
-          gather_quarter_tr<2>(tab, code[i], rows[0]);
-          __builtin_amdgcn_sched_barrier(0);
-          value_quarter<1>(rows[1], pth[i], O);
-          __builtin_amdgcn_sched_barrier(0);
-          gather_quarter_tr<3>(tab, code[i], rows[1]);
-          __builtin_amdgcn_sched_barrier(0);
-          value_quarter<2>(rows[0], pth[i], O);
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (i + 1 < kMaxBlocks) {
-            gather_quarter_tr<0>(tab, code[i + 1], rows[0]);  // clamped record: always in bounds
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          value_quarter<3>(rows[1], pth[i], O);
+          auto quarter = [&](auto qc) {
+            constexpr int n = 4 * i + decltype(qc)::value;
+            __builtin_amdgcn_sched_barrier(0);
+            issue(std::integral_constant<int, n + kAhead>{});
+            __builtin_amdgcn_sched_barrier(0);
+            value_quarter<n % 4>(rows[n % kBufs], pth[i], O);
+          };
+          static_for<4>(quarter);
         } else {
           value_groups<T>(tab, code[i], ident, pth[i], ptl[i], O);
         }
