@@ -415,7 +415,33 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   const int kv = blockIdx.x % a.n_kv_heads, split = blockIdx.x / a.n_kv_heads, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps per-wave values scalar
+  const int64_t cb_stride = static_cast<int64_t>(kGroups) * R * kCodes * kGroupDim;
+  const T* cb_k = static_cast<const T*>(a.k_cb) + kv * cb_stride;
+  const T* cb_v = static_cast<const T*>(a.v_cb) + kv * cb_stride;
+  auto table_src = [&](int p) { return p < R ? cb_k : cb_v; };
+  // sequence bounds, read before any memory operation so that they stay scalar loads
   const int L = a.seq_len[b];
+  const int64_t seq_start = a.seq_start[b];
+
+  // ---------------------------------------------------------------------------------- prologue
+  // (1) The codebooks of the first phases and (fp16 storage) the group-major packed-fp16 fine phases
+  // (16 KiB, once per workgroup; every wave then reads its lane's 64 phases from LDS), straight into LDS.
+  // They depend on nothing but the KV head, so they go out before the sequence bounds have arrived.
+  if constexpr (!kF32) {
+    constexpr int kFineChunks = kGroups * kFineRows;  // 16-byte entries
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine16Offset);
+#pragma unroll
+    for (int i = 0; i < kFineChunks / kThreads; ++i) {
+      const int c = (wave * (kFineChunks / kThreads) + i) * 64;
+      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, reinterpret_cast<unsigned char*>(fine_lds) + c * 16, 16,
+                                       0, 0);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < (kSlots < kPhases ? kSlots : kPhases); ++p)
+    load_table<T, R, kW>(table_src(p), p % R, lds + p * kTab, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
   const int S = a.split_tokens;
   const int t0 = split * S;
   const int h0 = kv * kGqa;
@@ -424,16 +450,13 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   if (t0 >= L) {
     if (split == 0)  // empty sequence: the output is zero
       for (int i = tid; i < kGqa * kHeadDim; i += kThreads) out_bh[i] = 0.f;
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // the direct-to-LDS loads land before the workgroup ends
     return;
   }
   const int nvalid = min(S, L - t0);
   const int nblocks = (nvalid + 63) >> 6;
   const int my_blocks = (nblocks - wave + kW - 1) / kW;  // this wave owns blocks wave, wave + kW, ...
-  const int64_t row_base = a.seq_start[b] + t0;
-  const int64_t cb_stride = static_cast<int64_t>(kGroups) * R * kCodes * kGroupDim;
-  const T* cb_k = static_cast<const T*>(a.k_cb) + kv * cb_stride;
-  const T* cb_v = static_cast<const T*>(a.v_cb) + kv * cb_stride;
-  auto table_src = [&](int p) { return p < R ? cb_k : cb_v; };
+  const int64_t row_base = seq_start + t0;
 
   // token row of block i for this lane, clamped into the split so every load is in bounds
   auto token_row = [&](int i) -> int64_t {
@@ -442,8 +465,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     return row_base + min(tl, nvalid - 1);
   };
 
-  // ---------------------------------------------------------------------------------- prologue
-  // (1) register operands the first block needs: query pairs, coarse phases of every block, fine phases.
+  // (2) register operands the first block needs: query pairs, coarse phases of every block, fine phases.
   // Query pairs this lane supplies to the broadcast A operand: head qi, pairs 2*quad + {0,1} (+32).
   const int quad = lane >> 2, qi = lane & 3;
   const T* qp = static_cast<const T*>(a.q) + (bh0 + qi) * kHeadDim;
@@ -469,23 +491,6 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     for (int m = 0; m < 2; ++m) cphase[i][m] = *reinterpret_cast<const float4*>(cr + 32 * m + 2 * quad);
   }
   const float2* fine = a.rope + lane;  // fp32 storage: fine[j * 64 + lane], read per group
-  __builtin_amdgcn_sched_barrier(0);
-  // (2a) fp16 storage: the group-major packed-fp16 fine phases (16 KiB) once per workgroup into LDS;
-  // every wave then reads its lane's 64 phases from there (instead of 8 waves loading the same table)
-  if constexpr (!kF32) {
-    constexpr int kFineChunks = kGroups * kFineRows;  // 16-byte entries
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine16Offset);
-#pragma unroll
-    for (int i = 0; i < kFineChunks / kThreads; ++i) {
-      const int c = (wave * (kFineChunks / kThreads) + i) * 64;
-      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, reinterpret_cast<unsigned char*>(fine_lds) + c * 16, 16,
-                                       0, 0);
-    }
-  }
-  // (2) codebooks of the first phases, straight into LDS
-#pragma unroll
-  for (int p = 0; p < (kSlots < kPhases ? kSlots : kPhases); ++p)
-    load_table<T, R, kW>(table_src(p), p % R, lds + p * kTab, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   // (3) code records of phase 0. Code records of the current phase live in code[]; once a block has
   // consumed its record, the record of the same token for the next phase is requested. Every phase
