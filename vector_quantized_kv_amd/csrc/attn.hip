@@ -283,6 +283,9 @@ __device__ __forceinline__ void key_quarter(const uint4 (&buf)[4], const uint4 (
 // n + kAhead go out before the arithmetic of unit n, rotating through kAhead + 1 register buffers.
 constexpr int kAhead = 2;
 constexpr int kBufs = kAhead + 1;
+// Wave priority while a wave works on block i of a phase: higher for waves with more blocks left, so the
+// two waves that share a SIMD advance together instead of the older one finishing first.
+constexpr int block_prio(int i) { return (kAttnMaxBlocksPerWave - 1 - i) * 3 / (kAttnMaxBlocksPerWave - 1); }
 
 // Fused residual key path (fp16, R = 2, both key codebooks resident): a block's groups go in pairs. Each
 // group's two residual rows are gathered and summed in fp16; the rotation is linear, so the sum is rotated
@@ -653,6 +656,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     }
     auto key_block = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      if constexpr (!kF32) __builtin_amdgcn_s_setprio(block_prio(i));
       if constexpr (r == 0 && i + kLeadBlocks < kMaxBlocks) request_key_records(i + kLeadBlocks);
       if constexpr (staged(r)) {
         if (i > 0) stage_store(r + 1, i - 1);
@@ -681,6 +685,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
       request_codes(r + 1, i);  // phase r + 1 always exists (the value phases follow)
     };
     static_for<kMaxBlocks>(key_block);
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (r + 1 < R) next_phase(r);
   };
   // Fused pass (fp16, R = 2): per group pair, the four rows of both residuals go out ahead of the previous
@@ -701,6 +706,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     if (my_blocks > 0) static_for<kAhead>(issue);
     auto key_block = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_s_setprio(block_prio(i));
       if constexpr (i + kLeadBlocks < kMaxBlocks) request_key_records(i + kLeadBlocks);
       if (i < my_blocks) {
         const h4 A0 = {(f16)cur[0].x, (f16)cur[0].y, (f16)cur[1].x, (f16)cur[1].y};
@@ -721,6 +727,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
       request_codes(R, i);
     };
     static_for<kMaxBlocks>(key_block);
+    __builtin_amdgcn_s_setprio(0);
   };
   if constexpr (kFusedKey) {
     fused_key_pass();
@@ -825,6 +832,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     }
     auto value_block = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
+      if constexpr (!kF32) __builtin_amdgcn_s_setprio(block_prio(i));
       if constexpr (staged(p)) {
         if (i > 0) stage_store(p + 1, i - 1);
         stage_load(p + 1, i);
@@ -846,6 +854,7 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
       if constexpr (r + 1 < R) request_codes(p + 1, i);
     };
     static_for<kMaxBlocks>(value_block);
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (r + 1 < R) next_phase(p);
   };
   value_phase(std::integral_constant<int, 0>{});
