@@ -334,6 +334,27 @@ __device__ __forceinline__ void value_quarter(const uint4 (&buf)[4], const h4& p
   value_step<4 * Q + 3>(buf[3], pt, O);
 }
 
+// Fused residual value path (fp16, R = 2, both value codebooks resident): each group's two residual rows
+// are gathered whole (16 bytes each: a random 16-byte LDS gather costs less than two transposing 8-byte
+// reads) and summed in fp16. An MFMA against the identity then transposes each 4-dim half within its quad
+// of lanes: lane 4b + j receives dim j of the quad's 4 tokens (exactly, in fp32), which converted back is
+// the B operand of p^T x v for MFMA block b = the quad. The p^T operand uses the same quad grouping.
+template <int G>
+__device__ __forceinline__ void value_step_quad(const uint4& row, const h4& ident, const h4& pt,
+                                                f4 (&O)[2 * kGroups]) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  const f4 x0 = mfma(cat(as_h2(row.x), as_h2(row.y)), ident, z);
+  const f4 x1 = mfma(cat(as_h2(row.z), as_h2(row.w)), ident, z);
+  O[2 * G] = mfma(pt, to_h4(x0), O[2 * G]);
+  O[2 * G + 1] = mfma(pt, to_h4(x1), O[2 * G + 1]);
+}
+template <int P>
+__device__ __forceinline__ void value_pair2(const uint4 (&buf)[2][2], const h4& ident, const h4& pt,
+                                            f4 (&O)[2 * kGroups]) {
+  value_step_quad<2 * P>(add_rows(buf[0][0], buf[0][1]), ident, pt, O);
+  value_step_quad<2 * P + 1>(add_rows(buf[1][0], buf[1][1]), ident, pt, O);
+}
+
 // A block's 16 groups are scheduled as a software pipeline: kPipeDepth codeword gathers are issued ahead,
 // then each group's VALU work and MFMA steps are followed by the gather kPipeDepth groups later, so
 // several LDS reads per wave are in flight while the rotation and products run.
@@ -724,7 +745,6 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 #pragma unroll
         for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
       }
-      request_codes(R, i);
     };
     static_for<kMaxBlocks>(key_block);
     __builtin_amdgcn_s_setprio(0);
@@ -735,17 +755,27 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     key_phase(std::integral_constant<int, 0>{});
     if constexpr (R > 1) key_phase(std::integral_constant<int, 1>{});
   }
-  // Fused key pass: both slots held key codebooks, so the first value codebook could not be staged during
-  // it. Each thread fetches its 8 rows now; they are written once every wave is done with the key slots.
+  // Fused passes: both slots held key codebooks, so the value codebooks could not be staged during the key
+  // pass. Each thread fetches its 8 rows of each now (and the value records of the first blocks); the rows
+  // are written once every wave is done with the key slots.
   constexpr int kRowsPerThread = kTab / 16 / kThreads;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // (a plain vector type keeps the rows in VGPRs)
-  u32x4 vrows[kRowsPerThread];
+  u32x4 vrows[2][kRowsPerThread];
+  auto request_value_records = [&](int i) {
+    code[i] = load_code_record(a.v_codes, a.total_tokens, kv, token_row(i), R, 0);
+    code1[i] = load_code_record(a.v_codes, a.total_tokens, kv, token_row(i), R, 1);
+  };
   if constexpr (kFusedKey) {
 #pragma unroll
-    for (int k = 0; k < kRowsPerThread; ++k) {
-      const int row = k * kThreads + tid, g = row >> 8, l = row & (kCodes - 1);
-      vrows[k] = *reinterpret_cast<const u32x4*>(cb_v + (static_cast<int64_t>(g) * R * kCodes + l) * kGroupDim);
-    }
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int k = 0; k < kRowsPerThread; ++k) {
+        const int row = k * kThreads + tid, g = row >> 8, l = row & (kCodes - 1);
+        vrows[rr][k] =
+            *reinterpret_cast<const u32x4*>(cb_v + ((static_cast<int64_t>(g) * R + rr) * kCodes + l) * kGroupDim);
+      }
+#pragma unroll
+    for (int i = 0; i < kLeadBlocks; ++i) request_value_records(i);
   }
 
   // ------------------------------------------------------------------------------ wave softmax
@@ -786,7 +816,10 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     const f4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kMaxBlocks; ++i) {
-      if constexpr (!kF32) {
+      if constexpr (kFusedKey) {
+        pth[i] = to_h4(mfma(to_h4(sc[i]), ident, z));  // quad grouping: an exact transpose of fp16 values
+        ptl[i] = pth[i];
+      } else if constexpr (!kF32) {
         // lane writes its token's 4 head weights (fp16); the transposing read returns, in lane 4b + e,
         // head e's weights of the 4 tokens of MFMA block b, matching the value operands
         p_scratch[wave][lane] = __builtin_bit_cast(uint2, to_h4(sc[i]));
@@ -808,8 +841,11 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   if constexpr (kFusedKey) {
     lds_barrier();  // every wave is done with both key codebooks
 #pragma unroll
-    for (int k = 0; k < kRowsPerThread; ++k) *reinterpret_cast<u32x4*>(slot_of(R) + (k * kThreads + tid) * 16) = vrows[k];
-    lds_barrier();  // first value codebook complete
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int k = 0; k < kRowsPerThread; ++k)
+        *reinterpret_cast<u32x4*>(slot_of(R + rr) + (k * kThreads + tid) * 16) = vrows[rr][k];
+    lds_barrier();  // both value codebooks complete
   } else {
     next_phase(R - 1);
   }
@@ -857,8 +893,43 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
     __builtin_amdgcn_s_setprio(0);
     if constexpr (r + 1 < R) next_phase(p);
   };
-  value_phase(std::integral_constant<int, 0>{});
-  if constexpr (R > 1) value_phase(std::integral_constant<int, 1>{});
+  // Fused value pass (fp16, R = 2): per group pair, the four rows of both residuals go out ahead of the
+  // previous pair's arithmetic; block i requests the records of block i + kLeadBlocks.
+  auto fused_value_pass = [&]() {
+    const unsigned char* tab0 = slot_of(R);
+    const unsigned char* tab1 = slot_of(R + 1);
+    uint4 rows[kBufs][2][2];  // [buffer][group of the pair][residual]
+    auto issue = [&](auto mc) {  // gathers of pair m = 8 * block + pair (clamped records: always in bounds)
+      constexpr int m = decltype(mc)::value;
+      constexpr int kPairs = kGroups / 2;
+      if constexpr (m < kPairs * kMaxBlocks)
+        gather_pair2<m % kPairs>(tab0, tab1, code[m / kPairs], code1[m / kPairs], rows[m % kBufs]);
+    };
+    if (my_blocks > 0) static_for<kAhead>(issue);
+    auto value_block = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_s_setprio(block_prio(i));
+      if constexpr (i + kLeadBlocks < kMaxBlocks) request_value_records(i + kLeadBlocks);
+      if (i < my_blocks) {
+        auto pair_step = [&](auto pc) {
+          constexpr int n = (kGroups / 2) * i + decltype(pc)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          issue(std::integral_constant<int, n + kAhead>{});
+          __builtin_amdgcn_sched_barrier(0);
+          value_pair2<n % (kGroups / 2)>(rows[n % kBufs], ident, pth[i], O);
+        };
+        static_for<kGroups / 2>(pair_step);
+      }
+    };
+    static_for<kMaxBlocks>(value_block);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  if constexpr (kFusedKey) {
+    fused_value_pass();
+  } else {
+    value_phase(std::integral_constant<int, 0>{});
+    if constexpr (R > 1) value_phase(std::integral_constant<int, 1>{});
+  }
 
   auto epilogue = [&](const int lane, const int tid, f4 (&O)[2 * kGroups], const float (&m_w)[kGqa]) {
   lds_barrier();  // every wave is done with the value codebooks; their space is reused below
