@@ -71,6 +71,11 @@ EDGE = [
     ("ragged_small_f16", 4, (1, 64, 65, 3000), 2, "float16"),
     ("empty_sequence_f16", 3, (700, 0, 2049), 2, "float16"),
     ("split_boundary_r1_f16", 2, (2048, 4096), 1, "float16"),
+    # more than 32 splits per (sequence, KV head): the last workgroup's merge runs several chunks and
+    # rescales the earlier ones by the running maximum
+    ("long_merge_chunks_f16", 1, (300000,), 2, "float16"),
+    ("long_merge_chunks_r1_f16", 2, (700001, 5000), 1, "float16"),
+    ("long_merge_chunks_f32", 1, (150000,), 2, "float32"),
 ]
 
 
