@@ -61,9 +61,10 @@ def lib():
         L.oracle_value_reduce.argtypes = [D, P, P, P, P, P, i64, i32, P]
         L.oracle_encode_greedy.argtypes = [D, P, P, i64, P, P]
         L.oracle_encode_eval.argtypes = [D, P, P, i64, P, P, P, P]
+        L.oracle_codebook_update.argtypes = [D, P, P, P, i64, P, P]
         for f in ("oracle_unpack", "oracle_decode", "oracle_rope", "oracle_key_block", "oracle_rotation",
                   "oracle_attn_decode", "oracle_table", "oracle_scores_via_table", "oracle_value_reduce",
-                  "oracle_encode_greedy", "oracle_encode_eval"):
+                  "oracle_encode_greedy", "oracle_encode_eval", "oracle_codebook_update"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -201,6 +202,20 @@ def encode_eval(d: Dims, x, codebook, codes):
     outs = [np.empty(cc.shape, dtype=np.float64) for _ in range(3)]
     lib().oracle_encode_eval(ctypes.byref(d), _ptr(xx), _ptr(cb), int(n), _ptr(cc), *(_ptr(o) for o in outs))
     return tuple(outs)
+
+
+def codebook_update(d: Dims, x, codebook, codes, want_counts: bool = False):
+    """One M-step of the residual codebook fit: x [Hkv][n][D], codebook [Hkv][G][R][N][W], codes
+    [Hkv][R][n][G]. Returns the new codebook (float64, same shape) and optionally the per-codeword token
+    counts [Hkv][G][R][N]."""
+    xx, cb, cc = _f64(x), _f64(codebook), _u8(codes)
+    n = xx.shape[1]
+    assert cc.shape == (d.n_kv_heads, d.n_residuals, n, d.n_groups)
+    out = np.empty(cb.shape, dtype=np.float64)
+    counts = np.empty((d.n_kv_heads, d.n_groups, d.n_residuals, d.n_codes), dtype=np.int64) if want_counts else None
+    lib().oracle_codebook_update(ctypes.byref(d), _ptr(xx), _ptr(cb), _ptr(cc), int(n), _ptr(out),
+                                 _ptr(counts) if counts is not None else None)
+    return (out, counts) if want_counts else out
 
 
 def run_config(cfg, inputs, n_threads: int = 1):

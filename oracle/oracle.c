@@ -403,3 +403,45 @@ void oracle_encode_eval(const oracle_dims* d, const double* x, const double* cod
       }
   free(res);
 }
+
+/* One M-step of the residual codebook fit ([VER] key_machinery: "the codebook is fit by an EM-style
+ * clustering algorithm", R residual rounds refine the reconstruction; [ABS]: EM training). Given the
+ * assignment codes [Hkv][R][T][G] (the E-step, e.g. oracle_encode_greedy), the new codeword
+ * (kv, g, r, l) is the mean, over the tokens whose round-r index is l, of their round-r residual
+ *     x_g(t) - sum_{r' < r} C_in[g][r'][idx_{r'}(t)],
+ * which minimizes the round's squared error for that assignment. All rounds use the input codebook for
+ * the residuals (a simultaneous update). A codeword no token selects keeps its input value. x [Hkv][T][D]
+ * (before RoPE); codebook_in / codebook_out [Hkv][G][R][N][W]; counts_out (optional) [Hkv][G][R][N]. */
+void oracle_codebook_update(const oracle_dims* d, const double* x, const double* codebook_in, const uint8_t* codes,
+                            int64_t n_tokens, double* codebook_out, int64_t* counts_out) {
+  int D = d->head_dim, G = d->n_groups, W = D / G, R = d->n_residuals, N = d->n_codes;
+  double* sum = (double*)calloc((size_t)N * W, sizeof(double));
+  int64_t* cnt = (int64_t*)calloc((size_t)N, sizeof(int64_t));
+  double* res = (double*)malloc(sizeof(double) * W);
+  for (int kv = 0; kv < d->n_kv_heads; ++kv)
+    for (int g = 0; g < G; ++g)
+      for (int r = 0; r < R; ++r) {
+        memset(sum, 0, sizeof(double) * (size_t)N * W);
+        memset(cnt, 0, sizeof(int64_t) * (size_t)N);
+        for (int64_t t = 0; t < n_tokens; ++t) {
+          const double* xv = x + ((int64_t)kv * n_tokens + t) * D + g * W;
+          for (int w = 0; w < W; ++w) res[w] = xv[w];
+          for (int rp = 0; rp < r; ++rp) {
+            const double* c = codebook_in + cw_off(d, kv, g, rp, codes[code_off(d, n_tokens, kv, t, rp, g)]);
+            for (int w = 0; w < W; ++w) res[w] -= c[w];
+          }
+          int l = codes[code_off(d, n_tokens, kv, t, r, g)];
+          for (int w = 0; w < W; ++w) sum[(int64_t)l * W + w] += res[w];
+          cnt[l] += 1;
+        }
+        for (int l = 0; l < N; ++l) {
+          const double* cin = codebook_in + cw_off(d, kv, g, r, l);
+          double* cout = codebook_out + cw_off(d, kv, g, r, l);
+          for (int w = 0; w < W; ++w) cout[w] = cnt[l] > 0 ? sum[(int64_t)l * W + w] / (double)cnt[l] : cin[w];
+          if (counts_out) counts_out[(((int64_t)kv * G + g) * R + r) * N + l] = cnt[l];
+        }
+      }
+  free(res);
+  free(cnt);
+  free(sum);
+}

@@ -421,6 +421,90 @@ def test_encode_eval_brute_force_and_greedy_consistency(oracle_lib):
     np.testing.assert_array_equal(best, dist)
 
 
+# ---------------------------------------------------------------------- residual codebook fit (M-step)
+def _fit_inputs(rng, Hkv, R, n, G=2, D=16, N=16):
+    d = oracle.dims(1, 4, Hkv, R, head_dim=D, n_groups=G, n_codes=N)
+    W = D // G
+    x = rng.standard_normal((Hkv, n, D))
+    return d, x, W
+
+
+def test_codebook_update_r1_is_one_lloyd_iteration(oracle_lib):
+    """R = 1: encode + update is one Lloyd k-means iteration, checked against scikit-learn's KMeans."""
+    sk = pytest.importorskip("sklearn.cluster")
+    rng = np.random.default_rng(30)
+    Hkv, n, G, D, N = 2, 400, 2, 16, 16
+    d, x, W = _fit_inputs(rng, Hkv, 1, n, G, D, N)
+    # initial codewords are data points, so every cluster keeps at least one member
+    pick = rng.choice(n, size=N, replace=False)
+    cb = np.stack([np.stack([x[kv, pick, g * W:(g + 1) * W] for g in range(G)]) for kv in range(Hkv)])[:, :, None]
+    codes = oracle.encode_greedy(d, x, cb)
+    new = oracle.codebook_update(d, x, cb, codes)
+    import warnings
+    for kv in range(Hkv):
+        for g in range(G):
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                km = sk.KMeans(n_clusters=N, init=cb[kv, g, 0], n_init=1, max_iter=1, tol=0.0,
+                               algorithm="lloyd").fit(x[kv, :, g * W:(g + 1) * W])
+            np.testing.assert_allclose(new[kv, g, 0], km.cluster_centers_, rtol=1e-10, atol=1e-12)
+
+
+def test_codebook_update_is_the_round_least_squares_solution(oracle_lib):
+    """Each updated codeword minimizes its round's squared error for the given assignment (residuals
+    built by decoding the earlier rounds); unused codewords keep their value; counts are the histogram."""
+    rng = np.random.default_rng(31)
+    Hkv, R, n, G, D, N = 1, 2, 60, 2, 16, 16
+    d, x, W = _fit_inputs(rng, Hkv, R, n, G, D, N)
+    cb = rng.standard_normal((Hkv, G, R, N, W)) * 0.5
+    codes = rng.integers(0, N - 2, size=(Hkv, R, n, G)).astype(np.uint8)  # codes N-2, N-1 never used
+    new, counts = oracle.codebook_update(d, x, cb, codes, want_counts=True)
+    for r in range(R):
+        cb_before = cb.copy()
+        cb_before[:, :, r:] = 0.0  # decode of rounds < r only
+        res = x - oracle.decode(d, cb_before, codes, n)  # round-r residual of every token
+        for g in range(G):
+            np.testing.assert_array_equal(counts[0, g, r], np.bincount(codes[0, r, :, g], minlength=N))
+            for l in range(N):
+                members = res[0, codes[0, r, :, g] == l, g * W:(g + 1) * W]
+                if len(members) == 0:
+                    np.testing.assert_array_equal(new[0, g, r, l], cb[0, g, r, l])
+                    continue
+                f = lambda c: float(((members - c[None, :]) ** 2).sum())
+                f0 = f(new[0, g, r, l])
+                for _ in range(4):
+                    delta = rng.standard_normal(W) * 1e-3
+                    assert f(new[0, g, r, l] + delta) > f0
+                assert f0 <= f(cb[0, g, r, l]) + 1e-12
+
+
+def test_codebook_update_fixed_point_on_exact_codewords(oracle_lib):
+    rng = np.random.default_rng(32)
+    Hkv, n, G, D, N = 2, 200, 2, 16, 16
+    d = oracle.dims(1, 4, Hkv, 1, head_dim=D, n_groups=G, n_codes=N)
+    cb = rng.standard_normal((Hkv, G, 1, N, D // G))
+    codes = np.tile(np.arange(n) % N, (Hkv, 1, G, 1)).transpose(0, 1, 3, 2).astype(np.uint8)  # every code used
+    x = oracle.decode(d, cb, codes, n)
+    got = oracle.encode_greedy(d, x, cb)
+    np.testing.assert_array_equal(got, codes)
+    np.testing.assert_allclose(oracle.codebook_update(d, x, cb, got), cb, rtol=0, atol=1e-14)
+
+
+def test_em_iterations_do_not_increase_r1_error(oracle_lib):
+    """Lloyd's iteration never increases the squared error (R = 1)."""
+    rng = np.random.default_rng(33)
+    Hkv, n, G, D, N = 1, 500, 2, 16, 16
+    d, x, W = _fit_inputs(rng, Hkv, 1, n, G, D, N)
+    cb = rng.standard_normal((Hkv, G, 1, N, W))
+    errs = []
+    for _ in range(6):
+        codes = oracle.encode_greedy(d, x, cb)
+        errs.append(float(((x - oracle.decode(d, cb, codes, n)) ** 2).sum()))
+        cb = oracle.codebook_update(d, x, cb, codes)
+    assert all(b <= a + 1e-9 for a, b in zip(errs, errs[1:]))
+    assert errs[-1] < errs[0]
+
+
 # ------------------------------------------------------------------------------------ page figures
 def test_page_figures_bit_rate_and_memory():
     with open(os.path.join(GOLDEN, "page_figures.json")) as f:
