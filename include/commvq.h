@@ -160,6 +160,25 @@ int commvq_encode_greedy(const commvq_dims* d /* host */, const void* x, const v
                          int64_t first_row /* host */, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Residual codebook update: the M-step of the codebook fit (pith.science verdict for arXiv 2506.18879,
+ * key_machinery: the codebook is fit by an EM-style clustering algorithm and R residual rounds refine the
+ * reconstruction; "1-bit quantization" tag page, CommVQ abstract: EM training). With the E-step being an
+ * assignment such as commvq_encode_greedy's, for every (kv, g, r, l):
+ *   codebook_out[kv][g][r][l] = mean over tokens t with codes[kv][r][t][g] == l of the round-r residual
+ *                               x[kv][t][8g .. 8g+7] - sum_{r' < r} codebook_in[kv][g][r'][codes[kv][r'][t][g]]
+ * (the least-squares codeword for that assignment; every round uses codebook_in for its residuals), and
+ * codebook_out = codebook_in for a codeword no token selects.
+ *   x             [Hkv][n_tokens][D] in dims->dtype, in the codebook's own frame (keys before RoPE)
+ *   codes         [Hkv][R][n_tokens][G] uint8 (commvq_encode_greedy with first_row 0, total_rows n_tokens)
+ *   codebook_in   [Hkv][G][R][N][W] in dims->dtype
+ *   codebook_out  same shape and type; must not overlap codebook_in (COMMVQ_EINVAL)
+ * Sums are accumulated in fp32 in an order that is not fixed, so repeated calls may differ by rounding.
+ * n_tokens = 0 copies codebook_in (x and codes may then be NULL).
+ * ------------------------------------------------------------------------------------------- */
+int commvq_codebook_update(const commvq_dims* d /* host */, const void* x, const uint8_t* codes,
+                           int64_t n_tokens /* host */, const void* codebook_in, void* codebook_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Code unpack exactly as the attention kernels read codes: out[kv][r][t][g] = index (int32).
  * codes [Hkv][R][total_tokens][G] uint8. Used to test the unpack bit-exactly.
  * ------------------------------------------------------------------------------------------- */

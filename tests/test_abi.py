@@ -119,3 +119,21 @@ def test_encode_greedy_rejects_bad_arguments_on_host():
     assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 0, p, 0, 0, None) == vq.OK         # nothing to do
     d.n_residuals = 3
     assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, 0, None) == vq.EUNSUPPORTED
+
+
+def test_codebook_update_rejects_bad_arguments_on_host():
+    d = vq.make_dims(1, 32, 8, 2)
+    L = vq.lib()
+    cb_bytes = 8 * 16 * 2 * 256 * 8 * 2  # fp16 codebook [Hkv][G][R][N][W]
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x100000 + cb_bytes)  # never dereferenced
+    p = ctypes.c_void_p(0x1000)
+    assert L.commvq_codebook_update(ctypes.byref(d), p, p, -1, a, b, None) == vq.EINVAL
+    assert L.commvq_codebook_update(ctypes.byref(d), None, p, 5, a, b, None) == vq.EINVAL
+    assert L.commvq_codebook_update(ctypes.byref(d), p, None, 5, a, b, None) == vq.EINVAL
+    assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, None, b, None) == vq.EINVAL
+    # output overlapping the input by one byte
+    assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, a, ctypes.c_void_p(0x100000 + cb_bytes - 1),
+                                    None) == vq.EINVAL
+    assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, a, a, None) == vq.EINVAL
+    d.n_residuals = 3
+    assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, a, b, None) == vq.EUNSUPPORTED

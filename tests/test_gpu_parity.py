@@ -237,3 +237,49 @@ def test_encode_greedy_recovers_exact_codewords_and_appends_in_place(vq):
     out = big.cpu().numpy()
     np.testing.assert_array_equal(out[:, :, 5:5 + n], idx)
     assert np.all(out[:, :, :5] == 0xAB) and np.all(out[:, :, 5 + n:] == 0xAB)
+
+
+@pytest.mark.parametrize("dtype,R,n", [("float32", 2, 3000), ("float16", 1, 2500), ("float16", 2, 4001)])
+def test_codebook_update_matches_oracle(vq, dtype, R, n):
+    """The M-step on the GPU against the oracle's for the same assignment (codes 250..255 unused)."""
+    announce(f"codebook_update {dtype} R={R} n={n}")
+    Hkv = 2
+    x, cb = encode_inputs(Hkv, n, R, dtype, 50 + R)
+    rng = np.random.default_rng(60 + R)
+    codes = rng.integers(0, 250, size=(Hkv, R, n, 16)).astype(np.uint8)
+    d = vq.make_dims(1, 4 * Hkv, Hkv, R, dtype)
+    got = vq.codebook_update(d, torch.from_numpy(x).cuda(), torch.from_numpy(codes).cuda(),
+                             torch.from_numpy(cb).cuda())
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    od = oracle.dims(1, 4 * Hkv, Hkv, R)
+    ref, counts = oracle.codebook_update(od, x, cb, codes, want_counts=True)
+    used = counts > 0
+    assert not used[..., 250:].any() and used[..., :250].all()
+    np.testing.assert_array_equal(got[..., 250:, :], cb[..., 250:, :])  # unused codewords are kept
+    if dtype == "float32":
+        np.testing.assert_allclose(got.astype(np.float64), ref, rtol=1e-5, atol=1e-6)
+    else:
+        # fp32 sums rounded once to fp16: within one fp16 ulp of the fp64 mean
+        ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(got.astype(np.float64) - ref) <= ulp)
+
+
+def test_fit_codebook_r1_error_never_increases(vq):
+    """E-step (encode_greedy) + M-step (codebook_update) on the GPU is Lloyd's iteration at R = 1: the squared
+    error, measured by the oracle's decode, never increases."""
+    announce("fit_codebook R=1")
+    Hkv, n, R = 1, 4000, 1
+    x, cb = encode_inputs(Hkv, n, R, "float32", 70)
+    d = vq.make_dims(1, 4, Hkv, R, "float32")
+    od = oracle.dims(1, 4, Hkv, R)
+    xt, cur = torch.from_numpy(x).cuda(), torch.from_numpy(cb).cuda()
+    errs = []
+    for _ in range(5):
+        cur_np = cur.cpu().numpy()
+        cur, codes = vq.fit_codebook(d, xt, cur, 1)
+        torch.cuda.synchronize()
+        errs.append(float(((x - oracle.decode(od, cur_np, codes.cpu().numpy(), n)) ** 2).sum()))
+    print("fit errors", errs, flush=True)
+    assert all(b <= a * (1 + 1e-6) for a, b in zip(errs, errs[1:]))
+    assert errs[-1] < 0.9 * errs[0]

@@ -20,7 +20,8 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 EXPORTED_SYMBOLS = (
     "commvq_status_string", "commvq_last_error_detail", "commvq_rope_table_size", "commvq_rope_table",
     "commvq_qcodebook_table", "commvq_attn_decode_workspace_size", "commvq_attn_decode",
-    "commvq_value_reduce_workspace_size", "commvq_value_reduce", "commvq_encode_greedy", "commvq_debug_unpack",
+    "commvq_value_reduce_workspace_size", "commvq_value_reduce", "commvq_encode_greedy", "commvq_codebook_update",
+    "commvq_debug_unpack",
 )
 
 
@@ -78,6 +79,8 @@ def lib():
         L.commvq_value_reduce.restype = ctypes.c_int
         L.commvq_encode_greedy.argtypes = [D, P, P, i64, P, i64, i64, P]
         L.commvq_encode_greedy.restype = ctypes.c_int
+        L.commvq_codebook_update.argtypes = [D, P, P, i64, P, P, P]
+        L.commvq_codebook_update.restype = ctypes.c_int
         L.commvq_debug_unpack.argtypes, L.commvq_debug_unpack.restype = [D, P, i64, P, P], ctypes.c_int
         _lib = L
     return _lib
@@ -188,6 +191,29 @@ def encode_greedy(d: Dims, x, codebook, codes=None, first_row: int = 0, stream=N
     _check(lib().commvq_encode_greedy(ctypes.byref(d), _ptr(x), _ptr(codebook), n, _ptr(codes), int(codes.shape[2]),
                                       int(first_row), _stream(stream)), "encode_greedy")
     return codes
+
+
+def codebook_update(d: Dims, x, codes, codebook_in, codebook_out=None, stream=None):
+    """One M-step of the residual codebook fit (see commvq_codebook_update): x [Hkv][n][D], codes
+    [Hkv][R][n][G] uint8, codebook_in [Hkv][G][R][N][W]. Returns codebook_out (a new tensor if None)."""
+    import torch
+    n = int(x.shape[1])
+    if codebook_out is None:
+        codebook_out = torch.empty_like(codebook_in)
+    _check(lib().commvq_codebook_update(ctypes.byref(d), _ptr(x), _ptr(codes), n, _ptr(codebook_in),
+                                        _ptr(codebook_out), _stream(stream)), "codebook_update")
+    return codebook_out
+
+
+def fit_codebook(d: Dims, x, codebook, iterations: int, stream=None):
+    """Residual codebook fit on the GPU: `iterations` rounds of the E-step (commvq_encode_greedy) and the
+    M-step (commvq_codebook_update), starting from `codebook`. Returns (codebook, codes of the last E-step)."""
+    cur = codebook
+    codes = None
+    for _ in range(int(iterations)):
+        codes = encode_greedy(d, x, cur, codes=codes, stream=stream)
+        cur = codebook_update(d, x, codes, cur, stream=stream)
+    return cur, codes
 
 
 def debug_unpack(d: Dims, codes, total_tokens: int, out=None, stream=None):

@@ -226,6 +226,22 @@ int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebo
                     "encode_greedy launch");
 }
 
+int commvq_codebook_update(const commvq_dims* d, const void* x, const uint8_t* codes, int64_t n_tokens,
+                           const void* codebook_in, void* codebook_out, void* stream) {
+  if (int st = check_dims(d)) return st;
+  if (n_tokens < 0) return fail(COMMVQ_EINVAL, "n_tokens = %lld must be >= 0", (long long)n_tokens);
+  if (!codebook_in || !codebook_out) return fail(COMMVQ_EINVAL, "codebook_in and codebook_out must be non-NULL");
+  if (n_tokens > 0 && (!x || !codes)) return fail(COMMVQ_EINVAL, "x and codes must be non-NULL");
+  const size_t cb_bytes = static_cast<size_t>(d->n_kv_heads) * kGroups * d->n_residuals * kCodes * kGroupDim *
+                          (d->dtype == COMMVQ_F16 ? 2 : 4);
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(codebook_in), b0 = reinterpret_cast<uintptr_t>(codebook_out);
+  if (a0 < b0 + cb_bytes && b0 < a0 + cb_bytes)
+    return fail(COMMVQ_EINVAL, "codebook_out overlaps codebook_in (the update reads the input while writing)");
+  return hip_status(launch_codebook_update(d->dtype, d->n_residuals, d->n_kv_heads, x, codes, n_tokens, codebook_in,
+                                           codebook_out, static_cast<hipStream_t>(stream)),
+                    "codebook_update launch");
+}
+
 int commvq_debug_unpack(const commvq_dims* d, const uint8_t* codes, int64_t total_tokens, int32_t* out, void* stream) {
   if (int st = check_dims(d)) return st;
   if (!codes || !out) return fail(COMMVQ_EINVAL, "codes and out must be non-NULL");

@@ -289,6 +289,70 @@ __global__ void __launch_bounds__(256) encode_greedy_kernel(const T* x, const T*
   }
 }
 
+// ------------------------------------------------------------------------ residual codebook M-step
+// One workgroup per (group g, round r, KV head): every token adds its round-r residual (x_g minus the input
+// codewords its earlier rounds select) to the bin of its round-r index, in fp32 LDS accumulators; then
+// thread l writes codeword l as the bin mean, or the input codeword when no token selects it. The
+// accumulation order across lanes is not fixed, so results may differ run to run by fp32 rounding.
+template <typename T, int R>
+__global__ void __launch_bounds__(256) codebook_update_kernel(const T* x, const uint8_t* codes, int64_t n,
+                                                              const T* cb_in, T* cb_out) {
+  const int g = blockIdx.x, r = blockIdx.y, kv = blockIdx.z;
+  __shared__ float sum[kCodes * kGroupDim];
+  __shared__ uint32_t cnt[kCodes];
+  for (int i = threadIdx.x; i < kCodes * kGroupDim; i += blockDim.x) sum[i] = 0.f;
+  for (int i = threadIdx.x; i < kCodes; i += blockDim.x) cnt[i] = 0u;
+  __syncthreads();
+  const T* cbg = cb_in + (static_cast<int64_t>(kv) * kGroups + g) * R * kCodes * kGroupDim;  // [R][N][W]
+  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) {
+    const T* xv = x + (static_cast<int64_t>(kv) * n + t) * kHeadDim + g * kGroupDim;
+    float res[kGroupDim];
+#pragma unroll
+    for (int w = 0; w < kGroupDim; ++w) res[w] = ld(xv + w);
+    for (int rp = 0; rp < r; ++rp) {
+      const int l = codes[((static_cast<int64_t>(kv) * R + rp) * n + t) * kGroups + g];
+      const T* c = cbg + (static_cast<int64_t>(rp) * kCodes + l) * kGroupDim;
+#pragma unroll
+      for (int w = 0; w < kGroupDim; ++w) res[w] -= ld(c + w);
+    }
+    const int l = codes[((static_cast<int64_t>(kv) * R + r) * n + t) * kGroups + g];
+#pragma unroll
+    for (int w = 0; w < kGroupDim; ++w) atomicAdd(&sum[l * kGroupDim + w], res[w]);
+    atomicAdd(&cnt[l], 1u);
+  }
+  __syncthreads();
+  for (int l = threadIdx.x; l < kCodes; l += blockDim.x) {
+    const int64_t o = ((static_cast<int64_t>(kv) * kGroups + g) * R + r) * kCodes * kGroupDim + l * kGroupDim;
+    const uint32_t c = cnt[l];
+#pragma unroll
+    for (int w = 0; w < kGroupDim; ++w)
+      cb_out[o + w] = c > 0 ? static_cast<T>(sum[l * kGroupDim + w] / static_cast<float>(c)) : cb_in[o + w];
+  }
+}
+
+hipError_t launch_codebook_update(int dtype, int R, int Hkv, const void* x, const uint8_t* codes, int64_t n,
+                                  const void* cb_in, void* cb_out, hipStream_t s) {
+  const dim3 grid(kGroups, R, Hkv);
+  if (dtype == COMMVQ_F16) {
+    if (R == 1)
+      codebook_update_kernel<f16, 1><<<grid, 256, 0, s>>>(static_cast<const f16*>(x), codes, n,
+                                                          static_cast<const f16*>(cb_in), static_cast<f16*>(cb_out));
+    else
+      codebook_update_kernel<f16, 2><<<grid, 256, 0, s>>>(static_cast<const f16*>(x), codes, n,
+                                                          static_cast<const f16*>(cb_in), static_cast<f16*>(cb_out));
+  } else {
+    if (R == 1)
+      codebook_update_kernel<float, 1><<<grid, 256, 0, s>>>(static_cast<const float*>(x), codes, n,
+                                                            static_cast<const float*>(cb_in),
+                                                            static_cast<float*>(cb_out));
+    else
+      codebook_update_kernel<float, 2><<<grid, 256, 0, s>>>(static_cast<const float*>(x), codes, n,
+                                                            static_cast<const float*>(cb_in),
+                                                            static_cast<float*>(cb_out));
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_encode_greedy(int dtype, int R, int Hkv, const void* x, const void* cb, int64_t n, uint8_t* codes,
                                 int64_t total_rows, int64_t first_row, hipStream_t s) {
   if (n == 0) return hipSuccess;
