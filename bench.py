@@ -228,6 +228,43 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
     return res, base
 
 
+def codebook_tools_timing(reps: int = 3):
+    """The two offline steps next to the decode path, at the 128K layer shape (8 KV heads, R = 2, fp16):
+    encoding every cached key of a 131072-token prefill with commvq_encode_greedy, and one codebook M-step
+    (commvq_codebook_update) over the same tokens. Per (token, KV head, group, round) the encoder evaluates
+    256 squared distances of 8 dims (8 subtractions + 8 multiply-adds = 24 flops each, fp32 VALU)."""
+    import torch
+    import vector_quantized_kv_amd as vq
+    Hkv, n, R = 8, 131072, 2
+    g = torch.Generator(device="cuda").manual_seed(123)
+    x = (torch.randn((Hkv, n, 128), generator=g, device="cuda") * 0.7).half()
+    cb = (torch.randn((Hkv, 16, R, 256, 8), generator=g, device="cuda") * 0.5).half()
+    d = vq.make_dims(1, 4 * Hkv, Hkv, R, "float16")
+    codes = vq.encode_greedy(d, x, cb)
+    out = vq.codebook_update(d, x, codes, cb)
+    torch.cuda.synchronize()
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+    t_enc = timed(lambda: vq.encode_greedy(d, x, cb, codes=codes))
+    t_upd = timed(lambda: vq.codebook_update(d, x, codes, cb, codebook_out=out))
+    enc_flops = float(Hkv) * n * 16 * R * 256 * 24
+    return {
+        "shape": f"{n} tokens x {Hkv} KV heads, R={R}, fp16",
+        # the library is built without packed-fp32 instructions, so its fp32 VALU peak is half the published
+        # 157.3 TFLOP/s: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz = 78.6 TFLOP/s
+        "encode_greedy": {"ms": t_enc * 1e3, "tokens_per_s": n / t_enc, "bound": "alu",
+                          "achieved_tflops": enc_flops / t_enc * 1e-12, "peak_tflops": 78.6,
+                          "frac": enc_flops / t_enc * 1e-12 / 78.6},
+        "codebook_update": {"ms": t_upd * 1e3, "tokens_per_s": n / t_upd},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +321,7 @@ def main():
         "hbm_read_stream_GBps": read_stream_gbps(),
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    line["codebook_tools"] = codebook_tools_timing()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, base)
     print(json.dumps(line), flush=True)
