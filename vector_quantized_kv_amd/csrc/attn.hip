@@ -137,28 +137,11 @@ __device__ __forceinline__ h4 identity_b(int lane) {
   return (h4){(f16)(j == 0), (f16)(j == 1), (f16)(j == 2), (f16)(j == 3)};
 }
 
-// ---------------------------------------------------------------------------------- per-group steps
-// Key step for group G of one 64-token block: gather, rotate, two MFMA steps (4 dims each).
-// F[G] holds the lane's fine phases of pairs 4G..4G+3 (packed fp16 (cos, sin) per pair).
+// ------------------------------------------------------------------ fp32 storage: per-group steps
+// Key step for group G of one 64-token block: gather, rotate, MFMA steps (4 dims each). The fp16 path
+// below processes groups in explicitly pipelined units instead.
 template <int G, typename T>
 struct KeyGroup;
-
-template <int G>
-struct KeyGroup<G, f16> {
-  __device__ __forceinline__ static void run(const unsigned char* tab, const uint4& code, const uint4 (&F)[kGroups],
-                                             const h4& A0, const h4& A1, f4& acc_even, f4& acc_odd) {
-    f4& acc = (G & 1) ? acc_odd : acc_even;  // two independent MFMA accumulation chains
-    const uint32_t idx = code_index(code, G);
-    const uint4 row = *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + idx * 16);
-    const h2 w0 = crot(as_h2(row.x), as_h2(F[G].x));
-    const h2 w1 = crot(as_h2(row.y), as_h2(F[G].y));
-    const h2 w2 = crot(as_h2(row.z), as_h2(F[G].z));
-    const h2 w3 = crot(as_h2(row.w), as_h2(F[G].w));
-    const h4 A = (G < 8) ? A0 : A1;
-    acc = mfma_bcast<(2 * G) & 15>(A, cat(w0, w1), acc);
-    acc = mfma_bcast<(2 * G + 1) & 15>(A, cat(w2, w3), acc);
-  }
-};
 
 // fp32: row of 8 floats (32 bytes); rotation in fp32, then hi/lo fp16 parts; three products per step.
 template <int G>
@@ -202,21 +185,6 @@ struct KeyGroup<G, float> {
 // Value step for group G: gather 8 dims, quad-transpose 2 tiles, accumulate p^T v into O[2G], O[2G+1].
 template <int G, typename T>
 struct ValueGroup;
-
-template <int G>
-struct ValueGroup<G, f16> {
-  __device__ __forceinline__ static void run(const unsigned char* tab, const uint4& code, const h4& ident,
-                                             const h4& pt, const h4& /*unused*/, f4 (&O)[2 * kGroups]) {
-    const uint32_t idx = code_index(code, G);
-    const uint4 row = *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + idx * 16);
-    const f4 z = {0.f, 0.f, 0.f, 0.f};
-    const f4 x0 = mfma(cat(as_h2(row.x), as_h2(row.y)), ident, z);
-    const f4 x1 = mfma(cat(as_h2(row.z), as_h2(row.w)), ident, z);
-    O[2 * G] = mfma(pt, to_h4(x0), O[2 * G]);
-    O[2 * G + 1] = mfma(pt, to_h4(x1), O[2 * G + 1]);
-  }
-};
-
 template <int G>
 struct ValueGroup<G, float> {
   __device__ __forceinline__ static void run(const unsigned char* tab, const uint4& code, const h4& ident,
@@ -245,9 +213,9 @@ struct ValueGroup<G, float> {
 };
 
 // ------------------------------------------------------- fp16: explicitly pipelined block processing
-// A block's 16 groups are processed in quarters of 4. The 4 codeword gathers of the next quarter (or of
-// the next block's first quarter) are issued in a scheduling region ahead of the current quarter's
-// arithmetic, so each wave keeps 4 LDS reads in flight while it rotates and multiplies.
+// A block's 16 groups are processed in units (quarters of 4 groups, or pairs of groups with both residual
+// rows); the gathers of a later unit are issued in a scheduling region ahead of the current unit's
+// arithmetic (see kAhead), so each wave keeps LDS reads in flight while it rotates and multiplies.
 template <int G>
 __device__ __forceinline__ uint4 gather_row(const unsigned char* tab, const uint4& code) {
   return *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + code_index(code, G) * 16);
@@ -355,10 +323,7 @@ __device__ __forceinline__ void value_pair2(const uint4 (&buf)[2][2], const h4& 
   value_step_quad<2 * P + 1>(add_rows(buf[1][0], buf[1][1]), ident, pt, O);
 }
 
-// A block's 16 groups are scheduled as a software pipeline: kPipeDepth codeword gathers are issued ahead,
-// then each group's VALU work and MFMA steps are followed by the gather kPipeDepth groups later, so
-// several LDS reads per wave are in flight while the rotation and products run.
-constexpr int kPipeDepth = 4;
+// fp32 storage: a block's 16 groups in sequence.
 template <typename T, int Base, typename... Args, int... Gs>
 __device__ __forceinline__ void key_seq(std::integer_sequence<int, Gs...>, Args&&... args) {
   (KeyGroup<Base + Gs, T>::run(args...), ...);
@@ -367,27 +332,13 @@ template <typename T, int Base, typename... Args, int... Gs>
 __device__ __forceinline__ void value_seq(std::integer_sequence<int, Gs...>, Args&&... args) {
   (ValueGroup<Base + Gs, T>::run(args...), ...);
 }
-// sched_group_barrier masks: 0x2 VALU, 0x8 MFMA, 0x100 LDS read
-template <int kValu, int kMfmaBefore, int kMfmaAfter>
-__device__ __forceinline__ void pipeline_schedule() {
-  __builtin_amdgcn_sched_group_barrier(0x100, kPipeDepth, 0);
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
-    if (kMfmaBefore > 0) __builtin_amdgcn_sched_group_barrier(0x008, kMfmaBefore, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaAfter, 0);
-    if (g + kPipeDepth < kGroups) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
 template <typename T, typename... Args>
 __device__ __forceinline__ void key_groups(Args&&... args) {
   key_seq<T, 0>(std::make_integer_sequence<int, kGroups>{}, args...);
-  if constexpr (std::is_same<T, f16>::value) pipeline_schedule<9, 0, 2>();
 }
 template <typename T, typename... Args>
 __device__ __forceinline__ void value_groups(Args&&... args) {
   value_seq<T, 0>(std::make_integer_sequence<int, kGroups>{}, args...);
-  if constexpr (std::is_same<T, f16>::value) pipeline_schedule<5, 2, 2>();
 }
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time unrolled).
