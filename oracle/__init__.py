@@ -62,9 +62,11 @@ def lib():
         L.oracle_encode_greedy.argtypes = [D, P, P, i64, P, P]
         L.oracle_encode_eval.argtypes = [D, P, P, i64, P, P, P, P]
         L.oracle_codebook_update.argtypes = [D, P, P, P, i64, P, P]
+        L.oracle_unpack_bits.argtypes = [D, P, i64, P]
         for f in ("oracle_unpack", "oracle_decode", "oracle_rope", "oracle_key_block", "oracle_rotation",
                   "oracle_attn_decode", "oracle_table", "oracle_scores_via_table", "oracle_value_reduce",
-                  "oracle_encode_greedy", "oracle_encode_eval", "oracle_codebook_update"):
+                  "oracle_encode_greedy", "oracle_encode_eval", "oracle_codebook_update",
+                  "oracle_unpack_bits"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -101,6 +103,14 @@ def unpack(d: Dims, codes: np.ndarray, total_tokens: int) -> np.ndarray:
     c = _u8(codes)
     out = np.empty(c.shape, dtype=np.int32)
     lib().oracle_unpack(ctypes.byref(d), _ptr(c), int(total_tokens), _ptr(out))
+    return out
+
+
+def unpack_bits(d: Dims, words, total_tokens: int) -> np.ndarray:
+    """Bit-packed index records [Hkv][T][ceil(bits*R*G/32)] uint32 -> indices [Hkv][R][T][G] uint8."""
+    ww = np.ascontiguousarray(words, dtype=np.uint32)
+    out = np.empty((d.n_kv_heads, d.n_residuals, int(total_tokens), d.n_groups), dtype=np.uint8)
+    lib().oracle_unpack_bits(ctypes.byref(d), ww.ctypes.data_as(ctypes.c_void_p), int(total_tokens), _ptr(out))
     return out
 
 
@@ -219,7 +229,11 @@ def codebook_update(d: Dims, x, codebook, codes, want_counts: bool = False):
 
 
 def run_config(cfg, inputs, n_threads: int = 1):
-    """Oracle output for a workloads config and its inputs dict."""
-    return attn_decode(dims_of(cfg), inputs["q"], inputs["k_codes"], inputs["v_codes"], inputs["k_cb"],
-                       inputs["v_cb"], inputs["seq_start"], inputs["seq_len"], int(inputs["max_len"]),
-                       n_threads=n_threads)
+    """Oracle output for a workloads config and its inputs dict (bit-packed records are unpacked here)."""
+    d = dims_of(cfg)
+    kc, vc = inputs["k_codes"], inputs["v_codes"]
+    if kc.dtype == np.uint32:
+        T = int(inputs["total_tokens"])
+        kc, vc = unpack_bits(d, kc, T), unpack_bits(d, vc, T)
+    return attn_decode(d, inputs["q"], kc, vc, inputs["k_cb"], inputs["v_cb"], inputs["seq_start"],
+                       inputs["seq_len"], int(inputs["max_len"]), n_threads=n_threads)

@@ -421,6 +421,93 @@ def test_encode_eval_brute_force_and_greedy_consistency(oracle_lib):
     np.testing.assert_array_equal(best, dist)
 
 
+# ------------------------------------------------------------------------- bit-packed indices (g = 64)
+def _pack_bits_bigint(idx, bits):
+    """Reference packing from the definition of a little-endian bitstream: one Python integer per token,
+    index k (k = r*G + g) at bit offset bits*k, cut into 32-bit words."""
+    Hkv, R, T, G = idx.shape
+    nwords = (bits * R * G + 31) // 32
+    out = np.zeros((Hkv, T, nwords), dtype=np.uint32)
+    for kv in range(Hkv):
+        for t in range(T):
+            v = 0
+            for r in range(R):
+                for g in range(G):
+                    v |= int(idx[kv, r, t, g]) << (bits * (r * G + g))
+            for k in range(nwords):
+                out[kv, t, k] = (v >> (32 * k)) & 0xFFFFFFFF
+    return out
+
+
+@pytest.mark.parametrize("R,G,N", [(11, 2, 64), (21, 2, 64), (3, 4, 16), (5, 2, 128)])
+def test_unpack_bits_matches_bigint_stream(oracle_lib, R, G, N):
+    rng = np.random.default_rng(40 + R)
+    d = oracle.dims(1, 4, 2, R, head_dim=64 * G, n_groups=G, n_codes=N)
+    idx = rng.integers(0, N, size=(2, R, 7, G)).astype(np.uint8)
+    bits = int(np.log2(N))
+    np.testing.assert_array_equal(oracle.unpack_bits(d, _pack_bits_bigint(idx, bits), 7), idx)
+
+
+def test_unpack_bits_hand_worked_words(oracle_lib):
+    d = oracle.dims(1, 4, 1, 11, head_dim=128, n_groups=2, n_codes=64)  # 132 bits -> 5 words per token
+    ones = np.zeros((1, 1, 5), dtype=np.uint32)
+    ones[0, 0, :4] = 0xFFFFFFFF
+    ones[0, 0, 4] = 0xF
+    assert np.all(oracle.unpack_bits(d, ones, 1) == 63)
+    one = np.zeros((1, 1, 5), dtype=np.uint32)
+    one[0, 0, 1] = 0x10000000  # bit 60 = index k = 10 = (round 5, group 0), value 1
+    got = oracle.unpack_bits(d, one, 1)
+    assert got[0, 5, 0, 0] == 1 and got.sum() == 1
+    straddle = np.zeros((1, 1, 5), dtype=np.uint32)
+    straddle[0, 0, 0] = 1 << 30  # index k = 5 (round 2, group 1) occupies bits 30..35: value 0b110101 = 53
+    straddle[0, 0, 1] = 0b1101
+    got = oracle.unpack_bits(d, straddle, 1)
+    assert got[0, 2, 0, 1] == 53 and got.sum() == 53
+
+
+def test_unpack_bits_at_8_bits_one_round_is_the_byte_layout(oracle_lib):
+    """With N = 256 and R = 1 a token's bitstream is its 16 code bytes, so the byte layout read as words
+    unpacks to itself."""
+    rng = np.random.default_rng(44)
+    d = oracle.dims(1, 4, 3, 1)
+    codes = rng.integers(0, 256, size=(3, 1, 11, 16)).astype(np.uint8)
+    words = codes.reshape(3, 11, 16).view(np.uint32)
+    np.testing.assert_array_equal(oracle.unpack_bits(d, words, 11), codes)
+    np.testing.assert_array_equal(oracle.unpack(d, codes, 11), codes.astype(np.int32))
+
+
+def test_pages_setting_attention_matches_torch_sdpa(oracle_lib):
+    """The pages' g = 64 / N' = 64 / R = 11 setting end to end: indices drawn here, laid out as bit-packed
+    records by the workloads generator, unpacked and attended by the oracle, against torch's SDPA over
+    keys and values built here by plain indexing."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(45)
+    Hkv, R, G, N, W, L = 2, 11, 2, 64, 64, 300
+    d = oracle.dims(1, 8, Hkv, R, head_dim=128, n_groups=G, n_codes=N, rope_base=500000.0)
+    kcb = rng.standard_normal((Hkv, G, R, N, W)) * 0.5
+    vcb = rng.standard_normal((Hkv, G, R, N, W)) * 0.5
+    q = rng.standard_normal((1, 8, 128))
+    ki = rng.integers(0, N, size=(Hkv, R, L, G)).astype(np.uint8)
+    vi = rng.integers(0, N, size=(Hkv, R, L, G)).astype(np.uint8)
+    kw, vw = workloads.pack_bits(ki, 6), workloads.pack_bits(vi, 6)
+    assert kw.shape == (Hkv, L, 5)
+    out = oracle.attn_decode(d, q, oracle.unpack_bits(d, kw, L), oracle.unpack_bits(d, vw, L), kcb, vcb,
+                             np.zeros(1, np.int64), np.array([L], np.int32), L)
+    theta = 500000.0 ** (-np.arange(64) * 2.0 / 128)
+    ph = np.exp(1j * np.outer(np.arange(L), theta))
+    for kv in range(Hkv):
+        K = sum(kcb[kv, np.arange(G)[None, :], r, ki[kv, r]] for r in range(R)).reshape(L, 128)
+        V = sum(vcb[kv, np.arange(G)[None, :], r, vi[kv, r]] for r in range(R)).reshape(L, 128)
+        Kc = (K[:, 0::2] + 1j * K[:, 1::2]) * ph
+        Kr = np.empty_like(K)
+        Kr[:, 0::2], Kr[:, 1::2] = Kc.real, Kc.imag
+        Q = torch.from_numpy(q[0, 4 * kv:4 * kv + 4])[:, None, :]
+        Kt = torch.from_numpy(Kr)[None].expand(4, L, 128).contiguous()
+        Vt = torch.from_numpy(V)[None].expand(4, L, 128).contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, Kt, Vt, scale=1 / np.sqrt(128))[:, 0]
+        np.testing.assert_allclose(out[0, 4 * kv:4 * kv + 4], ref.numpy(), atol=1e-11)
+
+
 # ---------------------------------------------------------------------- residual codebook fit (M-step)
 def _fit_inputs(rng, Hkv, R, n, G=2, D=16, N=16):
     d = oracle.dims(1, 4, Hkv, R, head_dim=D, n_groups=G, n_codes=N)

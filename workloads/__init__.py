@@ -9,6 +9,9 @@ Layouts (shared by every consumer):
   v_cb     [Hkv][G][R][N][W]       value codebook
   k_codes  [Hkv][R][T][G] uint8    one byte per code index (N = 256); one plane per residual
   v_codes  [Hkv][R][T][G] uint8
+           N < 256 (the pages' g = 64 setting, N = 64): bit-packed records [Hkv][T][words] uint32 instead,
+           each token's R*G indices of log2(N) bits as one little-endian bitstream, index (r, g) at bit
+           log2(N) * (r*G + g), words = ceil(log2(N) * R * G / 32)
   seq_start[B] int64, seq_len[B] int32: sequence b owns token rows seq_start[b] .. +seq_len[b]-1
 with D = head_dim, G = n_groups, W = D / G, R = n_residuals, N = n_codes, T = total tokens.
 
@@ -50,6 +53,19 @@ class Config:
     def group_dim(self) -> int:
         return self.head_dim // self.n_groups
 
+    @property
+    def index_bits(self) -> int:
+        return int(round(math.log2(self.n_codes)))
+
+    @property
+    def packed(self) -> bool:
+        """Bit-packed token records (N < 256) instead of one byte per index."""
+        return self.n_codes < 256
+
+    @property
+    def record_words(self) -> int:
+        return (self.index_bits * self.n_residuals * self.n_groups + 31) // 32
+
 
 # The five workloads: a tiny CPU-checkable step, the Llama-3.1-8B layer shape (8 KV / 32 q heads,
 # head dim 128) at 8K / 32K / 128K context, and a ragged batch of 16 sequences.
@@ -66,6 +82,19 @@ CONFIGS: Dict[str, Config] = {
                               description="Llama-3.1-8B layer, L=131072, 2-bit (R=2), fp16"),
     "ragged16_r2": Config("ragged16_r2", 16, 32, 8, None, 2, "float16", 5, ragged_range=(4096, 65536),
                           description="16 sequences, L_b ~ U[4096, 65536], 2-bit (R=2), fp16"),
+}
+
+# The pages' own setting: one index shared by 64 dims (G = 2 groups of 64), N' = 64 codewords (6-bit
+# indices, bit-packed), R = 11 (1.03 bits per scalar) or R = 21 (1.97 bits), at the same layer shape.
+PAGES_CONFIGS: Dict[str, Config] = {
+    "pages_g64_r11_small": Config("pages_g64_r11_small", 2, 8, 2, (1000, 3001), 11, "float16", 20, n_groups=2,
+                                  n_codes=64, description="g=64, N'=64, R=11, two short sequences, fp16"),
+    "pages_g64_r11_32k": Config("pages_g64_r11_32k", 1, 32, 8, (32768,), 11, "float16", 21, n_groups=2, n_codes=64,
+                                description="Llama-3.1-8B layer, L=32768, g=64, N'=64, R=11 (1.03 bit), fp16"),
+    "pages_g64_r21_32k": Config("pages_g64_r21_32k", 1, 32, 8, (32768,), 21, "float16", 22, n_groups=2, n_codes=64,
+                                description="Llama-3.1-8B layer, L=32768, g=64, N'=64, R=21 (1.97 bit), fp16"),
+    "pages_g64_r21_128k": Config("pages_g64_r21_128k", 1, 32, 8, (131072,), 21, "float16", 23, n_groups=2,
+                                 n_codes=64, description="Llama-3.1-8B layer, L=131072, g=64, N'=64, R=21, fp16"),
 }
 
 
@@ -102,10 +131,30 @@ def make_inputs(cfg: Config, seed: Optional[int] = None) -> Dict[str, np.ndarray
         rng.integers(0, N, size=(Hkv, R, total, G)).astype(np.uint8)
     v_codes = rng.integers(0, N, size=(Hkv, R, total, G), dtype=np.uint8) if N == 256 else \
         rng.integers(0, N, size=(Hkv, R, total, G)).astype(np.uint8)
+    if cfg.packed:
+        k_codes, v_codes = pack_bits(k_codes, cfg.index_bits), pack_bits(v_codes, cfg.index_bits)
     return dict(q=q, k_cb=k_cb, v_cb=v_cb, k_codes=k_codes, v_codes=v_codes, seq_start=seq_start,
                 seq_len=seq_len, total_tokens=np.int64(total), max_len=np.int32(max(lengths) if lengths else 0))
 
 
+def pack_bits(idx: np.ndarray, bits: int) -> np.ndarray:
+    """Lay out indices [Hkv][R][T][G] (each < 2**bits) as bit-packed token records [Hkv][T][words] uint32."""
+    Hkv, R, T, G = idx.shape
+    words = (bits * R * G + 31) // 32
+    out = np.zeros((Hkv, T, words), dtype=np.uint64)
+    for r in range(R):
+        for g in range(G):
+            pos = bits * (r * G + g)
+            w, sh = pos // 32, pos % 32
+            v = idx[:, r, :, g].astype(np.uint64)
+            out[:, :, w] |= (v << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+            if sh + bits > 32:
+                out[:, :, w + 1] |= v >> np.uint64(32 - sh)
+    return out.astype(np.uint32)
+
+
 def code_bytes(cfg: Config, total_tokens: int) -> int:
     """Bytes of key + value code indices for `total_tokens` cached tokens (all KV heads)."""
+    if cfg.packed:
+        return 2 * cfg.n_kv_heads * total_tokens * cfg.record_words * 4
     return 2 * cfg.n_kv_heads * total_tokens * cfg.n_residuals * cfg.n_groups
