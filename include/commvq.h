@@ -29,6 +29,15 @@
  * q head h reads KV head h / (Hq / Hkv). Pair j covers dims (2j, 2j+1); RoPE frequency
  * theta_j = rope_base^(-2j/D); group g holds pairs 4g .. 4g+3 (W = 8).
  *
+ * Bit-packed layout (the CommVQ pages' own code shape: one index shared by 64 dims, N = 64 codewords,
+ * R up to 32 residual rounds, e.g. R = 11 for about 1 bit per scalar and R = 21 for about 2; average
+ * bits R log2(N) / 64 per scalar: pith.science verdict for arXiv 2506.18879, key_machinery; the arXiv
+ * listing's Limitations section names R = 11 and 21). Selected by n_groups = 2, n_codes = 64:
+ *   k_codebook, v_codebook [Hkv][2][R][64][64]   as above with W = 64 (group g holds pairs 32g .. 32g+31)
+ *   k_codes, v_codes       [Hkv][T][ceil(12 R / 32)] little-endian uint32 words, passed through the
+ *                          uint8_t pointer: token t's R x 2 six-bit indices as one bitstream, index
+ *                          (r, g) at bit 6 (2 r + g) (bit k of the stream = bit k % 32 of word k / 32)
+ *
  * Conventions for every call:
  *   - Pointers are device pointers unless marked (host). Buffers are owned by the caller; the library
  *     keeps no state, allocates nothing, frees nothing and never synchronizes.
@@ -37,8 +46,10 @@
  *   - All argument checks run on the host before any launch; a failing call launches nothing and has
  *     no side effects. Return value: COMMVQ_OK (0) or a negative commvq_status; the thread-local
  *     commvq_last_error_detail() then names the offending argument.
- *   - Supported now: head_dim 128, n_groups 16, n_codes 256, n_residuals 1..2, Hq / Hkv = 4,
- *     dtype fp16 or fp32. Other values return COMMVQ_EUNSUPPORTED.
+ *   - Supported now: head_dim 128, Hq / Hkv = 4, and either the byte layout (n_groups 16, n_codes 256,
+ *     n_residuals 1..2, dtype fp16 or fp32) or the bit-packed layout (n_groups 2, n_codes 64,
+ *     n_residuals 1..32, dtype fp16; commvq_rope_table, commvq_attn_decode and commvq_debug_unpack
+ *     only). Other values return COMMVQ_EUNSUPPORTED.
  *   - No C++ exception crosses the ABI.
  */
 #ifndef COMMVQ_H
@@ -66,9 +77,9 @@ typedef struct {
   int32_t n_q_heads;    /* Hq */
   int32_t n_kv_heads;   /* Hkv; Hq % Hkv == 0 */
   int32_t head_dim;     /* D (128) */
-  int32_t n_groups;     /* G (16): one code index per residual per group of W = D/G dims */
-  int32_t n_residuals;  /* R (1..2): residual codebooks; R bits per scalar at N = 256, W = 8 */
-  int32_t n_codes;      /* N (256) */
+  int32_t n_groups;     /* G (16, or 2 bit-packed): one code index per residual per group of W = D/G dims */
+  int32_t n_residuals;  /* R (1..2, or 1..32 bit-packed): residual codebooks */
+  int32_t n_codes;      /* N (256, or 64 bit-packed) */
   double rope_base;     /* RoPE base (e.g. 500000) */
   float softmax_scale;  /* e.g. 1/sqrt(D) */
   int32_t dtype;        /* commvq_dtype of q and both codebooks; outputs are fp32 */
@@ -119,6 +130,7 @@ int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const
  * the last workgroup of each (b, kv) resets, so every completed call leaves it zero-filled again; the
  * rest is scratch. Calls that share one workspace must not overlap in time.
  * Codes, codebooks and rope_table must be 16-byte aligned.
+ * Both layouts: the bit-packed one reads its token records [Hkv][T][words] instead of the planes.
  * ------------------------------------------------------------------------------------------- */
 size_t commvq_attn_decode_workspace_size(const commvq_dims* d /* host */, int32_t max_len);
 int commvq_attn_decode(const commvq_dims* d /* host */, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
@@ -180,7 +192,9 @@ int commvq_codebook_update(const commvq_dims* d /* host */, const void* x, const
 
 /* ---------------------------------------------------------------------------------------------
  * Code unpack exactly as the attention kernels read codes: out[kv][r][t][g] = index (int32).
- * codes [Hkv][R][total_tokens][G] uint8. Used to test the unpack bit-exactly.
+ * codes [Hkv][R][total_tokens][G] uint8, or (bit-packed layout) the token records
+ * [Hkv][total_tokens][ceil(12 R / 32)] uint32, read in the attention kernel's windows of 4 residuals.
+ * Used to test the unpack bit-exactly.
  * ------------------------------------------------------------------------------------------- */
 int commvq_debug_unpack(const commvq_dims* d /* host */, const uint8_t* codes, int64_t total_tokens /* host */,
                         int32_t* out, void* stream);

@@ -137,3 +137,32 @@ def test_codebook_update_rejects_bad_arguments_on_host():
     assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, a, a, None) == vq.EINVAL
     d.n_residuals = 3
     assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, a, b, None) == vq.EUNSUPPORTED
+
+
+def test_bit_packed_layout_checks_on_host():
+    L = vq.lib()
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation or sizes only
+    d = vq.make_dims(1, 32, 8, 21, n_groups=2, n_codes=64)
+    # accepted shapes: workspace and table sizes are reported
+    assert vq.attn_decode_workspace_size(d, 4096) > 0
+    assert L.commvq_rope_table_size(ctypes.byref(d), 4096) > 0
+    for R, status in ((1, 0), (32, 0), (33, vq.EUNSUPPORTED), (0, vq.EINVAL)):
+        dd = vq.make_dims(1, 32, 8, R, n_groups=2, n_codes=64)
+        assert (L.commvq_attn_decode_workspace_size(ctypes.byref(dd), 64) > 0) == (status == 0), R
+    # fp32 codebooks are not implemented for the bit-packed layout
+    d32 = vq.make_dims(1, 32, 8, 11, dtype="float32", n_groups=2, n_codes=64)
+    assert _attn(d32, **ALL) == vq.EUNSUPPORTED
+    # the byte-layout-only entry points refuse the bit-packed layout
+    assert L.commvq_qcodebook_table(ctypes.byref(d), p, p, p, None) == vq.EUNSUPPORTED
+    assert L.commvq_value_reduce_workspace_size(ctypes.byref(d), 64) == 0
+    assert L.commvq_value_reduce(ctypes.byref(d), p, p, p, p, p, 64, 64, p, 1 << 20, p, None) == vq.EUNSUPPORTED
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, 0, None) == vq.EUNSUPPORTED
+    assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, p, ctypes.c_void_p(0x100000), None) == vq.EUNSUPPORTED
+    # mixed shapes stay unsupported
+    for g, n in ((2, 256), (16, 64), (4, 64)):
+        dd = vq.make_dims(1, 32, 8, 1, n_groups=g, n_codes=n)
+        assert _attn(dd, **ALL) == vq.EUNSUPPORTED, (g, n)
+    # misaligned records are rejected before any launch
+    ws = vq.attn_decode_workspace_size(d, 64)
+    st = _attn(d, **dict(ALL, kc=ctypes.c_void_p(0x1004), max_len=64, total=64, rope_pos=64, ws_bytes=ws))
+    assert st == vq.EINVAL

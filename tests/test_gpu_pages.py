@@ -1,0 +1,105 @@
+"""GPU parity of the bit-packed layout (one index per 64 dims, N = 64 codewords, R residual rounds: the
+CommVQ pages' own code shape) against the fp64 oracle, through the C ABI.
+
+Same bars as the byte layout: per (b, q head) output row, max_i |gpu - oracle| / max_i |oracle| <= 2e-3
+(fp16 codebooks), and the unpack of the bit-packed records compared bit-exactly with the oracle's.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+THREADS = 16
+
+
+@pytest.fixture(scope="module")
+def vq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vector_quantized_kv_amd as m
+    m.lib()
+    return m
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rowwise_rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    num = np.abs(got - ref).reshape(-1, ref.shape[-1]).max(-1)
+    den = np.abs(ref).reshape(-1, ref.shape[-1]).max(-1)
+    den = np.where(den == 0, 1.0, den)
+    return (num / den).max()
+
+
+def pages_cfg(name, B, lengths, R, seed, n_kv=2):
+    return workloads.custom(name, B, 4 * n_kv, n_kv, lengths, R, "float16", seed, n_groups=2, n_codes=64)
+
+
+@pytest.mark.parametrize("R", [1, 3, 4, 5, 11, 21, 32])
+def test_pages_unpack_bit_exact(vq, R):
+    cfg = pages_cfg(f"unpack_r{R}", 2, (777, 1), R, 300 + R)
+    announce(f"debug_unpack bit-packed R={R}")
+    inp = workloads.make_inputs(cfg)
+    d = vq.dims_of(cfg)
+    T = int(inp["total_tokens"])
+    for key in ("k_codes", "v_codes"):
+        words = torch.from_numpy(inp[key].view(np.int32)).cuda()
+        got = vq.debug_unpack(d, words, T)
+        torch.cuda.synchronize()
+        ref = oracle.unpack_bits(oracle.dims_of(cfg), inp[key], T)
+        np.testing.assert_array_equal(got.cpu().numpy(), ref.astype(np.int32))
+
+
+def check_attn(vq, cfg, inp, repeat=1):
+    layer = vq.Layer(vq.dims_of(cfg), inp)
+    outs = []
+    for _ in range(repeat):
+        outs.append(layer.attn_decode().clone())
+    torch.cuda.synchronize()
+    got = outs[0].cpu().numpy()
+    for o in outs[1:]:  # the arrival counters reset: a repeated call gives the same bits
+        np.testing.assert_array_equal(o.cpu().numpy(), got)
+    ref = oracle.run_config(cfg, inp, n_threads=THREADS)
+    assert np.all(np.isfinite(got))
+    for b, L in enumerate(inp["seq_len"]):
+        if L == 0:
+            assert np.all(got[b] == 0.0)
+    err = rowwise_rel_err(got, ref)
+    print(f"{cfg.name}: max row-relative error {err:.3e} (tol {TOL})", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("name", list(workloads.PAGES_CONFIGS))
+def test_pages_attn_matches_oracle_configs(vq, name):
+    cfg = workloads.PAGES_CONFIGS[name]
+    announce(f"attn_decode bit-packed {name}")
+    check_attn(vq, cfg, workloads.make_inputs(cfg), repeat=2)
+
+
+PAGES_EDGE = [
+    # name, B, lengths, R
+    ("pages_r1_ragged", 4, (1, 64, 65, 3000), 1),        # one pass per kind, three zero-row residuals
+    ("pages_r4_whole_pass", 2, (513, 4096), 4),          # exactly one full pass per kind
+    ("pages_r5_empty_seq", 3, (700, 0, 2049), 5),        # a one-residual last pass; an empty sequence
+    ("pages_r13_ragged", 2, (4097, 123), 13),
+    ("pages_r11_split_boundary", 2, (2048, 4096), 11),
+    ("pages_r32_max", 1, (5000,), 32),                   # the largest R: twelve-word records
+    ("pages_r21_long_merge", 1, (300000,), 21),          # more than 32 splits per (sequence, KV head)
+]
+
+
+@pytest.mark.parametrize("name,B,lengths,R", PAGES_EDGE)
+def test_pages_attn_edge_cases(vq, name, B, lengths, R):
+    announce(f"attn_decode bit-packed edge {name} lengths={lengths} R={R}")
+    cfg = pages_cfg(name, B, lengths, R, 400 + len(name) + R)
+    check_attn(vq, cfg, workloads.make_inputs(cfg))

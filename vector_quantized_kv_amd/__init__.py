@@ -226,6 +226,12 @@ def debug_unpack(d: Dims, codes, total_tokens: int, out=None, stream=None):
     return out
 
 
+def _code_array(a):
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    return a.view(np.int32) if a.dtype == np.uint32 else a
+
+
 class Layer:
     """Device-resident inputs of one decode step for one layer (helper for tests and benchmarks)."""
 
@@ -236,8 +242,9 @@ class Layer:
         self.q = torch.from_numpy(inputs["q"]).to(device=device, dtype=dt)
         self.k_cb = torch.from_numpy(inputs["k_cb"]).to(device=device, dtype=dt)
         self.v_cb = torch.from_numpy(inputs["v_cb"]).to(device=device, dtype=dt)
-        self.k_codes = torch.from_numpy(inputs["k_codes"]).to(device)
-        self.v_codes = torch.from_numpy(inputs["v_codes"]).to(device)
+        # bit-packed records (uint32 words) travel as int32 tensors of the same bits
+        self.k_codes = torch.from_numpy(_code_array(inputs["k_codes"])).to(device)
+        self.v_codes = torch.from_numpy(_code_array(inputs["v_codes"])).to(device)
         self.seq_start = torch.from_numpy(inputs["seq_start"]).to(device)
         self.seq_len = torch.from_numpy(inputs["seq_len"]).to(device)
         self.max_len = int(inputs["max_len"])

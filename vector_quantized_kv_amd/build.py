@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcommvq.so")
-SOURCES = ["api.cpp", "kernels.hip", "attn.hip"]
+SOURCES = ["api.cpp", "kernels.hip", "attn.hip", "attn_wide.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

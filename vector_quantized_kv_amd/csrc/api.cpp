@@ -36,7 +36,11 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shape checks shared by every entry point.
+bool packed_family(const commvq_dims* d) { return d->n_groups == kWideGroups && d->n_codes == kWideCodes; }
+
+// Shape checks shared by every entry point. Two index layouts are implemented: one byte per index
+// (n_groups 16, n_codes 256, R 1 or 2, fp16 or fp32) and bit-packed records (n_groups 2, n_codes 64,
+// R 1 .. kWideMaxResiduals, fp16).
 int check_dims(const commvq_dims* d) {
   if (!d) return fail(COMMVQ_EINVAL, "dims is NULL");
   if (d->batch < 1) return fail(COMMVQ_EINVAL, "batch = %d must be >= 1", d->batch);
@@ -48,14 +52,30 @@ int check_dims(const commvq_dims* d) {
     return fail(COMMVQ_EUNSUPPORTED, "q heads per KV head = %d; only %d is implemented",
                 d->n_q_heads / d->n_kv_heads, kGqa);
   if (d->head_dim != kHeadDim) return fail(COMMVQ_EUNSUPPORTED, "head_dim = %d; only %d is implemented", d->head_dim, kHeadDim);
-  if (d->n_groups != kGroups) return fail(COMMVQ_EUNSUPPORTED, "n_groups = %d; only %d is implemented", d->n_groups, kGroups);
-  if (d->n_codes != kCodes) return fail(COMMVQ_EUNSUPPORTED, "n_codes = %d; only %d is implemented", d->n_codes, kCodes);
   if (d->n_residuals < 1) return fail(COMMVQ_EINVAL, "n_residuals = %d must be >= 1", d->n_residuals);
-  if (d->n_residuals > 2) return fail(COMMVQ_EUNSUPPORTED, "n_residuals = %d; only 1 and 2 are implemented", d->n_residuals);
   if (d->dtype != COMMVQ_F16 && d->dtype != COMMVQ_F32) return fail(COMMVQ_EINVAL, "dtype = %d is not a commvq_dtype", d->dtype);
+  if (packed_family(d)) {
+    if (d->n_residuals > kWideMaxResiduals)
+      return fail(COMMVQ_EUNSUPPORTED, "n_residuals = %d; the bit-packed layout implements 1 .. %d", d->n_residuals,
+                  kWideMaxResiduals);
+    if (d->dtype != COMMVQ_F16) return fail(COMMVQ_EUNSUPPORTED, "the bit-packed layout implements fp16 codebooks only");
+  } else {
+    if (d->n_groups != kGroups || d->n_codes != kCodes)
+      return fail(COMMVQ_EUNSUPPORTED, "(n_groups, n_codes) = (%d, %d); only (%d, %d) and (%d, %d) are implemented",
+                  d->n_groups, d->n_codes, kGroups, kCodes, kWideGroups, kWideCodes);
+    if (d->n_residuals > 2)
+      return fail(COMMVQ_EUNSUPPORTED, "n_residuals = %d; the byte layout implements 1 and 2", d->n_residuals);
+  }
   if (!(d->rope_base > 1.0)) return fail(COMMVQ_EINVAL, "rope_base = %g must be > 1", d->rope_base);
   if (!(d->softmax_scale == d->softmax_scale) || d->softmax_scale == 0.f)
     return fail(COMMVQ_EINVAL, "softmax_scale must be finite and non-zero");
+  return COMMVQ_OK;
+}
+
+// Entry points implemented for the byte layout only.
+int check_byte_dims(const commvq_dims* d, const char* what) {
+  if (int st = check_dims(d)) return st;
+  if (packed_family(d)) return fail(COMMVQ_EUNSUPPORTED, "%s is implemented for the byte layout only", what);
   return COMMVQ_OK;
 }
 
@@ -119,7 +139,7 @@ int commvq_rope_table(const commvq_dims* d, int32_t n_positions, void* table, si
 }
 
 int commvq_qcodebook_table(const commvq_dims* d, const void* q, const void* k_codebook, void* table, void* stream) {
-  if (int st = check_dims(d)) return st;
+  if (int st = check_byte_dims(d, "qcodebook_table")) return st;
   if (!q || !k_codebook || !table) return fail(COMMVQ_EINVAL, "q, k_codebook and table must be non-NULL");
   return hip_status(launch_qtable(d->dtype, d->n_residuals, d->batch, d->n_q_heads, d->n_kv_heads, q, k_codebook,
                                   table, static_cast<hipStream_t>(stream)),
@@ -169,23 +189,27 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
   a.n_q_heads = d->n_q_heads;
   a.n_kv_heads = d->n_kv_heads;
   a.scale = d->softmax_scale;
+  a.n_residuals = d->n_residuals;
+  a.record_words = wide_record_words(d->n_residuals);
   a.counters = static_cast<uint32_t*>(workspace);
   a.part_ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + w.ml_offset);
   a.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + w.o_offset);
   a.out = out;
+  if (packed_family(d))
+    return hip_status(launch_attn_wide(d->batch, a, static_cast<hipStream_t>(stream)), "attn_decode launch");
   return hip_status(launch_attn(d->dtype, d->n_residuals, d->batch, a, static_cast<hipStream_t>(stream)),
                     "attn_decode launch");
 }
 
 size_t commvq_value_reduce_workspace_size(const commvq_dims* d, int32_t max_len) {
-  if (check_dims(d) != COMMVQ_OK || max_len < 0) return 0;
+  if (check_byte_dims(d, "value_reduce") != COMMVQ_OK || max_len < 0) return 0;
   return part_bytes(d, max_len);
 }
 
 int commvq_value_reduce(const commvq_dims* d, const float* p, const uint8_t* v_codes, const void* v_codebook,
                         const int64_t* seq_start, const int32_t* seq_len, int32_t max_len, int64_t total_tokens,
                         void* workspace, size_t ws_bytes, float* out, void* stream) {
-  if (int st = check_dims(d)) return st;
+  if (int st = check_byte_dims(d, "value_reduce")) return st;
   if (!p || !v_codes || !v_codebook || !seq_start || !seq_len || !out)
     return fail(COMMVQ_EINVAL, "a required pointer is NULL");
   if (max_len < 0) return fail(COMMVQ_EINVAL, "max_len = %d must be >= 0", max_len);
@@ -212,7 +236,7 @@ int commvq_value_reduce(const commvq_dims* d, const float* p, const uint8_t* v_c
 
 int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebook, int64_t n_tokens, uint8_t* codes,
                          int64_t total_rows, int64_t first_row, void* stream) {
-  if (int st = check_dims(d)) return st;
+  if (int st = check_byte_dims(d, "encode_greedy")) return st;
   if (n_tokens < 0) return fail(COMMVQ_EINVAL, "n_tokens = %lld must be >= 0", (long long)n_tokens);
   if (first_row < 0 || total_rows < 0 || first_row + n_tokens > total_rows)
     return fail(COMMVQ_EINVAL, "rows [%lld, %lld) do not fit total_rows = %lld", (long long)first_row,
@@ -228,7 +252,7 @@ int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebo
 
 int commvq_codebook_update(const commvq_dims* d, const void* x, const uint8_t* codes, int64_t n_tokens,
                            const void* codebook_in, void* codebook_out, void* stream) {
-  if (int st = check_dims(d)) return st;
+  if (int st = check_byte_dims(d, "codebook_update")) return st;
   if (n_tokens < 0) return fail(COMMVQ_EINVAL, "n_tokens = %lld must be >= 0", (long long)n_tokens);
   if (!codebook_in || !codebook_out) return fail(COMMVQ_EINVAL, "codebook_in and codebook_out must be non-NULL");
   if (n_tokens > 0 && (!x || !codes)) return fail(COMMVQ_EINVAL, "x and codes must be non-NULL");
@@ -247,6 +271,11 @@ int commvq_debug_unpack(const commvq_dims* d, const uint8_t* codes, int64_t tota
   if (!codes || !out) return fail(COMMVQ_EINVAL, "codes and out must be non-NULL");
   if (total_tokens < 0) return fail(COMMVQ_EINVAL, "total_tokens = %lld must be >= 0", (long long)total_tokens);
   if (!aligned16(codes)) return fail(COMMVQ_EINVAL, "codes must be 16-byte aligned");
+  if (packed_family(d))
+    return hip_status(launch_debug_unpack_bits(d->n_residuals, d->n_kv_heads, total_tokens,
+                                               reinterpret_cast<const uint32_t*>(codes), out,
+                                               static_cast<hipStream_t>(stream)),
+                      "debug_unpack launch");
   return hip_status(launch_debug_unpack(d->n_residuals, d->n_kv_heads, total_tokens, codes, out,
                                         static_cast<hipStream_t>(stream)),
                     "debug_unpack launch");

@@ -27,6 +27,15 @@ constexpr int kCounterBytes = 256;  // attention workspace head: per-(b, kv) arr
 constexpr int kAttnMaxSplits = 8192;  // splits per sequence the last-workgroup merge can hold in LDS
 constexpr int kCUs = 256;             // compute units the split sizing aims to fill (one workgroup each)
 
+// Bit-packed family (one index per 64 dims): G = 2 groups, N = 64 codewords, 6-bit indices packed per
+// token into ceil(6 R G / 32) little-endian 32-bit words, index (r, g) at bit 6 (r G + g).
+constexpr int kWideGroups = 2;
+constexpr int kWideCodes = 64;
+constexpr int kWideBits = 6;
+constexpr int kWideMaxResiduals = 32;
+constexpr int kWideResPerPass = 4;  // residual codebooks per attention pass (one 64 KiB LDS slot)
+inline int wide_record_words(int R) { return (kWideBits * R * kWideGroups + 31) / 32; }
+
 // Attention workgroup: fp16 storage runs 8 waves (two per SIMD) over two 64 KiB codebook slots; fp32
 // storage runs 4 waves over one 128 KiB slot. Either way one workgroup owns a CU's LDS.
 inline int attn_waves(int dtype) { return dtype == COMMVQ_F16 ? 8 : 4; }
@@ -71,6 +80,8 @@ struct AttnArgs {
   int32_t n_q_heads;
   int32_t n_kv_heads;
   float scale;
+  int32_t n_residuals;   // bit-packed family only
+  int32_t record_words;  // bit-packed family only: 32-bit words per token record
   uint32_t* counters;  // [B][Hkv], zero between calls
   float2* part_ml;     // [B][Hq][n_splits]: (m, l) of each split
   float* part_o;       // [B][Hq][n_splits][D]: unnormalised output of each split
@@ -95,6 +106,7 @@ hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hi
 hipError_t launch_qtable(int dtype, int R, int B, int Hq, int Hkv, const void* q, const void* kcb, void* out,
                          hipStream_t s);
 hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_wide(int B, const AttnArgs& a, hipStream_t s);
 hipError_t launch_value_reduce(int dtype, int R, int B, const ValueReduceArgs& a, float* out, hipStream_t s);
 hipError_t launch_encode_greedy(int dtype, int R, int Hkv, const void* x, const void* cb, int64_t n, uint8_t* codes,
                                 int64_t total_rows, int64_t first_row, hipStream_t s);
@@ -102,5 +114,7 @@ hipError_t launch_codebook_update(int dtype, int R, int Hkv, const void* x, cons
                                   const void* cb_in, void* cb_out, hipStream_t s);
 hipError_t launch_debug_unpack(int R, int Hkv, int64_t total_tokens, const uint8_t* codes, int32_t* out,
                                hipStream_t s);
+hipError_t launch_debug_unpack_bits(int R, int Hkv, int64_t total_tokens, const uint32_t* words, int32_t* out,
+                                    hipStream_t s);
 
 }  // namespace commvq

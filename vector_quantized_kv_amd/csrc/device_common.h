@@ -21,6 +21,34 @@ __device__ __forceinline__ uint4 load_code_record(const uint8_t* codes, int64_t 
   return *reinterpret_cast<const uint4*>(codes + ((static_cast<int64_t>(kv) * R + r) * total_tokens + row) * 16);
 }
 
+// Bit-packed records (one index per 64 dims, N = 64): a token's R x 2 six-bit indices form one
+// little-endian bitstream of 32-bit words, index (r, g) at bit 6 (2 r + g). Kernels read it in windows
+// of kWideResPerPass residuals: window c starts at bit 6 * 2 * kWideResPerPass * c, inside words
+// packed_window_word(c) and the one after it (48 bits from a 0- or 16-bit offset: always two words).
+__device__ __forceinline__ int packed_window_word(int c) { return (kWideBits * kWideGroups * kWideResPerPass * c) >> 5; }
+__device__ __forceinline__ int packed_window_shift(int c) {
+  return (kWideBits * kWideGroups * kWideResPerPass * c) & 31;
+}
+// (x0, x1) = bits sh .. sh + 31 and sh + 32 .. of the word pair (lo, hi).
+__device__ __forceinline__ void packed_window(uint32_t lo, uint32_t hi, int sh, uint32_t& x0, uint32_t& x1) {
+  x0 = __builtin_amdgcn_alignbit(hi, lo, sh);
+  x1 = hi >> sh;
+}
+// Index F of a window (F = 2 rho + g for residual kWideResPerPass * c + rho, group g).
+template <int F>
+__device__ __forceinline__ uint32_t packed_index(uint32_t x0, uint32_t x1) {
+  constexpr int bit = kWideBits * F;
+  constexpr uint32_t mask = (1u << kWideBits) - 1;
+  if constexpr (bit + kWideBits <= 32) {
+    return (x0 >> bit) & mask;
+  } else if constexpr (bit >= 32) {
+    return (x1 >> (bit - 32)) & mask;
+  } else {
+    return ((x0 >> bit) | (x1 << (32 - bit))) & mask;
+  }
+}
+static_assert(kWideBits * kWideGroups * kWideResPerPass <= 48, "a window fits two words from a 16-bit offset");
+
 // row_ror DPP: lane l of each 16-lane row reads lane (l + n) mod 16 of the same row. Every source lane
 // exists, so bound_ctrl is irrelevant to the result; setting it lets the compiler fold the move into the
 // consuming add or max.

@@ -237,6 +237,49 @@ hipError_t launch_debug_unpack(int R, int Hkv, int64_t total_tokens, const uint8
   return hipGetLastError();
 }
 
+// Bit-packed records: one thread per (kv, token, window c); it reads the window's two words and unpacks
+// them with the same window functions the attention kernel uses. out is [Hkv][R][T][2] int32.
+__global__ void debug_unpack_bits_kernel(const uint32_t* words, int64_t total_tokens, int R, int Wd, int n_windows,
+                                         int64_t n_items, int32_t* out) {
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (item >= n_items) return;
+  const int c = static_cast<int>(item % n_windows);
+  const int64_t kt = item / n_windows;  // kv * T + t
+  const int64_t kv = kt / total_tokens, t = kt % total_tokens;
+  const uint32_t* rec = words + kt * Wd;
+  const int w0 = packed_window_word(c);
+  uint32_t x0, x1;
+  packed_window(rec[w0], rec[min(w0 + 1, Wd - 1)], packed_window_shift(c), x0, x1);
+  uint32_t idx[2 * kWideResPerPass];
+  idx[0] = packed_index<0>(x0, x1);
+  idx[1] = packed_index<1>(x0, x1);
+  idx[2] = packed_index<2>(x0, x1);
+  idx[3] = packed_index<3>(x0, x1);
+  idx[4] = packed_index<4>(x0, x1);
+  idx[5] = packed_index<5>(x0, x1);
+  idx[6] = packed_index<6>(x0, x1);
+  idx[7] = packed_index<7>(x0, x1);
+  static_assert(kWideResPerPass == 4, "eight indices per window");
+#pragma unroll
+  for (int rho = 0; rho < kWideResPerPass; ++rho) {
+    const int r = kWideResPerPass * c + rho;
+    if (r >= R) break;
+#pragma unroll
+    for (int g = 0; g < kWideGroups; ++g)
+      out[((kv * R + r) * total_tokens + t) * kWideGroups + g] = static_cast<int32_t>(idx[2 * rho + g]);
+  }
+}
+
+hipError_t launch_debug_unpack_bits(int R, int Hkv, int64_t total_tokens, const uint32_t* words, int32_t* out,
+                                    hipStream_t s) {
+  const int n_windows = (R + kWideResPerPass - 1) / kWideResPerPass;
+  const int64_t n = static_cast<int64_t>(Hkv) * total_tokens * n_windows;
+  if (n == 0) return hipSuccess;
+  debug_unpack_bits_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(
+      words, total_tokens, R, wide_record_words(R), n_windows, n, out);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------------- greedy residual encoder
 // Writes the code indices of new tokens ("1-bit quantization" tag page, CommVQ abstract: keys and values
 // are encoded into indices of an additive codebook; pith.science verdict for arXiv 2506.18879,
