@@ -29,22 +29,29 @@ import numpy as np  # noqa: E402
 import workloads  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+# LDS: 256 CUs x 256 B per clock x 2.4 GHz (a broadcast ds_read_b128 wave instruction, 1 KiB, takes 4 clocks
+# per CU); random 16-byte gathers measured at 12.04 clocks per 1 KiB wave instruction (bank conflicts)
+LDS_PEAK_TBPS = 256 * 256 * 2.4e9 / 1e12
+LDS_GATHER_TBPS = 256 * 1024 / 12.04 * 2.4e9 / 1e12
 PROFILES = os.path.join(ROOT, "profiles")
-# sources that determine the fused attention kernel's memory traffic (split sizing, layout, kernel body)
-KERNEL_SOURCES = [os.path.join(ROOT, "vector_quantized_kv_amd", "csrc", f)
-                  for f in ("attn.hip", "commvq_internal.h", "device_common.h", "api.cpp")]
+# sources that determine each attention kernel's memory traffic (split sizing, layout, kernel body)
+_CSRC = os.path.join(ROOT, "vector_quantized_kv_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
+                  ("attn.hip", "attn_common.h", "commvq_internal.h", "device_common.h", "api.cpp")]
+WIDE_KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
+                       ("attn_wide.hip", "attn_common.h", "commvq_internal.h", "device_common.h", "api.cpp")]
 KERNEL_NAME = "attn_kernel"
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(config_name: str):
+def read_traffic(config_name: str, sources=None):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches the current kernels."""
     path = os.path.join(PROFILES, f"traffic_attn_decode_{config_name}.txt")
     if not os.path.exists(path):
@@ -55,7 +62,7 @@ def read_traffic(config_name: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -116,7 +123,7 @@ def profile_run(names, launches: int):
     import torch
     import vector_quantized_kv_amd as vq
     for name in names:
-        cfg = workloads.CONFIGS[name]
+        cfg = workload(name)
         d = vq.dims_of(cfg)
         base = workloads.make_inputs(cfg)
         per_layer = algorithmic_bytes(cfg, int(base["total_tokens"]))["total"]
@@ -212,6 +219,7 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
         graph_ms = a.elapsed_time(b) / (reps * layers)
 
     per_step_ms = total_ms / steps
+    print(f"[bench] {cfg.name}: {layers} layers, {launch_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
     L = total
     res = {
         "config": cfg.name, "tokens": L, "layers_rotated": layers, "ms_per_step": per_step_ms,
@@ -223,6 +231,16 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
         "pct_hbm_peak_code_stream": 100.0 * per_layer["codes"] / (launch_ms * 1e-3) * 1e-9 / HBM_PEAK_GBPS,
         "bytes": per_layer, "max_row_rel_err_vs_oracle": check_err,
     }
+    if cfg.packed:
+        # bit-packed records: every token gathers, per residual and group, its 128-byte fp16 codeword row
+        # from LDS for keys and again for values; that LDS stream, not HBM, bounds the kernel
+        gathered = 2 * cfg.n_kv_heads * L * cfg.n_residuals * cfg.n_groups * cfg.group_dim * 2
+        tbps = gathered / (launch_ms * 1e-3) * 1e-12
+        res["hbm_traffic_bytes_per_launch"] = read_traffic(cfg.name, WIDE_KERNEL_SOURCES)
+        res["lds_roofline"] = {"bound": "lds", "gathered_bytes_per_launch": gathered, "achieved": tbps,
+                               "unit": "TB/s", "peak": LDS_PEAK_TBPS, "frac": tbps / LDS_PEAK_TBPS,
+                               "random_gather_ceiling": LDS_GATHER_TBPS,
+                               "frac_of_random_gather_ceiling": tbps / LDS_GATHER_TBPS}
     del Ls
     torch.cuda.empty_cache()
     return res, base
@@ -265,13 +283,18 @@ def codebook_tools_timing(reps: int = 3):
     }
 
 
+def workload(name: str):
+    return workloads.CONFIGS[name] if name in workloads.CONFIGS else workloads.PAGES_CONFIGS[name]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama8b_128k_r2", help="primary workload (value, roofline)")
-    ap.add_argument("--also", default="llama8b_128k_r1", help="comma list of extra workloads reported in variants")
+    ap.add_argument("--also", default="llama8b_128k_r1,pages_g64_r11_128k,pages_g64_r21_128k",
+                    help="comma list of extra workloads reported in variants")
     ap.add_argument("--layers", type=int, default=0, help="distinct layer buffers to rotate (0: >= 1 GiB)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -296,8 +319,8 @@ def main():
     prim, base = run_config(cfg, args.steps, args.warmup, args.layers, not args.no_graph, args.check)
     variants = {cfg.name: prim}
     for name in [s for s in args.also.split(",") if s and s != cfg.name]:
-        variants[name], _ = run_config(workloads.CONFIGS[name], args.steps, args.warmup, args.layers,
-                                       not args.no_graph, args.check)
+        variants[name], _ = run_config(workload(name), args.steps, args.warmup, args.layers, not args.no_graph,
+                                       args.check)
 
     achieved = prim["bytes"]["codes"] / (prim["us_per_launch"] * 1e-6) * 1e-9
     traffic = read_traffic(cfg.name)
@@ -320,6 +343,7 @@ def main():
         "variants": variants,
         "hbm_read_stream_GBps": read_stream_gbps(),
         "kernel_source_sha256_16": kernel_source_hash(),
+        "wide_kernel_source_sha256_16": kernel_source_hash(WIDE_KERNEL_SOURCES),
     }
     line["codebook_tools"] = codebook_tools_timing()
     if not args.no_cpu_baseline:

@@ -95,6 +95,8 @@ PAGES_CONFIGS: Dict[str, Config] = {
                                 description="Llama-3.1-8B layer, L=32768, g=64, N'=64, R=21 (1.97 bit), fp16"),
     "pages_g64_r21_128k": Config("pages_g64_r21_128k", 1, 32, 8, (131072,), 21, "float16", 23, n_groups=2,
                                  n_codes=64, description="Llama-3.1-8B layer, L=131072, g=64, N'=64, R=21, fp16"),
+    "pages_g64_r11_128k": Config("pages_g64_r11_128k", 1, 32, 8, (131072,), 11, "float16", 24, n_groups=2,
+                                 n_codes=64, description="Llama-3.1-8B layer, L=131072, g=64, N'=64, R=11, fp16"),
 }
 
 
