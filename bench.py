@@ -305,8 +305,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is described in the "
-                                   "design notes and not implemented", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "bench.py measures one GPU; sharding across GPUs is not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch

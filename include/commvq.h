@@ -31,8 +31,9 @@
  *
  * Bit-packed layout (the CommVQ pages' own code shape: one index shared by 64 dims, N = 64 codewords,
  * R up to 32 residual rounds, e.g. R = 11 for about 1 bit per scalar and R = 21 for about 2; average
- * bits R log2(N) / 64 per scalar: pith.science verdict for arXiv 2506.18879, key_machinery; the arXiv
- * listing's Limitations section names R = 11 and 21). Selected by n_groups = 2, n_codes = 64:
+ * bits R log2(N) / 64 per scalar: pith.science verdict for arXiv 2506.18879, key_machinery and the
+ * referee report's minor comments; the CommVQ summary page, Limitations, names R = 11 and 21).
+ * Selected by n_groups = 2, n_codes = 64:
  *   k_codebook, v_codebook [Hkv][2][R][64][64]   as above with W = 64 (group g holds pairs 32g .. 32g+31)
  *   k_codes, v_codes       [Hkv][T][ceil(12 R / 32)] little-endian uint32 words, passed through the
  *                          uint8_t pointer: token t's R x 2 six-bit indices as one bitstream, index

@@ -1,12 +1,12 @@
-// Decode-step attention over a CommVQ cache in the papers' own code shape, on gfx950.
+// Decode-step attention over a CommVQ cache in the pages' own code shape, on gfx950.
 //
 // Same computation as attn_kernel (score = scale * sum_j Re(conj(q_j) khat_{t,j} e^{i t theta_j}),
 // out = softmax-weighted sum of vhat), for the setting the CommVQ pages evaluate: one code index shared by
 // the 64 dims of a half head (G = 2 groups of 64 dims), N = 64 codewords per residual codebook (6-bit
-// indices), and many residual rounds (R = 11 gives about 1 bit per scalar, R = 21 about 2; avg bits
-// R log2(N) / 64: pith.science verdict for arXiv 2506.18879, key_machinery, and the review's note on the
-// bit-rate formula; the Limitations section of the arXiv listing names R = 11 and R = 21). A token's R x G
-// indices are one little-endian bitstream of 32-bit words, index (r, g) at bit 6 (r G + g).
+// indices), and many residual rounds. The average is R log2(N) / g bits per scalar (pith.science verdict
+// for arXiv 2506.18879, key_machinery; its referee report's minor comments give g = 64, N' = 64), so
+// R = 11 gives about 1 bit and R = 21 about 2 (the CommVQ summary page, Limitations, names these two).
+// A token's R x G indices are one little-endian bitstream of 32-bit words, index (r, g) at bit 6 (r G + g).
 //
 // The codebooks (R x 16 KiB per KV head for keys, as much for values) do not fit in LDS, so the kernel
 // runs in passes of kRes residuals: key passes c = 0 .. nch-1, then the wave softmax, then value passes.
