@@ -74,7 +74,11 @@ __device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[kRes], const h
     k0 = mfma(ident, cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), k0);
     k1 = mfma(ident, cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), k1);
   }
-  auto pk = [](float x, float y) { return __builtin_bit_cast(uint32_t, (h2){(f16)x, (f16)y}); };
+  // one v_cvt_pk_f16_f32 (round to nearest even) per pair
+  auto pk = [](float x, float y) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, h2));
+  };
   key_step<G>(make_uint4(pk(k0[0], k0[1]), pk(k0[2], k0[3]), pk(k1[0], k1[1]), pk(k1[2], k1[3])), F, A0, A1, acc);
 }
 
