@@ -103,3 +103,11 @@ def test_pages_attn_edge_cases(vq, name, B, lengths, R):
     announce(f"attn_decode bit-packed edge {name} lengths={lengths} R={R}")
     cfg = pages_cfg(name, B, lengths, R, 400 + len(name) + R)
     check_attn(vq, cfg, workloads.make_inputs(cfg))
+
+
+@pytest.mark.parametrize("n_kv,B,lengths,R", [(1, 1, (2500,), 11), (3, 2, (1500, 777), 21)])
+def test_pages_attn_kv_head_counts(vq, n_kv, B, lengths, R):
+    # one KV head (4 q heads), and an odd count that does not divide the 8 XCDs the grid is dealt to
+    announce(f"attn_decode bit-packed n_kv={n_kv} lengths={lengths} R={R}")
+    cfg = pages_cfg(f"pages_kv{n_kv}", B, lengths, R, 500 + n_kv, n_kv=n_kv)
+    check_attn(vq, cfg, workloads.make_inputs(cfg))
