@@ -111,3 +111,24 @@ def test_pages_attn_kv_head_counts(vq, n_kv, B, lengths, R):
     announce(f"attn_decode bit-packed n_kv={n_kv} lengths={lengths} R={R}")
     cfg = pages_cfg(f"pages_kv{n_kv}", B, lengths, R, 500 + n_kv, n_kv=n_kv)
     check_attn(vq, cfg, workloads.make_inputs(cfg))
+
+
+def test_pages_split_size_does_not_change_the_result(vq):
+    # one sequence alone (512-token splits) and as 8 copies in one batch (2048-token splits)
+    announce("bit-packed split-size independence")
+    L, B = 8192, 8
+    cfg1 = pages_cfg("pages_split_b1", 1, (L,), 11, 91, n_kv=8)
+    inp1 = workloads.make_inputs(cfg1)
+    cfg8 = pages_cfg("pages_split_b8", B, (L,) * B, 11, 91, n_kv=8)
+    inp8 = dict(inp1, q=np.repeat(inp1["q"], B, axis=0), seq_start=np.zeros(B, np.int64),
+                seq_len=np.full(B, L, np.int32))
+    out = []
+    for cfg, inp in ((cfg1, inp1), (cfg8, inp8)):
+        layer = vq.Layer(vq.dims_of(cfg), inp)
+        out.append(layer.attn_decode().cpu().numpy())
+    for b in range(B):
+        np.testing.assert_array_equal(out[1][b], out[1][0])
+    err = rowwise_rel_err(out[1][0], out[0][0].astype(np.float64))
+    print(f"bit-packed split 512 vs 2048 tokens: max row-relative difference {err:.3e}", flush=True)
+    assert err <= TOL
+    assert rowwise_rel_err(out[0], oracle.run_config(cfg1, inp1, n_threads=THREADS)) <= TOL

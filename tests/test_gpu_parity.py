@@ -283,3 +283,31 @@ def test_fit_codebook_r1_error_never_increases(vq):
     print("fit errors", errs, flush=True)
     assert all(b <= a * (1 + 1e-6) for a, b in zip(errs, errs[1:]))
     assert errs[-1] < 0.9 * errs[0]
+
+
+def split_tokens(B, L, n_kv):
+    """The library's split sizing: 512 tokens per block of 8 waves x 64, 1..8 blocks per wave, ~one item per CU."""
+    blocks = max(1, min(8, -(-(L * B * n_kv) // (256 * 512))))
+    return 512 * blocks
+
+
+@pytest.mark.parametrize("R", [1, 2])
+def test_split_size_does_not_change_the_result(vq, R):
+    # one sequence alone (512-token splits) and as 8 copies in one batch (2048-token splits)
+    announce(f"split-size independence R={R}")
+    L, B = 8192, 8
+    cfg1 = workloads.custom("split_b1", 1, 32, 8, (L,), R, "float16", 77 + R)
+    inp1 = workloads.make_inputs(cfg1)
+    cfg8 = workloads.custom("split_b8", B, 32, 8, (L,) * B, R, "float16", 77 + R)
+    inp8 = dict(inp1, q=np.repeat(inp1["q"], B, axis=0), seq_start=np.zeros(B, np.int64),
+                seq_len=np.full(B, L, np.int32))
+    assert split_tokens(1, L, 8) != split_tokens(B, L, 8)
+    out1 = run_attn(vq, cfg1, inp1)
+    out8 = run_attn(vq, cfg8, inp8)
+    for b in range(B):
+        np.testing.assert_array_equal(out8[b], out8[0])  # same inputs, same split: same bits
+    err = rowwise_rel_err(out8[0], out1[0].astype(np.float64))
+    print(f"split 512 vs 2048 tokens: max row-relative difference {err:.3e}", flush=True)
+    assert err <= TOL["float16"]
+    ref = oracle.run_config(cfg1, inp1, n_threads=THREADS)
+    assert rowwise_rel_err(out1, ref) <= TOL["float16"]
