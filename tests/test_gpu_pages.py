@@ -132,3 +132,14 @@ def test_pages_split_size_does_not_change_the_result(vq):
     print(f"bit-packed split 512 vs 2048 tokens: max row-relative difference {err:.3e}", flush=True)
     assert err <= TOL
     assert rowwise_rel_err(out[0], oracle.run_config(cfg1, inp1, n_threads=THREADS)) <= TOL
+
+
+@pytest.mark.parametrize("R", [5, 21])
+def test_pages_attention_reads_every_value_index_back(vq, R):
+    # 64 one-token sequences: p = 1, and codeword l of residual r holds l in dim r of its group, so each output
+    # row is the token's stored value indices (read through the window unpack, the gathers and the value MFMAs)
+    from test_gpu_parity import read_indices_back
+    announce(f"bit-packed value indices through attention R={R}")
+    cfg = pages_cfg("pages_counting", 1, (3000,), R, 61 + R)
+    d = oracle.dims_of(cfg)
+    read_indices_back(vq, cfg, lambda words, T: oracle.unpack_bits(d, words, T))

@@ -311,3 +311,40 @@ def test_split_size_does_not_change_the_result(vq, R):
     assert err <= TOL["float16"]
     ref = oracle.run_config(cfg1, inp1, n_threads=THREADS)
     assert rowwise_rel_err(out1, ref) <= TOL["float16"]
+
+
+def counting_value_codebook(Hkv, G, R, N, W, dtype):
+    """Codeword l of residual r holds l in dim r of its group and zeros elsewhere: a decode reveals the indices."""
+    cb = np.zeros((Hkv, G, R, N, W), dtype=dtype)
+    for r in range(R):
+        cb[:, :, r, :, r] = np.arange(N, dtype=np.float32).astype(dtype)
+    return cb
+
+
+def read_indices_back(vq, cfg, unpack):
+    """64 one-token sequences at scattered rows: p = 1, so out = the decoded value, i.e. the stored indices."""
+    B = 64
+    inp = workloads.make_inputs(cfg)
+    T = int(inp["total_tokens"])
+    rows = (np.arange(B, dtype=np.int64) * 37 + 5) % T
+    G, R, N, W = cfg.n_groups, cfg.n_residuals, cfg.n_codes, cfg.group_dim
+    inp = dict(inp, v_cb=counting_value_codebook(cfg.n_kv_heads, G, R, N, W, np.dtype(cfg.dtype)),
+               q=np.repeat(inp["q"][:1], B, axis=0), seq_start=rows, seq_len=np.ones(B, np.int32),
+               max_len=np.int32(1))
+    cfgB = workloads.custom(cfg.name + "_b64", B, cfg.n_q_heads, cfg.n_kv_heads, (1,) * B, R, cfg.dtype, cfg.seed,
+                            n_groups=G, n_codes=N)
+    got = run_attn(vq, cfgB, inp)  # [B][Hq][D]
+    idx = unpack(inp["v_codes"], T)  # [Hkv][R][T][G]
+    for h in range(cfg.n_q_heads):
+        kv = h // 4
+        for r in range(R):
+            want = idx[kv, r][rows]  # [B][G]
+            np.testing.assert_array_equal(got[:, h, np.arange(G) * W + r], want.astype(np.float32))
+
+
+@pytest.mark.parametrize("dtype,R", [("float16", 1), ("float16", 2), ("float32", 2)])
+def test_attention_reads_every_value_index_back(vq, dtype, R):
+    announce(f"value indices through attention {dtype} R={R}")
+    cfg = workloads.custom("counting", 1, 8, 2, (3000,), R, dtype, 31 + R)
+    d = oracle.dims_of(cfg)
+    read_indices_back(vq, cfg, lambda codes, T: oracle.unpack(d, codes, T))
