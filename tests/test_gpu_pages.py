@@ -105,6 +105,14 @@ def test_pages_attn_edge_cases(vq, name, B, lengths, R):
     check_attn(vq, cfg, workloads.make_inputs(cfg))
 
 
+def test_pages_attn_ragged_batch(vq):
+    # 16 sequences of 4096 .. 65536 tokens at the Llama-3.1-8B layer shape (the byte layout's ragged16_r2)
+    announce("attn_decode bit-packed ragged batch of 16, R=11")
+    cfg = workloads.Config("pages_ragged16_r11", 16, 32, 8, None, 11, "float16", 25, n_groups=2, n_codes=64,
+                           ragged_range=(4096, 65536))
+    check_attn(vq, cfg, workloads.make_inputs(cfg))
+
+
 @pytest.mark.parametrize("n_kv,B,lengths,R", [(1, 1, (2500,), 11), (3, 2, (1500, 777), 21)])
 def test_pages_attn_kv_head_counts(vq, n_kv, B, lengths, R):
     # one KV head (4 q heads), and an odd count that does not divide the 8 XCDs the grid is dealt to
