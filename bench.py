@@ -247,9 +247,9 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
 
 
 def codebook_tools_timing(reps: int = 3):
-    """The two offline steps next to the decode path, at the 128K layer shape (8 KV heads, R = 2, fp16):
-    encoding every cached key of a 131072-token prefill with commvq_encode_greedy, and one codebook M-step
-    (commvq_codebook_update) over the same tokens. Per (token, KV head, group, round) the encoder evaluates
+    """The offline steps next to the decode path, at the 128K layer shape (8 KV heads, R = 2, fp16):
+    encoding every cached key of a 131072-token prefill with commvq_encode_greedy, one codebook M-step
+    (commvq_codebook_update) over the same tokens, and the same prefill encoded into bit-packed records (R = 21). Per (token, KV head, group, round) the encoder evaluates
     256 squared distances of 8 dims (8 subtractions + 8 multiply-adds = 24 flops each, fp32 VALU)."""
     import torch
     import vector_quantized_kv_amd as vq
@@ -272,6 +272,15 @@ def codebook_tools_timing(reps: int = 3):
     t_enc = timed(lambda: vq.encode_greedy(d, x, cb, codes=codes))
     t_upd = timed(lambda: vq.codebook_update(d, x, codes, cb, codebook_out=out))
     enc_flops = float(Hkv) * n * 16 * R * 256 * 24
+    # the same prefill encoded into bit-packed records (one index per 64 dims, N = 64, R = 21): per (token,
+    # KV head, group, round) 64 squared distances of 64 dims (3 flops per dim)
+    Rb = 21
+    cbb = (torch.randn((Hkv, 2, Rb, 64, 64), generator=g, device="cuda") * 0.5).half()
+    db = vq.make_dims(1, 4 * Hkv, Hkv, Rb, "float16", n_groups=2, n_codes=64)
+    words = vq.encode_greedy(db, x, cbb)
+    torch.cuda.synchronize()
+    t_encb = timed(lambda: vq.encode_greedy(db, x, cbb, codes=words))
+    encb_flops = float(Hkv) * n * 2 * Rb * 64 * 64 * 3
     return {
         "shape": f"{n} tokens x {Hkv} KV heads, R={R}, fp16",
         # the library is built without packed-fp32 instructions, so its fp32 VALU peak is half the published
@@ -280,6 +289,9 @@ def codebook_tools_timing(reps: int = 3):
                           "achieved_tflops": enc_flops / t_enc * 1e-12, "peak_tflops": 78.6,
                           "frac": enc_flops / t_enc * 1e-12 / 78.6},
         "codebook_update": {"ms": t_upd * 1e3, "tokens_per_s": n / t_upd},
+        "encode_greedy_bit_packed_r21": {"ms": t_encb * 1e3, "tokens_per_s": n / t_encb, "bound": "alu",
+                                         "achieved_tflops": encb_flops / t_encb * 1e-12, "peak_tflops": 78.6,
+                                         "frac": encb_flops / t_encb * 1e-12 / 78.6},
     }
 
 

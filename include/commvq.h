@@ -49,8 +49,8 @@
  *     commvq_last_error_detail() then names the offending argument.
  *   - Supported now: head_dim 128, Hq / Hkv = 4, and either the byte layout (n_groups 16, n_codes 256,
  *     n_residuals 1..2, dtype fp16 or fp32) or the bit-packed layout (n_groups 2, n_codes 64,
- *     n_residuals 1..32, dtype fp16; commvq_rope_table, commvq_attn_decode and commvq_debug_unpack
- *     only). Other values return COMMVQ_EUNSUPPORTED.
+ *     n_residuals 1..32, dtype fp16; commvq_rope_table, commvq_attn_decode, commvq_encode_greedy and
+ *     commvq_debug_unpack only). Other values return COMMVQ_EUNSUPPORTED.
  *   - No C++ exception crosses the ABI.
  */
 #ifndef COMMVQ_H
@@ -160,11 +160,13 @@ int commvq_value_reduce(const commvq_dims* d /* host */, const float* p, const u
  * codebook; pith.science verdict for arXiv 2506.18879, key_machinery: R residual rounds). It stands in
  * for the pages' learned encoder, whose weights are not available: per (KV head, token, group), round
  * r = 0..R-1 picks l* = argmin_l ||res - C[kv][g][r][l]||^2 (distances in fp32; the first minimum in index
- * order) and subtracts that codeword from res (res starts as the group's 8 values of x).
+ * order) and subtracts that codeword from res (res starts as the group's W values of x).
  *   x         [Hkv][n_tokens][D] in dims->dtype, in the codebook's own frame (keys before RoPE)
  *   codebook  [Hkv][G][R][N][W] in dims->dtype
- *   codes     a [Hkv][R][total_rows][G] uint8 code array; token t is written to row first_row + t, other
- *             rows are untouched (so new tokens can be appended to a cache in place)
+ *   codes     a [Hkv][R][total_rows][G] uint8 code array, or (bit-packed layout) token records
+ *             [Hkv][total_rows][ceil(12 R / 32)] uint32, 16-byte aligned; token t is written to row
+ *             first_row + t (its whole record), other rows are untouched (so new tokens can be appended to
+ *             a cache in place)
  * Returns COMMVQ_EINVAL unless 0 <= first_row and first_row + n_tokens <= total_rows; n_tokens = 0 is a
  * no-op.
  * ------------------------------------------------------------------------------------------- */

@@ -156,7 +156,9 @@ def test_bit_packed_layout_checks_on_host():
     assert L.commvq_qcodebook_table(ctypes.byref(d), p, p, p, None) == vq.EUNSUPPORTED
     assert L.commvq_value_reduce_workspace_size(ctypes.byref(d), 64) == 0
     assert L.commvq_value_reduce(ctypes.byref(d), p, p, p, p, p, 64, 64, p, 1 << 20, p, None) == vq.EUNSUPPORTED
-    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, 0, None) == vq.EUNSUPPORTED
+    # the encoder writes bit-packed records too; misaligned records are rejected before any launch
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, ctypes.c_void_p(0x1004), 10, 0, None) == vq.EINVAL
+    assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, 6, None) == vq.EINVAL  # rows 6..10 > 10
     assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, p, ctypes.c_void_p(0x100000), None) == vq.EUNSUPPORTED
     # mixed shapes stay unsupported
     for g, n in ((2, 256), (16, 64), (4, 64)):

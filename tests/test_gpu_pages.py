@@ -151,3 +151,51 @@ def test_pages_attention_reads_every_value_index_back(vq, R):
     cfg = pages_cfg("pages_counting", 1, (3000,), R, 61 + R)
     d = oracle.dims_of(cfg)
     read_indices_back(vq, cfg, lambda words, T: oracle.unpack_bits(d, words, T))
+
+
+def pages_encode_inputs(Hkv, n, R, seed):
+    rng = np.random.default_rng(seed)
+    cb = (rng.standard_normal((Hkv, 2, R, 64, 64), dtype=np.float32) * np.float32(0.5)).astype(np.float16)
+    x = (rng.standard_normal((Hkv, n, 128), dtype=np.float32) * np.float32(0.7)).astype(np.float16)
+    return x, cb
+
+
+@pytest.mark.parametrize("R,n", [(1, 300), (11, 1000), (21, 513)])
+def test_pages_encode_greedy_choices_are_optimal(vq, R, n):
+    # the greedy encoder writing bit-packed records: read back through the oracle's unpack, every choice is a
+    # minimum of the fp64 replay up to fp32 rounding, and clear minima are picked exactly
+    announce(f"encode_greedy bit-packed R={R} n={n}")
+    Hkv = 2
+    x, cb = pages_encode_inputs(Hkv, n, R, 70 + R)
+    d = vq.make_dims(1, 4 * Hkv, Hkv, R, "float16", n_groups=2, n_codes=64)
+    words = vq.encode_greedy(d, torch.from_numpy(x).cuda(), torch.from_numpy(cb).cuda())
+    torch.cuda.synchronize()
+    od = oracle.dims(1, 4 * Hkv, Hkv, R, n_groups=2, n_codes=64)
+    codes = oracle.unpack_bits(od, words.cpu().numpy().view(np.uint32), n)
+    chosen, best, second = oracle.encode_eval(od, x, cb, codes)
+    scale = best + 1e-3
+    assert np.all(chosen - best <= 1e-5 * scale)
+    unique = (second - best) > 1e-4 * scale
+    assert unique.mean() > 0.95
+    np.testing.assert_array_equal(chosen[unique], best[unique])
+    ref = oracle.encode_greedy(od, x, cb)
+    first_round_unique = unique[:, 0]
+    np.testing.assert_array_equal(codes[:, 0][first_round_unique], ref[:, 0][first_round_unique])
+
+
+def test_pages_encode_greedy_recovers_codewords_and_appends_in_place(vq):
+    announce("encode_greedy bit-packed exact recovery + append")
+    Hkv, n, R = 2, 300, 1
+    rng = np.random.default_rng(80)
+    cb = (rng.standard_normal((Hkv, 2, R, 64, 64), dtype=np.float32) * np.float32(0.5)).astype(np.float16)
+    idx = rng.integers(0, 64, size=(Hkv, R, n, 2)).astype(np.uint8)
+    od = oracle.dims(1, 4 * Hkv, Hkv, R, n_groups=2, n_codes=64)
+    x = oracle.decode(od, cb, idx, n).astype(np.float16)  # exact: one fp16 codeword per group
+    d = vq.make_dims(1, 4 * Hkv, Hkv, R, "float16", n_groups=2, n_codes=64)
+    big = torch.full((Hkv, n + 9, 1), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    vq.encode_greedy(d, torch.from_numpy(x).cuda(), torch.from_numpy(cb).cuda(), codes=big, first_row=5)
+    torch.cuda.synchronize()
+    out = big.cpu().numpy()
+    got = oracle.unpack_bits(od, np.ascontiguousarray(out[:, 5:5 + n]).view(np.uint32), n)
+    np.testing.assert_array_equal(got, idx)
+    assert np.all(out[:, :5] == 0x5A5A5A5A) and np.all(out[:, 5 + n:] == 0x5A5A5A5A)

@@ -182,13 +182,20 @@ def value_reduce(d: Dims, p, v_codes, v_codebook, seq_start, seq_len, max_len: i
 
 
 def encode_greedy(d: Dims, x, codebook, codes=None, first_row: int = 0, stream=None):
-    """Greedy residual codes of x [Hkv][n][D] (see commvq_encode_greedy). With codes=None a new
-    [Hkv][R][n][G] array is returned; otherwise the tokens are written to rows first_row.. of codes."""
+    """Greedy residual codes of x [Hkv][n][D] (see commvq_encode_greedy). With codes=None a new array is
+    returned: [Hkv][R][n][G] uint8, or for the bit-packed layout the token records [Hkv][n][words] (int32
+    tensor holding the uint32 words); otherwise the tokens are written to rows first_row.. of codes."""
     import torch
     n = int(x.shape[1])
+    packed = d.n_codes < 256
     if codes is None:
-        codes = torch.zeros((d.n_kv_heads, d.n_residuals, n, d.n_groups), dtype=torch.uint8, device=x.device)
-    _check(lib().commvq_encode_greedy(ctypes.byref(d), _ptr(x), _ptr(codebook), n, _ptr(codes), int(codes.shape[2]),
+        if packed:
+            words = (6 * d.n_residuals * d.n_groups + 31) // 32
+            codes = torch.zeros((d.n_kv_heads, n, words), dtype=torch.int32, device=x.device)
+        else:
+            codes = torch.zeros((d.n_kv_heads, d.n_residuals, n, d.n_groups), dtype=torch.uint8, device=x.device)
+    rows = int(codes.shape[1] if packed else codes.shape[2])
+    _check(lib().commvq_encode_greedy(ctypes.byref(d), _ptr(x), _ptr(codebook), n, _ptr(codes), rows,
                                       int(first_row), _stream(stream)), "encode_greedy")
     return codes
 

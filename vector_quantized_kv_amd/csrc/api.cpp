@@ -236,7 +236,7 @@ int commvq_value_reduce(const commvq_dims* d, const float* p, const uint8_t* v_c
 
 int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebook, int64_t n_tokens, uint8_t* codes,
                          int64_t total_rows, int64_t first_row, void* stream) {
-  if (int st = check_byte_dims(d, "encode_greedy")) return st;
+  if (int st = check_dims(d)) return st;
   if (n_tokens < 0) return fail(COMMVQ_EINVAL, "n_tokens = %lld must be >= 0", (long long)n_tokens);
   if (first_row < 0 || total_rows < 0 || first_row + n_tokens > total_rows)
     return fail(COMMVQ_EINVAL, "rows [%lld, %lld) do not fit total_rows = %lld", (long long)first_row,
@@ -245,6 +245,13 @@ int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebo
   if (!x || !codebook || !codes) return fail(COMMVQ_EINVAL, "x, codebook and codes must be non-NULL");
   if ((n_tokens + 255) / 256 > 0x7fffffffLL) return fail(COMMVQ_EUNSUPPORTED, "n_tokens = %lld is too large",
                                                           (long long)n_tokens);
+  if (packed_family(d)) {
+    if (!aligned16(codes)) return fail(COMMVQ_EINVAL, "codes must be 16-byte aligned");
+    return hip_status(launch_encode_greedy_bits(d->n_residuals, d->n_kv_heads, x, codebook, n_tokens,
+                                                reinterpret_cast<uint32_t*>(codes), total_rows, first_row,
+                                                static_cast<hipStream_t>(stream)),
+                      "encode_greedy launch");
+  }
   return hip_status(launch_encode_greedy(d->dtype, d->n_residuals, d->n_kv_heads, x, codebook, n_tokens, codes,
                                          total_rows, first_row, static_cast<hipStream_t>(stream)),
                     "encode_greedy launch");

@@ -34,7 +34,7 @@ constexpr int kWideCodes = 64;
 constexpr int kWideBits = 6;
 constexpr int kWideMaxResiduals = 32;
 constexpr int kWideResPerPass = 4;  // residual codebooks per attention pass (one 64 KiB LDS slot)
-inline int wide_record_words(int R) { return (kWideBits * R * kWideGroups + 31) / 32; }
+__host__ __device__ inline int wide_record_words(int R) { return (kWideBits * R * kWideGroups + 31) / 32; }
 
 // Attention workgroup: fp16 storage runs 8 waves (two per SIMD) over two 64 KiB codebook slots; fp32
 // storage runs 4 waves over one 128 KiB slot. Either way one workgroup owns a CU's LDS.
@@ -110,6 +110,8 @@ hipError_t launch_attn_wide(int B, const AttnArgs& a, hipStream_t s);
 hipError_t launch_value_reduce(int dtype, int R, int B, const ValueReduceArgs& a, float* out, hipStream_t s);
 hipError_t launch_encode_greedy(int dtype, int R, int Hkv, const void* x, const void* cb, int64_t n, uint8_t* codes,
                                 int64_t total_rows, int64_t first_row, hipStream_t s);
+hipError_t launch_encode_greedy_bits(int R, int Hkv, const void* x, const void* cb, int64_t n, uint32_t* words,
+                                     int64_t total_rows, int64_t first_row, hipStream_t s);
 hipError_t launch_codebook_update(int dtype, int R, int Hkv, const void* x, const uint8_t* codes, int64_t n,
                                   const void* cb_in, void* cb_out, hipStream_t s);
 hipError_t launch_debug_unpack(int R, int Hkv, int64_t total_tokens, const uint8_t* codes, int32_t* out,

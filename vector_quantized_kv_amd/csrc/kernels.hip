@@ -396,6 +396,94 @@ hipError_t launch_codebook_update(int dtype, int R, int Hkv, const void* x, cons
   return hipGetLastError();
 }
 
+// Bit-packed records (one index per 64 dims: G = 2, N = 64, R up to 32): the same greedy residual rounds.
+// One thread per token and one group at a time (a 64-dim fp32 residual in registers). A workgroup's 256
+// tokens take the rounds together: round r's codebook of the group (64 codewords x 64 dims, 16 KiB) sits in
+// LDS as fp32, and all lanes read the same codeword (a broadcast). The first minimum of the fp32 squared
+// distance is chosen and subtracted. Index (r, g) goes to bit 12 r + 6 g of the token's record: group 0's
+// pass stores every word, group 1's pass ORs its fields into them (ceil(12 R / 32) words per token).
+__global__ void __launch_bounds__(256) encode_greedy_bits_kernel(const f16* x, const f16* cb, int R, int64_t n,
+                                                                 uint32_t* words, int64_t total_rows,
+                                                                 int64_t first_row) {
+  constexpr int W = kHeadDim / kWideGroups, N = kWideCodes;
+  constexpr int kTabF4 = N * W / 4;  // float4 entries per (group, round) codebook
+  __shared__ float4 cw[kTabF4];
+  const int kv = blockIdx.y;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const bool live = t < n;
+  const int64_t tt = live ? t : n - 1;  // clamped: every thread takes part in the rounds (and their barriers)
+  const int Wd = wide_record_words(R);
+  uint32_t* rec = words + (static_cast<int64_t>(kv) * total_rows + first_row + tt) * Wd;
+  for (int g = 0; g < kWideGroups; ++g) {
+    float res[W];
+    const f16* xv = x + (static_cast<int64_t>(kv) * n + tt) * kHeadDim + g * W;
+#pragma unroll
+    for (int w = 0; w < W; ++w) res[w] = static_cast<float>(xv[w]);
+    uint64_t acc = 0;  // acc bit 0 = record bit 32 * word
+    int word = 0;
+    auto flush = [&]() {
+      uint32_t v = static_cast<uint32_t>(acc);
+      if (live) {
+        if (g > 0) v |= rec[word];
+        rec[word] = v;
+      }
+      acc >>= 32;
+      ++word;
+    };
+    for (int r = 0; r < R; ++r) {
+      __syncthreads();  // every thread is done with the previous round's codewords
+      for (int i = threadIdx.x; i < kTabF4; i += blockDim.x) {
+        const f16* c = cb + ((static_cast<int64_t>(kv) * kWideGroups + g) * R + r) * N * W + i * 4;
+        cw[i] = make_float4(static_cast<float>(c[0]), static_cast<float>(c[1]), static_cast<float>(c[2]),
+                            static_cast<float>(c[3]));
+      }
+      __syncthreads();
+      float best = INFINITY;
+      int bi = 0;
+      for (int l = 0; l < N; ++l) {
+        const float4* c = cw + l * (W / 4);
+        float dsum = 0.f;
+#pragma unroll
+        for (int q = 0; q < W / 4; ++q) {
+          const float4 v = c[q];
+          const float e0 = res[4 * q] - v.x, e1 = res[4 * q + 1] - v.y;
+          const float e2 = res[4 * q + 2] - v.z, e3 = res[4 * q + 3] - v.w;
+          dsum = fmaf(e0, e0, dsum);
+          dsum = fmaf(e1, e1, dsum);
+          dsum = fmaf(e2, e2, dsum);
+          dsum = fmaf(e3, e3, dsum);
+        }
+        if (dsum < best) {  // strict: ties keep the lowest index
+          best = dsum;
+          bi = l;
+        }
+      }
+      const float4* c = cw + bi * (W / 4);
+#pragma unroll
+      for (int q = 0; q < W / 4; ++q) {
+        const float4 v = c[q];
+        res[4 * q] -= v.x;
+        res[4 * q + 1] -= v.y;
+        res[4 * q + 2] -= v.z;
+        res[4 * q + 3] -= v.w;
+      }
+      acc |= static_cast<uint64_t>(bi) << (kWideBits * (kWideGroups * r + g) - 32 * word);
+      // the group's next field starts at or past bit 32 of acc: the low word is final for this group
+      if (kWideBits * (kWideGroups * (r + 1) + g) - 32 * word >= 32) flush();
+    }
+    while (word < Wd) flush();
+  }
+}
+
+hipError_t launch_encode_greedy_bits(int R, int Hkv, const void* x, const void* cb, int64_t n, uint32_t* words,
+                                     int64_t total_rows, int64_t first_row, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256), Hkv);
+  encode_greedy_bits_kernel<<<grid, 256, 0, s>>>(static_cast<const f16*>(x), static_cast<const f16*>(cb), R, n, words,
+                                                 total_rows, first_row);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode_greedy(int dtype, int R, int Hkv, const void* x, const void* cb, int64_t n, uint8_t* codes,
                                 int64_t total_rows, int64_t first_row, hipStream_t s) {
   if (n == 0) return hipSuccess;
