@@ -17,16 +17,16 @@
 // Work item, lanes and MFMA layouts are those of attn_kernel: lane = token of a 64-token block, 4 GQA
 // heads per KV head, the per-64-token RoPE phase on the query and the per-lane phase on the keys. A
 // 16-byte chunk cc of the 128-byte row of group g holds RoPE pairs 32 g + 4 cc .. + 3, exactly the pairs
-// of the byte layout's group 8 g + cc, so the key MFMA step, the value transposes and the epilogue are
-// shared. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual rows,
+// of the byte layout's group 8 g + cc, so the key MFMA step, the p^T operands, the softmax and the epilogue
+// are shared. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual rows,
 // sums them in fp32 on the matrix core (an MFMA with the identity as A adds a lane's four fp16 values to
 // its fp32 accumulator), and then
 //   keys:   rounds the sum to fp16, rotates it by the fine phase and runs the two key MFMA steps;
 //   values: sums with the identity as B instead, which transposes each 4x4 (token x dim) quad tile as it
 //           accumulates, then multiplies by p^T.
 // Rows are stored with their 16-byte chunks permuted by the codeword (physical chunk = cc xor
-// ((l >> 1) & 7)), so the 16 lanes that share an LDS cycle spread over all 16 bank groups instead of the
-// two a 128-byte row stride would give them.
+// ((l >> 1) & 7)), so the 16 lanes that share an LDS cycle land on random ones of the 16 bank groups
+// instead of the two that a 128-byte row stride would give them.
 #include "attn_common.h"
 
 namespace commvq {
