@@ -199,3 +199,9 @@ def test_pages_encode_greedy_recovers_codewords_and_appends_in_place(vq):
     got = oracle.unpack_bits(od, np.ascontiguousarray(out[:, 5:5 + n]).view(np.uint32), n)
     np.testing.assert_array_equal(got, idx)
     assert np.all(out[:, :5] == 0x5A5A5A5A) and np.all(out[:, 5 + n:] == 0x5A5A5A5A)
+
+
+def test_pages_attn_sixteen_kv_heads(vq):
+    announce("attn_decode bit-packed 16 KV heads, R=11")
+    cfg = pages_cfg("pages_kv16", 3, (5000, 1, 2049), 11, 95, n_kv=16)
+    check_attn(vq, cfg, workloads.make_inputs(cfg))

@@ -348,3 +348,15 @@ def test_attention_reads_every_value_index_back(vq, dtype, R):
     cfg = workloads.custom("counting", 1, 8, 2, (3000,), R, dtype, 31 + R)
     d = oracle.dims_of(cfg)
     read_indices_back(vq, cfg, lambda codes, T: oracle.unpack(d, codes, T))
+
+
+@pytest.mark.parametrize("R", [1, 2])
+def test_attn_decode_sixteen_kv_heads(vq, R):
+    # 16 KV heads (64 q heads) in a batch of 3: two heads per XCD in the grid's dealing order
+    announce(f"attn_decode 16 KV heads R={R}")
+    cfg = workloads.custom("kv16", 3, 64, 16, (5000, 1, 2049), R, "float16", 90 + R)
+    inp = workloads.make_inputs(cfg)
+    got = run_attn(vq, cfg, inp)
+    err = rowwise_rel_err(got, oracle.run_config(cfg, inp, n_threads=THREADS))
+    print(f"kv16 R={R}: {err:.3e}", flush=True)
+    assert err <= TOL["float16"]
