@@ -205,3 +205,27 @@ def test_pages_attn_sixteen_kv_heads(vq):
     announce("attn_decode bit-packed 16 KV heads, R=11")
     cfg = pages_cfg("pages_kv16", 3, (5000, 1, 2049), 11, 95, n_kv=16)
     check_attn(vq, cfg, workloads.make_inputs(cfg))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_encode_then_attend_round_trip(vq, packed):
+    # keys and values encoded on the GPU into the cache layout, then read by the attention kernel: the output
+    # matches the oracle's attention over the same stored codes (written by one kernel, read by another)
+    announce(f"encode -> attn_decode round trip, {'bit-packed R=11' if packed else 'byte R=2'}")
+    Hkv, L = 2, 3000
+    G, N, R = (2, 64, 11) if packed else (16, 256, 2)
+    W = 128 // G
+    cfg = workloads.custom("roundtrip", 1, 4 * Hkv, Hkv, (L,), R, "float16", 97, n_groups=G, n_codes=N)
+    inp = workloads.make_inputs(cfg)
+    rng = np.random.default_rng(98)
+    xk = (rng.standard_normal((Hkv, L, 128), dtype=np.float32) * np.float32(0.8)).astype(np.float16)
+    xv = (rng.standard_normal((Hkv, L, 128), dtype=np.float32) * np.float32(0.8)).astype(np.float16)
+    d = vq.dims_of(cfg)
+    kc = vq.encode_greedy(d, torch.from_numpy(xk).cuda(), torch.from_numpy(inp["k_cb"]).cuda())
+    vc = vq.encode_greedy(d, torch.from_numpy(xv).cuda(), torch.from_numpy(inp["v_cb"]).cuda())
+    torch.cuda.synchronize()
+    kc, vc = kc.cpu().numpy(), vc.cpu().numpy()
+    if packed:
+        kc, vc = kc.view(np.uint32), vc.view(np.uint32)
+    assert W * G == 128
+    check_attn(vq, cfg, dict(inp, k_codes=kc, v_codes=vc))
