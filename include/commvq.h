@@ -124,8 +124,11 @@ int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const
  *   out[b][h] = sum_t softmax(s)_t * vhat_t,  vhat_t = sum_r v_codebook[kv][g][r][v_codes[kv][r][..][g]]
  * No key or value is dequantized to memory. Sequences with L_b = 0 produce zeros.
  * rope_table: from commvq_rope_table with rope_positions >= max_len.
- * max_len (host) must be >= every seq_len[b], and seq_start[b] + seq_len[b] <= total_tokens (host),
- * the row count of the code arrays. rope_table must hold at least rope_positions positions.
+ * max_len (host) should be >= every seq_len[b], and seq_start[b] + seq_len[b] <= total_tokens (host),
+ * the row count of the code arrays. The kernels cannot report a descriptor that breaks these bounds (it
+ * is in device memory); they clamp it instead: start into [0, total_tokens], length into
+ * [0, min(max_len, total_tokens - start)], so no read leaves the code arrays, the RoPE table or the
+ * workspace. rope_table must hold at least rope_positions positions.
  * workspace: at least commvq_attn_decode_workspace_size(d, max_len) bytes, caller owned, 256-byte
  * aligned, and zero-filled before its first use: its head holds one arrival counter per (b, kv) that
  * the last workgroup of each (b, kv) resets, so every completed call leaves it zero-filled again; the
@@ -147,6 +150,7 @@ int commvq_attn_decode(const commvq_dims* d /* host */, const void* q, const uin
  *   out[b][h][8g+w] = sum_r sum_l bins[g][r][l] * v_codebook[kv][g][r][l][w]
  * p: [B][Hq][max_len] fp32, any finite real values, used as given (no renormalisation); entries at
  * t >= L_b are ignored. workspace: commvq_value_reduce_workspace_size(d, max_len) bytes.
+ * seq_start / seq_len are clamped as in commvq_attn_decode (length at most max_len and the rows left).
  * ------------------------------------------------------------------------------------------- */
 size_t commvq_value_reduce_workspace_size(const commvq_dims* d /* host */, int32_t max_len);
 int commvq_value_reduce(const commvq_dims* d /* host */, const float* p, const uint8_t* v_codes,

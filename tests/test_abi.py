@@ -58,7 +58,8 @@ ALL = dict(q="p", kc="p", vc="p", kb="p", vb="p", ss="p", sl="p", rope="p", out=
     ("n_residuals", 3, vq.EUNSUPPORTED), ("n_residuals", 0, vq.EINVAL), ("head_dim", 64, vq.EUNSUPPORTED),
     ("n_groups", 8, vq.EUNSUPPORTED), ("n_codes", 64, vq.EUNSUPPORTED), ("n_q_heads", 30, vq.EINVAL),
     ("n_q_heads", 16, vq.EUNSUPPORTED), ("batch", 0, vq.EINVAL), ("dtype", 7, vq.EINVAL),
-    ("rope_base", 0.5, vq.EINVAL),
+    ("rope_base", 0.5, vq.EINVAL), ("softmax_scale", 0.0, vq.EINVAL), ("softmax_scale", float("inf"), vq.EINVAL),
+    ("softmax_scale", float("nan"), vq.EINVAL),
 ])
 def test_bad_dims_rejected(field, value, status):
     d = vq.make_dims(1, 32, 8, 2)

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <string>
 
 #include "commvq_internal.h"
@@ -67,7 +68,7 @@ int check_dims(const commvq_dims* d) {
       return fail(COMMVQ_EUNSUPPORTED, "n_residuals = %d; the byte layout implements 1 and 2", d->n_residuals);
   }
   if (!(d->rope_base > 1.0)) return fail(COMMVQ_EINVAL, "rope_base = %g must be > 1", d->rope_base);
-  if (!(d->softmax_scale == d->softmax_scale) || d->softmax_scale == 0.f)
+  if (!std::isfinite(d->softmax_scale) || d->softmax_scale == 0.f)
     return fail(COMMVQ_EINVAL, "softmax_scale must be finite and non-zero");
   return COMMVQ_OK;
 }
@@ -183,6 +184,7 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
   a.seq_start = seq_start;
   a.seq_len = seq_len;
   a.total_tokens = total_tokens;
+  a.max_len = max_len;
   a.rope = static_cast<const float2*>(rope_table);
   a.split_tokens = split_tokens;
   a.n_splits = static_cast<int32_t>(attn_n_splits(max_len, split_tokens));
@@ -241,7 +243,7 @@ int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebo
   if (first_row < 0 || total_rows < 0 || first_row + n_tokens > total_rows)
     return fail(COMMVQ_EINVAL, "rows [%lld, %lld) do not fit total_rows = %lld", (long long)first_row,
                 (long long)(first_row + n_tokens), (long long)total_rows);
-  if (n_tokens == 0) return COMMVQ_OK;
+  if (n_tokens == 0) return ok();
   if (!x || !codebook || !codes) return fail(COMMVQ_EINVAL, "x, codebook and codes must be non-NULL");
   if ((n_tokens + 255) / 256 > 0x7fffffffLL) return fail(COMMVQ_EUNSUPPORTED, "n_tokens = %lld is too large",
                                                           (long long)n_tokens);

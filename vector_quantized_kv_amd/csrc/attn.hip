@@ -279,9 +279,10 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
   const T* cb_k = static_cast<const T*>(a.k_cb) + kv * cb_stride;
   const T* cb_v = static_cast<const T*>(a.v_cb) + kv * cb_stride;
   auto table_src = [&](int p) { return p < R ? cb_k : cb_v; };
-  // sequence bounds, read before any memory operation so that they stay scalar loads
-  const int L = a.seq_len[b];
-  const int64_t seq_start = a.seq_start[b];
+  // sequence bounds (clamped), read before any memory operation so that they stay scalar loads
+  const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.max_len, a.total_tokens);
+  const int L = sb.len;
+  const int64_t seq_start = sb.start;
 
   // ---------------------------------------------------------------------------------- prologue
   // (1) The codebooks of the first phases and (fp16 storage) the group-major packed-fp16 fine phases

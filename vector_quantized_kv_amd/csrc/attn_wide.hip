@@ -114,8 +114,10 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   const int64_t cb_stride = static_cast<int64_t>(kWG) * R * kWN * (kWRow / 2);
   const f16* cb_k = static_cast<const f16*>(a.k_cb) + kv * cb_stride;
   const f16* cb_v = static_cast<const f16*>(a.v_cb) + kv * cb_stride;
-  const int L = a.seq_len[b];  // read before any memory operation so that they stay scalar loads
-  const int64_t seq_start = a.seq_start[b];
+  // sequence bounds (clamped), read before any memory operation so that they stay scalar loads
+  const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.max_len, a.total_tokens);
+  const int L = sb.len;
+  const int64_t seq_start = sb.start;
 
   // ---------------------------------------------------------------------------------- prologue
   // (0) the zero row that stands in for the rows of residuals past R in the last pass of each kind (an

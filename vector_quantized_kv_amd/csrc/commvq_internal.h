@@ -74,6 +74,7 @@ struct AttnArgs {
   const int64_t* seq_start;
   const int32_t* seq_len;
   int64_t total_tokens;
+  int32_t max_len;  // longest sequence the launch was sized for (seq_len is clamped to it)
   const float2* rope;
   int32_t n_splits;
   int32_t split_tokens;

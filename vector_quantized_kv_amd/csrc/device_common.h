@@ -15,6 +15,22 @@ __device__ __forceinline__ uint32_t code_index(const uint4& w, int g) {
   return (word >> ((g & 3) * 8)) & 0xffu;
 }
 
+// Bounds of sequence b as every kernel uses them. seq_start and seq_len live in device memory, where the
+// host cannot check them, so they are clamped: the start into [0, total_tokens], the length into
+// [0, min(max_len, total_tokens - start)]. Descriptors within the documented bounds pass unchanged; any
+// other one still reads only rows of the code arrays, positions of the RoPE table and splits of the
+// workspace that exist. Loaded before any other memory operation of a kernel, they stay scalar.
+struct SeqBounds {
+  int64_t start;
+  int len;
+};
+__device__ __forceinline__ SeqBounds seq_bounds(const int64_t* seq_start, const int32_t* seq_len, int b,
+                                                int32_t max_len, int64_t total_tokens) {
+  const int64_t s = min(max(seq_start[b], static_cast<int64_t>(0)), total_tokens);
+  const int64_t L = min(min(static_cast<int64_t>(max(seq_len[b], 0)), static_cast<int64_t>(max_len)), total_tokens - s);
+  return {s, static_cast<int>(L)};
+}
+
 // 16-byte code record of (kv head, token row, residual r) in a [Hkv][R][T][G] byte array.
 __device__ __forceinline__ uint4 load_code_record(const uint8_t* codes, int64_t total_tokens, int kv, int64_t row,
                                                   int R, int r) {

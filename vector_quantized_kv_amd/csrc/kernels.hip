@@ -146,10 +146,11 @@ __global__ void __launch_bounds__(256) value_reduce_kernel(const ValueReduceArgs
   __shared__ float red[4][kGqa];
   __shared__ __attribute__((aligned(16))) int32_t work[kGqa * kGroups * R * kCodes];
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int L = a.seq_len[b];
+  const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens);
+  const int L = sb.len;
   const int t0 = split * kSplitTokens;
   if (t0 >= L) return;
-  const int64_t row0 = a.seq_start[b] + t0;
+  const int64_t row0 = sb.start + t0;
   const int h0 = kv * kGqa;
   const int wave = tid >> 6, lane = tid & 63;
   bool valid[TPT];
@@ -191,10 +192,10 @@ __global__ void __launch_bounds__(256) value_reduce_kernel(const ValueReduceArgs
   contract_bins<T, R>(work, vcb, fx_scale, part, row_stride);
 }
 
-__global__ void __launch_bounds__(128) combine_sum_kernel(const float* part, const int32_t* seq_len,
-                                                          int32_t n_splits, int32_t Hq, float* out) {
-  const int bh = blockIdx.x, b = bh / Hq, d = threadIdx.x;
-  const int L = seq_len[b];
+__global__ void __launch_bounds__(128) combine_sum_kernel(const float* part, const ValueReduceArgs a, float* out) {
+  const int bh = blockIdx.x, b = bh / a.n_q_heads, d = threadIdx.x;
+  const int L = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens).len;  // as value_reduce_kernel
+  const int n_splits = a.n_splits;
   const int ns = (L + kSplitTokens - 1) / kSplitTokens;
   const float* p = part + static_cast<int64_t>(bh) * n_splits * kPartFloats;
   float acc = 0.f;
@@ -213,7 +214,7 @@ hipError_t launch_value_reduce(int dtype, int R, int B, const ValueReduceArgs& a
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_sum_kernel<<<dim3(B * a.n_q_heads), dim3(128), 0, s>>>(a.part, a.seq_len, a.n_splits, a.n_q_heads, out);
+  combine_sum_kernel<<<dim3(B * a.n_q_heads), dim3(128), 0, s>>>(a.part, a, out);
   return hipGetLastError();
 }
 
