@@ -249,7 +249,8 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
 def codebook_tools_timing(reps: int = 3):
     """The offline steps next to the decode path, at the 128K layer shape (8 KV heads, R = 2, fp16):
     encoding every cached key of a 131072-token prefill with commvq_encode_greedy, one codebook M-step
-    (commvq_codebook_update) over the same tokens, and the same prefill encoded into bit-packed records (R = 21). Per (token, KV head, group, round) the encoder evaluates
+    (commvq_codebook_update) over the same tokens, and the same prefill encoded into bit-packed records (R = 21)
+    with one M-step over them. Per (token, KV head, group, round) the encoder evaluates
     256 squared distances of 8 dims (8 subtractions + 8 multiply-adds = 24 flops each, fp32 VALU)."""
     import torch
     import vector_quantized_kv_amd as vq
@@ -278,8 +279,10 @@ def codebook_tools_timing(reps: int = 3):
     cbb = (torch.randn((Hkv, 2, Rb, 64, 64), generator=g, device="cuda") * 0.5).half()
     db = vq.make_dims(1, 4 * Hkv, Hkv, Rb, "float16", n_groups=2, n_codes=64)
     words = vq.encode_greedy(db, x, cbb)
+    outb = vq.codebook_update(db, x, words, cbb)
     torch.cuda.synchronize()
     t_encb = timed(lambda: vq.encode_greedy(db, x, cbb, codes=words))
+    t_updb = timed(lambda: vq.codebook_update(db, x, words, cbb, codebook_out=outb))
     encb_flops = float(Hkv) * n * 2 * Rb * 64 * 64 * 3
     return {
         "shape": f"{n} tokens x {Hkv} KV heads, R={R}, fp16",
@@ -292,6 +295,7 @@ def codebook_tools_timing(reps: int = 3):
         "encode_greedy_bit_packed_r21": {"ms": t_encb * 1e3, "tokens_per_s": n / t_encb, "bound": "alu",
                                          "achieved_tflops": encb_flops / t_encb * 1e-12, "peak_tflops": 78.6,
                                          "frac": encb_flops / t_encb * 1e-12 / 78.6},
+        "codebook_update_bit_packed_r21": {"ms": t_updb * 1e3, "tokens_per_s": n / t_updb},
     }
 
 

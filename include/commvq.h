@@ -49,8 +49,7 @@
  *     commvq_last_error_detail() then names the offending argument.
  *   - Supported now: head_dim 128, Hq / Hkv = 4, and either the byte layout (n_groups 16, n_codes 256,
  *     n_residuals 1..2, dtype fp16 or fp32) or the bit-packed layout (n_groups 2, n_codes 64,
- *     n_residuals 1..32, dtype fp16; commvq_rope_table, commvq_attn_decode, commvq_encode_greedy and
- *     commvq_debug_unpack only). Other values return COMMVQ_EUNSUPPORTED.
+ *     n_residuals 1..32, dtype fp16), on every entry point. Other values return COMMVQ_EUNSUPPORTED.
  *   - No C++ exception crosses the ABI.
  */
 #ifndef COMMVQ_H
@@ -111,7 +110,8 @@ int commvq_rope_table(const commvq_dims* d /* host */, int32_t n_positions, void
  * pith.science verdict, key_machinery; summary page, Approach):
  *   table[b][h][g][r][l][2u]   = q[b][h][2j] * a + q[b][h][2j+1] * b
  *   table[b][h][g][r][l][2u+1] = q[b][h][2j] * b - q[b][h][2j+1] * a
- * i.e. conj(q_j) * (a + i b) for pair j = 4g + u and codeword (a, b) = k_codebook[kv][g][r][l][2u..2u+1].
+ * i.e. conj(q_j) * (a + i b) for pair j = (W/2) g + u and codeword (a, b) = k_codebook[kv][g][r][l][2u..2u+1]
+ * (W = 8 in the byte layout, 64 in the bit-packed one).
  * Output [B][Hq][G][R][N][W] in dtype (fp16 results are rounded once from fp32).
  * ------------------------------------------------------------------------------------------- */
 int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const void* k_codebook, void* table,
@@ -146,8 +146,9 @@ int commvq_attn_decode(const commvq_dims* d /* host */, const void* q, const uin
 /* ---------------------------------------------------------------------------------------------
  * Value reduce with given weights, in the reordered form of the pages (pith.science verdict,
  * forward_implications: the softmax weights multiply the value codes before the codebook product):
- *   bins[g][r][l] = sum_{t < L_b} p[b][h][t] * [v_codes[kv][seq_start[b]+t][r][g] == l]
- *   out[b][h][8g+w] = sum_r sum_l bins[g][r][l] * v_codebook[kv][g][r][l][w]
+ *   bins[g][r][l] = sum_{t < L_b} p[b][h][t] * [index (r, g) of token row seq_start[b]+t == l]
+ *   out[b][h][W g + w] = sum_r sum_l bins[g][r][l] * v_codebook[kv][g][r][l][w]
+ * v_codes: the byte planes [Hkv][R][T][G], or (bit-packed layout) the token records [Hkv][T][words].
  * p: [B][Hq][max_len] fp32, any finite real values, used as given (no renormalisation); entries at
  * t >= L_b are ignored. workspace: commvq_value_reduce_workspace_size(d, max_len) bytes.
  * seq_start / seq_len are clamped as in commvq_attn_decode (length at most max_len and the rows left).
@@ -183,12 +184,14 @@ int commvq_encode_greedy(const commvq_dims* d /* host */, const void* x, const v
  * key_machinery: the codebook is fit by an EM-style clustering algorithm and R residual rounds refine the
  * reconstruction; "1-bit quantization" tag page, CommVQ abstract: EM training). With the E-step being an
  * assignment such as commvq_encode_greedy's, for every (kv, g, r, l):
- *   codebook_out[kv][g][r][l] = mean over tokens t with codes[kv][r][t][g] == l of the round-r residual
- *                               x[kv][t][8g .. 8g+7] - sum_{r' < r} codebook_in[kv][g][r'][codes[kv][r'][t][g]]
+ *   codebook_out[kv][g][r][l] = mean over tokens t whose index (r, g) is l of the round-r residual
+ *                               x[kv][t][W g .. W g + W-1] - sum_{r' < r} codebook_in[kv][g][r'][index (r', g) of t]
  * (the least-squares codeword for that assignment; every round uses codebook_in for its residuals), and
  * codebook_out = codebook_in for a codeword no token selects.
  *   x             [Hkv][n_tokens][D] in dims->dtype, in the codebook's own frame (keys before RoPE)
- *   codes         [Hkv][R][n_tokens][G] uint8 (commvq_encode_greedy with first_row 0, total_rows n_tokens)
+ *   codes         [Hkv][R][n_tokens][G] uint8 (commvq_encode_greedy with first_row 0, total_rows n_tokens),
+ *                 or (bit-packed layout) the token records [Hkv][n_tokens][ceil(12 R / 32)] uint32, 16-byte
+ *                 aligned
  *   codebook_in   [Hkv][G][R][N][W] in dims->dtype
  *   codebook_out  same shape and type; must not overlap codebook_in (COMMVQ_EINVAL)
  * Sums are accumulated in fp32 in an order that is not fixed, so repeated calls may differ by rounding.

@@ -153,14 +153,23 @@ def test_bit_packed_layout_checks_on_host():
     # fp32 codebooks are not implemented for the bit-packed layout
     d32 = vq.make_dims(1, 32, 8, 11, dtype="float32", n_groups=2, n_codes=64)
     assert _attn(d32, **ALL) == vq.EUNSUPPORTED
-    # the byte-layout-only entry points refuse the bit-packed layout
-    assert L.commvq_qcodebook_table(ctypes.byref(d), p, p, p, None) == vq.EUNSUPPORTED
-    assert L.commvq_value_reduce_workspace_size(ctypes.byref(d), 64) == 0
-    assert L.commvq_value_reduce(ctypes.byref(d), p, p, p, p, p, 64, 64, p, 1 << 20, p, None) == vq.EUNSUPPORTED
+    # the codebook tools take the bit-packed layout too; bad arguments are rejected before any launch
+    assert L.commvq_qcodebook_table(ctypes.byref(d), p, p, None, None) == vq.EINVAL
+    assert L.commvq_qcodebook_table(ctypes.byref(d32), p, p, p, None) == vq.EUNSUPPORTED
+    vr = L.commvq_value_reduce_workspace_size(ctypes.byref(d), 64)
+    assert vr > 0
+    assert L.commvq_value_reduce(ctypes.byref(d), p, p, p, p, p, 64, 64, p, vr - 1, p, None) == vq.EWORKSPACE
+    assert L.commvq_value_reduce(ctypes.byref(d), p, ctypes.c_void_p(0x1004), p, p, p, 64, 64, p, vr, p,
+                                 None) == vq.EINVAL
+    cb_bytes = 8 * 2 * 21 * 64 * 64 * 2  # fp16 codebook [Hkv][2][R][64][64]
+    a, b = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x100000 + cb_bytes)  # never dereferenced
+    assert L.commvq_codebook_update(ctypes.byref(d), p, ctypes.c_void_p(0x1004), 5, a, b, None) == vq.EINVAL
+    assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, a, ctypes.c_void_p(0x100000 + cb_bytes - 1),
+                                    None) == vq.EINVAL  # overlap by one byte at the bit-packed size
+    assert L.commvq_codebook_update(ctypes.byref(d32), p, p, 5, a, b, None) == vq.EUNSUPPORTED
     # the encoder writes bit-packed records too; misaligned records are rejected before any launch
     assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, ctypes.c_void_p(0x1004), 10, 0, None) == vq.EINVAL
     assert L.commvq_encode_greedy(ctypes.byref(d), p, p, 5, p, 10, 6, None) == vq.EINVAL  # rows 6..10 > 10
-    assert L.commvq_codebook_update(ctypes.byref(d), p, p, 5, p, ctypes.c_void_p(0x100000), None) == vq.EUNSUPPORTED
     # mixed shapes stay unsupported
     for g, n in ((2, 256), (16, 64), (4, 64)):
         dd = vq.make_dims(1, 32, 8, 1, n_groups=g, n_codes=n)

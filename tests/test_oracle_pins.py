@@ -342,6 +342,48 @@ def test_value_binning_identity(oracle_lib):
             assert np.max(np.abs(out[b, h] - ref)) <= 1e-12 * np.abs(ref).max()
 
 
+def test_value_binning_identity_bit_packed_shape(oracle_lib):
+    """The same identity at the pages' own shape (one index per 64 dims, N = 64, R = 11), codes read from
+    bit-packed records."""
+    cfg = workloads.custom("pin", 2, 8, 2, (333, 64), 11, "float16", 18, n_groups=2, n_codes=64)
+    inp = workloads.make_inputs(cfg)
+    d = oracle.dims_of(cfg)
+    T, L = int(inp["total_tokens"]), int(inp["max_len"])
+    vc = oracle.unpack_bits(d, inp["v_codes"], T)
+    rng = np.random.default_rng(19)
+    p = rng.uniform(-1, 1, size=(2, 8, L))
+    out = oracle.value_reduce(d, p, vc, inp["v_cb"], inp["seq_start"], inp["seq_len"], L)
+    dec = oracle.decode(d, inp["v_cb"], vc, T)
+    for b in range(2):
+        s0, lb = int(inp["seq_start"][b]), int(inp["seq_len"][b])
+        for h in range(8):
+            ref = p[b, h, :lb] @ dec[h // 4, s0:s0 + lb]
+            assert np.max(np.abs(out[b, h] - ref)) <= 1e-12 * np.abs(ref).max()
+
+
+def test_table_closed_forms_bit_packed_shape(oracle_lib):
+    """A one-hot query picks out one RoPE pair of the 64-dim groups: q_j = 1 gives (a, b), q_j = i gives (b, -a)."""
+    B, Hq, Hkv, R, D = 1, 2, 1, 3, 128
+    d = oracle.dims(B, Hq, Hkv, R, n_groups=2, n_codes=64)
+    rng = np.random.default_rng(6)
+    kcb = rng.standard_normal((Hkv, 2, R, 64, 64))
+    j = 45  # pair 45 lies in group 1, slot 13
+    q = np.zeros((B, Hq, D))
+    q[0, 0, 2 * j] = 1.0
+    q[0, 1, 2 * j + 1] = 1.0
+    T = oracle.table(d, q, kcb)  # [B][Hq][2][R][64][64]
+    g, u = divmod(j, 32)
+    a, b = kcb[0, g, :, :, 2 * u], kcb[0, g, :, :, 2 * u + 1]
+    np.testing.assert_array_equal(T[0, 0, g, :, :, 2 * u], a)
+    np.testing.assert_array_equal(T[0, 0, g, :, :, 2 * u + 1], b)
+    np.testing.assert_array_equal(T[0, 1, g, :, :, 2 * u], b)
+    np.testing.assert_array_equal(T[0, 1, g, :, :, 2 * u + 1], -a)
+    mask = np.ones((2, 32), dtype=bool)
+    mask[g, u] = False
+    Tp = T[0, 0].reshape(2, R, 64, 32, 2).transpose(0, 3, 1, 2, 4)
+    assert np.all(Tp[mask] == 0.0)
+
+
 def test_value_reduce_one_hot_selects_token(oracle_lib):
     cfg = workloads.custom("pin", 1, 4, 1, (90,), 1, "float32", 17)
     inp = workloads.make_inputs(cfg)

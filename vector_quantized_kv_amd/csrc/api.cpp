@@ -73,13 +73,6 @@ int check_dims(const commvq_dims* d) {
   return COMMVQ_OK;
 }
 
-// Entry points implemented for the byte layout only.
-int check_byte_dims(const commvq_dims* d, const char* what) {
-  if (int st = check_dims(d)) return st;
-  if (packed_family(d)) return fail(COMMVQ_EUNSUPPORTED, "%s is implemented for the byte layout only", what);
-  return COMMVQ_OK;
-}
-
 size_t rope_bytes(int32_t n_positions) {
   return (static_cast<size_t>(kRopeCoarseOffset) + static_cast<size_t>(rope_coarse_rows(n_positions)) * kPairs) *
          sizeof(float2);
@@ -140,10 +133,10 @@ int commvq_rope_table(const commvq_dims* d, int32_t n_positions, void* table, si
 }
 
 int commvq_qcodebook_table(const commvq_dims* d, const void* q, const void* k_codebook, void* table, void* stream) {
-  if (int st = check_byte_dims(d, "qcodebook_table")) return st;
+  if (int st = check_dims(d)) return st;
   if (!q || !k_codebook || !table) return fail(COMMVQ_EINVAL, "q, k_codebook and table must be non-NULL");
-  return hip_status(launch_qtable(d->dtype, d->n_residuals, d->batch, d->n_q_heads, d->n_kv_heads, q, k_codebook,
-                                  table, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_qtable(d->dtype, packed_family(d), d->n_residuals, d->batch, d->n_q_heads, d->n_kv_heads,
+                                  q, k_codebook, table, static_cast<hipStream_t>(stream)),
                     "qcodebook_table launch");
 }
 
@@ -204,14 +197,14 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
 }
 
 size_t commvq_value_reduce_workspace_size(const commvq_dims* d, int32_t max_len) {
-  if (check_byte_dims(d, "value_reduce") != COMMVQ_OK || max_len < 0) return 0;
+  if (check_dims(d) != COMMVQ_OK || max_len < 0) return 0;
   return part_bytes(d, max_len);
 }
 
 int commvq_value_reduce(const commvq_dims* d, const float* p, const uint8_t* v_codes, const void* v_codebook,
                         const int64_t* seq_start, const int32_t* seq_len, int32_t max_len, int64_t total_tokens,
                         void* workspace, size_t ws_bytes, float* out, void* stream) {
-  if (int st = check_byte_dims(d, "value_reduce")) return st;
+  if (int st = check_dims(d)) return st;
   if (!p || !v_codes || !v_codebook || !seq_start || !seq_len || !out)
     return fail(COMMVQ_EINVAL, "a required pointer is NULL");
   if (max_len < 0) return fail(COMMVQ_EINVAL, "max_len = %d must be >= 0", max_len);
@@ -232,7 +225,8 @@ int commvq_value_reduce(const commvq_dims* d, const float* p, const uint8_t* v_c
   a.n_q_heads = d->n_q_heads;
   a.n_kv_heads = d->n_kv_heads;
   a.part = static_cast<float*>(workspace);
-  return hip_status(launch_value_reduce(d->dtype, d->n_residuals, d->batch, a, out, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_value_reduce(d->dtype, packed_family(d), d->n_residuals, d->batch, a, out,
+                                        static_cast<hipStream_t>(stream)),
                     "value_reduce launch");
 }
 
@@ -261,15 +255,22 @@ int commvq_encode_greedy(const commvq_dims* d, const void* x, const void* codebo
 
 int commvq_codebook_update(const commvq_dims* d, const void* x, const uint8_t* codes, int64_t n_tokens,
                            const void* codebook_in, void* codebook_out, void* stream) {
-  if (int st = check_byte_dims(d, "codebook_update")) return st;
+  if (int st = check_dims(d)) return st;
   if (n_tokens < 0) return fail(COMMVQ_EINVAL, "n_tokens = %lld must be >= 0", (long long)n_tokens);
   if (!codebook_in || !codebook_out) return fail(COMMVQ_EINVAL, "codebook_in and codebook_out must be non-NULL");
   if (n_tokens > 0 && (!x || !codes)) return fail(COMMVQ_EINVAL, "x and codes must be non-NULL");
-  const size_t cb_bytes = static_cast<size_t>(d->n_kv_heads) * kGroups * d->n_residuals * kCodes * kGroupDim *
+  const bool packed = packed_family(d);
+  if (packed && n_tokens > 0 && !aligned16(codes)) return fail(COMMVQ_EINVAL, "codes must be 16-byte aligned");
+  // [Hkv][G][R][N][W] with G W = head_dim
+  const size_t cb_bytes = static_cast<size_t>(d->n_kv_heads) * d->n_residuals * d->n_codes * kHeadDim *
                           (d->dtype == COMMVQ_F16 ? 2 : 4);
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(codebook_in), b0 = reinterpret_cast<uintptr_t>(codebook_out);
   if (a0 < b0 + cb_bytes && b0 < a0 + cb_bytes)
     return fail(COMMVQ_EINVAL, "codebook_out overlaps codebook_in (the update reads the input while writing)");
+  if (packed)
+    return hip_status(launch_codebook_update_bits(d->n_residuals, d->n_kv_heads, x, reinterpret_cast<const uint32_t*>(codes),
+                                                  n_tokens, codebook_in, codebook_out, static_cast<hipStream_t>(stream)),
+                      "codebook_update launch");
   return hip_status(launch_codebook_update(d->dtype, d->n_residuals, d->n_kv_heads, x, codes, n_tokens, codebook_in,
                                            codebook_out, static_cast<hipStream_t>(stream)),
                     "codebook_update launch");

@@ -104,17 +104,20 @@ struct ValueReduceArgs {
 };
 
 hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hipStream_t s);
-hipError_t launch_qtable(int dtype, int R, int B, int Hq, int Hkv, const void* q, const void* kcb, void* out,
-                         hipStream_t s);
+hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, const void* q, const void* kcb,
+                         void* out, hipStream_t s);
 hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_wide(int B, const AttnArgs& a, hipStream_t s);
-hipError_t launch_value_reduce(int dtype, int R, int B, const ValueReduceArgs& a, float* out, hipStream_t s);
+hipError_t launch_value_reduce(int dtype, bool packed, int R, int B, const ValueReduceArgs& a, float* out,
+                               hipStream_t s);
 hipError_t launch_encode_greedy(int dtype, int R, int Hkv, const void* x, const void* cb, int64_t n, uint8_t* codes,
                                 int64_t total_rows, int64_t first_row, hipStream_t s);
 hipError_t launch_encode_greedy_bits(int R, int Hkv, const void* x, const void* cb, int64_t n, uint32_t* words,
                                      int64_t total_rows, int64_t first_row, hipStream_t s);
 hipError_t launch_codebook_update(int dtype, int R, int Hkv, const void* x, const uint8_t* codes, int64_t n,
                                   const void* cb_in, void* cb_out, hipStream_t s);
+hipError_t launch_codebook_update_bits(int R, int Hkv, const void* x, const uint32_t* words, int64_t n,
+                                       const void* cb_in, void* cb_out, hipStream_t s);
 hipError_t launch_debug_unpack(int R, int Hkv, int64_t total_tokens, const uint8_t* codes, int32_t* out,
                                hipStream_t s);
 hipError_t launch_debug_unpack_bits(int R, int Hkv, int64_t total_tokens, const uint32_t* words, int32_t* out,

@@ -64,6 +64,15 @@ __device__ __forceinline__ uint32_t packed_index(uint32_t x0, uint32_t x1) {
   }
 }
 static_assert(kWideBits * kWideGroups * kWideResPerPass <= 48, "a window fits two words from a 16-bit offset");
+// Index (r, g) of one token record, read field by field (the codebook tools; the attention kernel reads
+// whole windows). A field that crosses a word boundary takes its high bits from the next word, which is
+// then still inside the record (the field ends at or before bit 12 R).
+__device__ __forceinline__ uint32_t packed_field(const uint32_t* rec, int r, int g) {
+  const int bit = kWideBits * (kWideGroups * r + g), w = bit >> 5, sh = bit & 31;
+  uint32_t v = rec[w] >> sh;
+  if (sh > 32 - kWideBits) v |= rec[w + 1] << (32 - sh);
+  return v & ((1u << kWideBits) - 1);
+}
 
 // row_ror DPP: lane l of each 16-lane row reads lane (l + n) mod 16 of the same row. Every source lane
 // exists, so bound_ctrl is irrelevant to the result; setting it lets the compiler fold the move into the

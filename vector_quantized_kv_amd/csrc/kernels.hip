@@ -64,31 +64,40 @@ hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hi
 }
 
 // ------------------------------------------------------------------------- query x codebook table
-// grid (G*R, Hq, B), block 256: thread l writes the 4 complex entries of code l.
-template <typename T>
+// grid (G*R, Hq, B), block N: thread l writes the W/2 complex entries of code l. Byte layout G = 16, N = 256,
+// W = 8; bit-packed layout G = 2, N = 64, W = 64.
+template <typename T, int G, int N>
 __global__ void __launch_bounds__(256) qtable_kernel(const T* q, const T* kcb, T* out, int Hq, int Hkv, int R) {
+  constexpr int W = kHeadDim / G;
   const int gr = blockIdx.x, h = blockIdx.y, b = blockIdx.z, l = threadIdx.x;
   const int g = gr / R, r = gr % R, kv = h / (Hq / Hkv);
-  const T* qq = q + (static_cast<int64_t>(b) * Hq + h) * kHeadDim + kGroupDim * g;
-  const T* c = kcb + (((static_cast<int64_t>(kv) * kGroups + g) * R + r) * kCodes + l) * kGroupDim;
-  T* o = out + ((((static_cast<int64_t>(b) * Hq + h) * kGroups + g) * R + r) * kCodes + l) * kGroupDim;
+  const T* qq = q + (static_cast<int64_t>(b) * Hq + h) * kHeadDim + W * g;
+  const T* c = kcb + (((static_cast<int64_t>(kv) * G + g) * R + r) * N + l) * W;
+  T* o = out + ((((static_cast<int64_t>(b) * Hq + h) * G + g) * R + r) * N + l) * W;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < W / 2; ++u) {
     const float q0 = ld(qq + 2 * u), q1 = ld(qq + 2 * u + 1), a = ld(c + 2 * u), bb = ld(c + 2 * u + 1);
     o[2 * u] = static_cast<T>(q0 * a + q1 * bb);
     o[2 * u + 1] = static_cast<T>(q0 * bb - q1 * a);
   }
 }
 
-hipError_t launch_qtable(int dtype, int R, int B, int Hq, int Hkv, const void* q, const void* kcb, void* out,
-                         hipStream_t s) {
+hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, const void* q, const void* kcb,
+                         void* out, hipStream_t s) {
+  if (packed) {  // fp16 only
+    qtable_kernel<f16, kWideGroups, kWideCodes><<<dim3(kWideGroups * R, Hq, B), kWideCodes, 0, s>>>(
+        static_cast<const f16*>(q), static_cast<const f16*>(kcb), static_cast<f16*>(out), Hq, Hkv, R);
+    return hipGetLastError();
+  }
   dim3 grid(kGroups * R, Hq, B);
   if (dtype == COMMVQ_F16)
-    qtable_kernel<f16><<<grid, 256, 0, s>>>(static_cast<const f16*>(q), static_cast<const f16*>(kcb),
-                                            static_cast<f16*>(out), Hq, Hkv, R);
+    qtable_kernel<f16, kGroups, kCodes><<<grid, kCodes, 0, s>>>(static_cast<const f16*>(q),
+                                                                static_cast<const f16*>(kcb), static_cast<f16*>(out),
+                                                                Hq, Hkv, R);
   else
-    qtable_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float*>(q), static_cast<const float*>(kcb),
-                                              static_cast<float*>(out), Hq, Hkv, R);
+    qtable_kernel<float, kGroups, kCodes><<<grid, kCodes, 0, s>>>(static_cast<const float*>(q),
+                                                                  static_cast<const float*>(kcb),
+                                                                  static_cast<float*>(out), Hq, Hkv, R);
   return hipGetLastError();
 }
 
@@ -203,9 +212,88 @@ __global__ void __launch_bounds__(128) combine_sum_kernel(const float* part, con
   out[static_cast<int64_t>(bh) * kHeadDim + d] = acc;
 }
 
-hipError_t launch_value_reduce(int dtype, int R, int B, const ValueReduceArgs& a, float* out, hipStream_t s) {
+// Bit-packed records (G = 2, N = 64, W = 64, R up to 32): the same split, fixed-point bins and partials.
+// Bins [kGqa][2][R][64] (64 KiB at R = 32); each token reads its R x 2 indices field by field.
+__global__ void __launch_bounds__(256) value_reduce_bits_kernel(const ValueReduceArgs a, int R) {
+  constexpr int TPT = kSplitTokens / 256;
+  constexpr int G = kWideGroups, N = kWideCodes, W = kHeadDim / G;
+  __shared__ float red[4][kGqa];
+  __shared__ __attribute__((aligned(16))) int32_t bins[kGqa * G * kWideMaxResiduals * N];
+  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens);
+  const int L = sb.len;
+  const int t0 = split * kSplitTokens;
+  if (t0 >= L) return;
+  const int64_t row0 = sb.start + t0;
+  const int h0 = kv * kGqa;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int Wd = wide_record_words(R);
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(a.v_codes);
+  bool valid[TPT];
+  float w[TPT][kGqa];
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    const int t = t0 + tid + 256 * k;
+    valid[k] = t < L;
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h)
+      w[k][h] = valid[k] ? a.p[(static_cast<int64_t>(b) * a.n_q_heads + h0 + h) * a.p_stride + t] : 0.f;
+  }
+  for (int i = tid; i < kGqa * G * R * N; i += 256) bins[i] = 0;
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) {
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) mx = fmaxf(mx, fabsf(w[k][h]));
+    mx = wave_max(mx);
+    if (lane == 0) red[wave][h] = mx;
+  }
+  __syncthreads();
+  float fx_scale[kGqa];
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) {
+    const float mx = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+    fx_scale[h] = mx > 0.f ? 1048576.f / mx : 1.f;
+  }
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    if (!valid[k]) continue;
+    int32_t fx[kGqa];
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<int32_t>(rintf(w[k][h] * fx_scale[h]));
+    const uint32_t* rec = words + (static_cast<int64_t>(kv) * a.total_tokens + row0 + tid + 256 * k) * Wd;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint32_t l = packed_field(rec, r, g);
+#pragma unroll
+        for (int h = 0; h < kGqa; ++h) atomicAdd(&bins[((h * G + g) * R + r) * N + l], fx[h]);
+      }
+  }
+  __syncthreads();
+  // o[h][64g + w] = sum_r sum_l bins[h][g][r][l] * CV[g][r][l][w] / fx_scale[h]; each thread 2 outputs
+  float* part = a.part + ((static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits + split) * kPartFloats;
+  const int64_t row_stride = static_cast<int64_t>(a.n_splits) * kPartFloats;
+  const f16* vcb = static_cast<const f16*>(a.v_cb) + static_cast<int64_t>(kv) * G * R * N * W;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, h = idx >> 7, d = idx & 127, g = d / W, wd = d % W;
+    float acc = 0.f;
+    for (int r = 0; r < R; ++r) {
+      const int32_t* bb = bins + ((h * G + g) * R + r) * N;
+      const f16* cv = vcb + (static_cast<int64_t>(g) * R + r) * N * W + wd;
+      for (int l = 0; l < N; ++l) acc = fmaf(static_cast<float>(bb[l]), static_cast<float>(cv[l * W]), acc);
+    }
+    part[h * row_stride + 4 + d] = acc / fx_scale[h];
+  }
+}
+
+hipError_t launch_value_reduce(int dtype, bool packed, int R, int B, const ValueReduceArgs& a, float* out,
+                               hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv_heads, B);
-  if (dtype == COMMVQ_F16) {
+  if (packed) {  // fp16 only
+    value_reduce_bits_kernel<<<grid, 256, 0, s>>>(a, R);
+  } else if (dtype == COMMVQ_F16) {
     if (R == 1) value_reduce_kernel<f16, 1><<<grid, 256, 0, s>>>(a);
     else value_reduce_kernel<f16, 2><<<grid, 256, 0, s>>>(a);
   } else {
@@ -474,6 +562,57 @@ __global__ void __launch_bounds__(256) encode_greedy_bits_kernel(const f16* x, c
     }
     while (word < Wd) flush();
   }
+}
+
+// Residual codebook M-step on bit-packed records. One workgroup per (group g, slice of kUpdSlice dims, KV
+// head): the fp32 sums of every round's bins for the slice ([R][64][kUpdSlice], 64 KiB at R = 32) and the
+// counts sit in LDS. Each token walks its rounds once: it adds its residual slice to bin (r, l), then
+// subtracts the input codeword's slice, so round r's bins receive x_g - sum_{r' < r} C_in[g][r'][l_r'].
+// Thread i then writes entry i of the slice as the bin mean, or the input value when no token selects the
+// codeword. The accumulation order across lanes is not fixed (fp32 rounding may differ run to run).
+constexpr int kUpdSlice = 8;
+__global__ void __launch_bounds__(256) codebook_update_bits_kernel(const f16* x, const uint32_t* words, int R,
+                                                                   int64_t n, const f16* cb_in, f16* cb_out) {
+  constexpr int G = kWideGroups, N = kWideCodes, W = kHeadDim / G, kSlices = W / kUpdSlice;
+  __shared__ float sum[kWideMaxResiduals * N * kUpdSlice];
+  __shared__ uint32_t cnt[kWideMaxResiduals * N];
+  const int g = blockIdx.x / kSlices, s = blockIdx.x % kSlices, kv = blockIdx.y;
+  for (int i = threadIdx.x; i < R * N * kUpdSlice; i += blockDim.x) sum[i] = 0.f;
+  for (int i = threadIdx.x; i < R * N; i += blockDim.x) cnt[i] = 0u;
+  __syncthreads();
+  const int Wd = wide_record_words(R);
+  const int64_t cb_base = (static_cast<int64_t>(kv) * G + g) * R * N * W + s * kUpdSlice;  // + (r N + l) W + w
+  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) {
+    const uint32_t* rec = words + (static_cast<int64_t>(kv) * n + t) * Wd;
+    const f16* xv = x + (static_cast<int64_t>(kv) * n + t) * kHeadDim + g * W + s * kUpdSlice;
+    float res[kUpdSlice];
+#pragma unroll
+    for (int w = 0; w < kUpdSlice; ++w) res[w] = static_cast<float>(xv[w]);
+    for (int r = 0; r < R; ++r) {
+      const int l = static_cast<int>(packed_field(rec, r, g));
+#pragma unroll
+      for (int w = 0; w < kUpdSlice; ++w) atomicAdd(&sum[(r * N + l) * kUpdSlice + w], res[w]);
+      atomicAdd(&cnt[r * N + l], 1u);
+      const f16* c = cb_in + cb_base + static_cast<int64_t>(r * N + l) * W;
+#pragma unroll
+      for (int w = 0; w < kUpdSlice; ++w) res[w] -= static_cast<float>(c[w]);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R * N * kUpdSlice; i += blockDim.x) {
+    const int rl = i / kUpdSlice, w = i % kUpdSlice;  // rl = r N + l
+    const int64_t o = cb_base + static_cast<int64_t>(rl) * W + w;
+    const uint32_t c = cnt[rl];
+    cb_out[o] = c > 0 ? static_cast<f16>(sum[i] / static_cast<float>(c)) : cb_in[o];
+  }
+}
+
+hipError_t launch_codebook_update_bits(int R, int Hkv, const void* x, const uint32_t* words, int64_t n,
+                                       const void* cb_in, void* cb_out, hipStream_t s) {
+  const dim3 grid(kWideGroups * (kHeadDim / kWideGroups / kUpdSlice), Hkv);
+  codebook_update_bits_kernel<<<grid, 256, 0, s>>>(static_cast<const f16*>(x), words, R, n,
+                                                   static_cast<const f16*>(cb_in), static_cast<f16*>(cb_out));
+  return hipGetLastError();
 }
 
 hipError_t launch_encode_greedy_bits(int R, int Hkv, const void* x, const void* cb, int64_t n, uint32_t* words,
