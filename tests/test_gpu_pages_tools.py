@@ -99,11 +99,13 @@ def test_pages_codebook_update_matches_oracle(vq, R, n):
     codes = rng.integers(0, 60, size=(Hkv, R, n, 2)).astype(np.uint8)
     words = workloads.pack_bits(codes, 6)
     d = vq.make_dims(1, 4 * Hkv, Hkv, R, "float16", n_groups=2, n_codes=64)
-    got = vq.codebook_update(d, torch.from_numpy(x).cuda(),
-                             torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).cuda(),
-                             torch.from_numpy(cb).cuda())
+    args = (torch.from_numpy(x).cuda(), torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).cuda(),
+            torch.from_numpy(cb).cuda())
+    got = vq.codebook_update(d, *args)
+    again = vq.codebook_update(d, *args)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
+    np.testing.assert_array_equal(again.cpu().numpy(), got)  # exact sums: no dependence on the order of adds
     od = oracle.dims(1, 4 * Hkv, Hkv, R, n_groups=2, n_codes=64)
     np.testing.assert_array_equal(oracle.unpack_bits(od, words, n), codes)  # the records hold these codes
     ref, counts = oracle.codebook_update(od, x, cb, codes, want_counts=True)
@@ -111,7 +113,7 @@ def test_pages_codebook_update_matches_oracle(vq, R, n):
     assert not used[..., 60:].any()
     np.testing.assert_array_equal(got[..., 60:, :], cb[..., 60:, :])  # unused codewords are kept
     np.testing.assert_array_equal(got[~used], cb[~used])
-    # fp32 sums rounded once to fp16: within one fp16 ulp of the fp64 mean
+    # fp64 residuals summed exactly, rounded to fp16 at the end: within one fp16 ulp of the fp64 mean
     ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
     assert np.all(np.abs(got.astype(np.float64) - ref) <= ulp)
 

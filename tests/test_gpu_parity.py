@@ -248,10 +248,12 @@ def test_codebook_update_matches_oracle(vq, dtype, R, n):
     rng = np.random.default_rng(60 + R)
     codes = rng.integers(0, 250, size=(Hkv, R, n, 16)).astype(np.uint8)
     d = vq.make_dims(1, 4 * Hkv, Hkv, R, dtype)
-    got = vq.codebook_update(d, torch.from_numpy(x).cuda(), torch.from_numpy(codes).cuda(),
-                             torch.from_numpy(cb).cuda())
+    args = (torch.from_numpy(x).cuda(), torch.from_numpy(codes).cuda(), torch.from_numpy(cb).cuda())
+    got = vq.codebook_update(d, *args)
+    again = vq.codebook_update(d, *args)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
+    np.testing.assert_array_equal(again.cpu().numpy(), got)  # exact sums: no dependence on the order of adds
     od = oracle.dims(1, 4 * Hkv, Hkv, R)
     ref, counts = oracle.codebook_update(od, x, cb, codes, want_counts=True)
     used = counts > 0

@@ -423,42 +423,65 @@ __global__ void __launch_bounds__(256) encode_greedy_kernel(const T* x, const T*
 
 // ------------------------------------------------------------------------ residual codebook M-step
 // One workgroup per (group g, round r, KV head): every token adds its round-r residual (x_g minus the input
-// codewords its earlier rounds select) to the bin of its round-r index, in fp32 LDS accumulators; then
-// thread l writes codeword l as the bin mean, or the input codeword when no token selects it. The
-// accumulation order across lanes is not fixed, so results may differ run to run by fp32 rounding.
+// codewords its earlier rounds select) to the bin of its round-r index; then thread l writes codeword l as
+// the bin mean, or the input codeword when no token selects it. As in the bit-packed M-step below, the
+// residual is kept in fp64 and the bins are int64 fixed point (integer LDS atomics; the scale 2^62 / (bound n)
+// with bound = max|x_g| + r max|earlier codeword| keeps every sum inside int64), so the sums are exact and
+// the result does not depend on the order of the adds.
 template <typename T, int R>
 __global__ void __launch_bounds__(256) codebook_update_kernel(const T* x, const uint8_t* codes, int64_t n,
                                                               const T* cb_in, T* cb_out) {
   const int g = blockIdx.x, r = blockIdx.y, kv = blockIdx.z;
-  __shared__ float sum[kCodes * kGroupDim];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ unsigned long long sum[kCodes * kGroupDim];
   __shared__ uint32_t cnt[kCodes];
-  for (int i = threadIdx.x; i < kCodes * kGroupDim; i += blockDim.x) sum[i] = 0.f;
-  for (int i = threadIdx.x; i < kCodes; i += blockDim.x) cnt[i] = 0u;
-  __syncthreads();
+  __shared__ float red[2][4];
+  for (int i = tid; i < kCodes * kGroupDim; i += blockDim.x) sum[i] = 0ull;
+  for (int i = tid; i < kCodes; i += blockDim.x) cnt[i] = 0u;
   const T* cbg = cb_in + (static_cast<int64_t>(kv) * kGroups + g) * R * kCodes * kGroupDim;  // [R][N][W]
-  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) {
+  float xmax = 0.f, cmax = 0.f;
+  for (int i = tid; i < r * kCodes * kGroupDim; i += blockDim.x) cmax = fmaxf(cmax, fabsf(ld(cbg + i)));
+  for (int64_t t = tid; t < n; t += blockDim.x) {
     const T* xv = x + (static_cast<int64_t>(kv) * n + t) * kHeadDim + g * kGroupDim;
-    float res[kGroupDim];
 #pragma unroll
-    for (int w = 0; w < kGroupDim; ++w) res[w] = ld(xv + w);
+    for (int w = 0; w < kGroupDim; ++w) xmax = fmaxf(xmax, fabsf(ld(xv + w)));
+  }
+  xmax = wave_max(xmax);
+  cmax = wave_max(cmax);
+  if (lane == 0) {
+    red[0][wave] = xmax;
+    red[1][wave] = cmax;
+  }
+  __syncthreads();
+  const double bound = static_cast<double>(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]))) +
+                       r * static_cast<double>(fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3])));
+  const double scale = bound > 0.0 && n > 0 ? ldexp(1.0, 62) / (bound * static_cast<double>(n)) : 1.0;
+  for (int64_t t = tid; t < n; t += blockDim.x) {
+    const T* xv = x + (static_cast<int64_t>(kv) * n + t) * kHeadDim + g * kGroupDim;
+    double res[kGroupDim];
+#pragma unroll
+    for (int w = 0; w < kGroupDim; ++w) res[w] = static_cast<double>(ld(xv + w));
     for (int rp = 0; rp < r; ++rp) {
       const int l = codes[((static_cast<int64_t>(kv) * R + rp) * n + t) * kGroups + g];
       const T* c = cbg + (static_cast<int64_t>(rp) * kCodes + l) * kGroupDim;
 #pragma unroll
-      for (int w = 0; w < kGroupDim; ++w) res[w] -= ld(c + w);
+      for (int w = 0; w < kGroupDim; ++w) res[w] -= static_cast<double>(ld(c + w));
     }
     const int l = codes[((static_cast<int64_t>(kv) * R + r) * n + t) * kGroups + g];
 #pragma unroll
-    for (int w = 0; w < kGroupDim; ++w) atomicAdd(&sum[l * kGroupDim + w], res[w]);
+    for (int w = 0; w < kGroupDim; ++w)
+      atomicAdd(&sum[l * kGroupDim + w], static_cast<unsigned long long>(static_cast<long long>(rint(res[w] * scale))));
     atomicAdd(&cnt[l], 1u);
   }
   __syncthreads();
-  for (int l = threadIdx.x; l < kCodes; l += blockDim.x) {
+  for (int l = tid; l < kCodes; l += blockDim.x) {
     const int64_t o = ((static_cast<int64_t>(kv) * kGroups + g) * R + r) * kCodes * kGroupDim + l * kGroupDim;
     const uint32_t c = cnt[l];
 #pragma unroll
     for (int w = 0; w < kGroupDim; ++w)
-      cb_out[o + w] = c > 0 ? static_cast<T>(sum[l * kGroupDim + w] / static_cast<float>(c)) : cb_in[o + w];
+      cb_out[o + w] = c > 0 ? static_cast<T>(static_cast<double>(static_cast<long long>(sum[l * kGroupDim + w])) /
+                                             (scale * c))
+                            : cb_in[o + w];
   }
 }
 
@@ -565,45 +588,85 @@ __global__ void __launch_bounds__(256) encode_greedy_bits_kernel(const f16* x, c
 }
 
 // Residual codebook M-step on bit-packed records. One workgroup per (group g, slice of kUpdSlice dims, KV
-// head): the fp32 sums of every round's bins for the slice ([R][64][kUpdSlice], 64 KiB at R = 32) and the
-// counts sit in LDS. Each token walks its rounds once: it adds its residual slice to bin (r, l), then
-// subtracts the input codeword's slice, so round r's bins receive x_g - sum_{r' < r} C_in[g][r'][l_r'].
+// head): every round's bins for the slice ([R][64][kUpdSlice]), their counts and the slice of every input
+// codeword (fp32) sit in LDS. Each token walks its rounds once: it adds its residual slice to bin (r, l),
+// then subtracts the input codeword's slice, so round r's bins receive x_g - sum_{r' < r} C_in[g][r'][l_r'].
+// The residual is kept in fp64, where x and the fp16 codewords, and their sums over the rounds, are exact, so
+// late rounds carry no accumulated rounding. The bins are int64 fixed point (LDS float atomics are slow on
+// this chip, integer ones are not): a first pass bounds every residual by max|x slice| + R max|codeword
+// slice|, and the scale 2^62 / (bound n) keeps each term within 2^62 / n, so no bin can overflow. The sums
+// are exact, so the result does not depend on the order of the adds; only the final fp16 rounding remains.
 // Thread i then writes entry i of the slice as the bin mean, or the input value when no token selects the
-// codeword. The accumulation order across lanes is not fixed (fp32 rounding may differ run to run).
-constexpr int kUpdSlice = 8;
+// codeword.
+constexpr int kUpdSlice = 4;
 __global__ void __launch_bounds__(256) codebook_update_bits_kernel(const f16* x, const uint32_t* words, int R,
                                                                    int64_t n, const f16* cb_in, f16* cb_out) {
   constexpr int G = kWideGroups, N = kWideCodes, W = kHeadDim / G, kSlices = W / kUpdSlice;
-  __shared__ float sum[kWideMaxResiduals * N * kUpdSlice];
+  static_assert(kUpdSlice == 4, "one float4 of codeword slice per (round, code)");
+  __shared__ unsigned long long sum[kWideMaxResiduals * N * kUpdSlice];
+  __shared__ float4 cws[kWideMaxResiduals * N];
   __shared__ uint32_t cnt[kWideMaxResiduals * N];
+  __shared__ float red[2][4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = blockIdx.x / kSlices, s = blockIdx.x % kSlices, kv = blockIdx.y;
-  for (int i = threadIdx.x; i < R * N * kUpdSlice; i += blockDim.x) sum[i] = 0.f;
-  for (int i = threadIdx.x; i < R * N; i += blockDim.x) cnt[i] = 0u;
-  __syncthreads();
-  const int Wd = wide_record_words(R);
   const int64_t cb_base = (static_cast<int64_t>(kv) * G + g) * R * N * W + s * kUpdSlice;  // + (r N + l) W + w
-  for (int64_t t = threadIdx.x; t < n; t += blockDim.x) {
+  for (int i = tid; i < R * N * kUpdSlice; i += blockDim.x) sum[i] = 0ull;
+  float cmax = 0.f, xmax = 0.f;
+  for (int i = tid; i < R * N; i += blockDim.x) {
+    const f16* c = cb_in + cb_base + static_cast<int64_t>(i) * W;
+    const float4 v = make_float4(static_cast<float>(c[0]), static_cast<float>(c[1]), static_cast<float>(c[2]),
+                                 static_cast<float>(c[3]));
+    cws[i] = v;
+    cnt[i] = 0u;
+    cmax = fmaxf(cmax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  for (int64_t t = tid; t < n; t += blockDim.x) {
+    const f16* xv = x + (static_cast<int64_t>(kv) * n + t) * kHeadDim + g * W + s * kUpdSlice;
+#pragma unroll
+    for (int w = 0; w < kUpdSlice; ++w) xmax = fmaxf(xmax, fabsf(static_cast<float>(xv[w])));
+  }
+  xmax = wave_max(xmax);
+  cmax = wave_max(cmax);
+  if (lane == 0) {
+    red[0][wave] = xmax;
+    red[1][wave] = cmax;
+  }
+  __syncthreads();
+  const float bound = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])) +
+                      static_cast<float>(R) * fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  const double scale = bound > 0.f && n > 0 ? ldexp(1.0, 62) / (static_cast<double>(bound) * static_cast<double>(n))
+                                            : 1.0;
+  const int Wd = wide_record_words(R);
+  for (int64_t t = tid; t < n; t += blockDim.x) {
     const uint32_t* rec = words + (static_cast<int64_t>(kv) * n + t) * Wd;
     const f16* xv = x + (static_cast<int64_t>(kv) * n + t) * kHeadDim + g * W + s * kUpdSlice;
-    float res[kUpdSlice];
+    double res[kUpdSlice];
 #pragma unroll
-    for (int w = 0; w < kUpdSlice; ++w) res[w] = static_cast<float>(xv[w]);
+    for (int w = 0; w < kUpdSlice; ++w) res[w] = static_cast<double>(static_cast<float>(xv[w]));
     for (int r = 0; r < R; ++r) {
       const int l = static_cast<int>(packed_field(rec, r, g));
+      // the codeword read goes out before the atomics: LDS operations complete in order, so waiting for it
+      // afterwards would also wait for every atomic of the round
+      const float4 c = cws[r * N + l];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int w = 0; w < kUpdSlice; ++w) atomicAdd(&sum[(r * N + l) * kUpdSlice + w], res[w]);
+      for (int w = 0; w < kUpdSlice; ++w)
+        atomicAdd(&sum[(r * N + l) * kUpdSlice + w],
+                  static_cast<unsigned long long>(static_cast<long long>(rint(res[w] * scale))));
       atomicAdd(&cnt[r * N + l], 1u);
-      const f16* c = cb_in + cb_base + static_cast<int64_t>(r * N + l) * W;
-#pragma unroll
-      for (int w = 0; w < kUpdSlice; ++w) res[w] -= static_cast<float>(c[w]);
+      res[0] -= c.x;
+      res[1] -= c.y;
+      res[2] -= c.z;
+      res[3] -= c.w;
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < R * N * kUpdSlice; i += blockDim.x) {
+  for (int i = tid; i < R * N * kUpdSlice; i += blockDim.x) {
     const int rl = i / kUpdSlice, w = i % kUpdSlice;  // rl = r N + l
     const int64_t o = cb_base + static_cast<int64_t>(rl) * W + w;
     const uint32_t c = cnt[rl];
-    cb_out[o] = c > 0 ? static_cast<f16>(sum[i] / static_cast<float>(c)) : cb_in[o];
+    const double mean = static_cast<double>(static_cast<long long>(sum[i])) / (scale * c);
+    cb_out[o] = c > 0 ? static_cast<f16>(static_cast<float>(mean)) : cb_in[o];
   }
 }
 
