@@ -14,6 +14,7 @@ cpu_baseline times the fp64 oracle on the host on a bounded sample of the same w
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -156,9 +157,12 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
     if layers <= 0:
         layers = max(4, int(math.ceil((1 << 30) / per_layer["total"])))
     rope = vq.rope_table(d, int(base["max_len"]))
+    # the rotated copies keep the first copy's sequence lengths (a ragged workload would otherwise draw new
+    # ones per copy) and draw new codes, codebooks and queries
+    same_lengths = dataclasses.replace(cfg, lengths=tuple(int(x) for x in base["seq_len"]), ragged_range=None)
     Ls = []
     for i in range(layers):
-        inp = base if i == 0 else workloads.make_inputs(cfg, seed=cfg.seed + 1000 * i)
+        inp = base if i == 0 else workloads.make_inputs(same_lengths, seed=cfg.seed + 1000 * i)
         Ls.append(vq.Layer(d, inp, rope=rope, rope_positions=int(base["max_len"])))
     torch.cuda.synchronize()
     check_err = None
