@@ -114,10 +114,11 @@ def test_attn_decode_clamps_sequence_descriptors(vq, name, kw):
     assert err_nat <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,R", [("float16", 2), ("float32", 1)])
-def test_value_reduce_clamps_sequence_descriptors(vq, dtype, R):
-    announce(f"value_reduce out-of-bounds descriptors {dtype} R={R}")
-    cfg = workloads.custom("bounds_vr", len(LENGTHS), 8, 2, LENGTHS, R, dtype, 32)
+@pytest.mark.parametrize("dtype,R,packed", [("float16", 2, False), ("float32", 1, False), ("float16", 21, True)])
+def test_value_reduce_clamps_sequence_descriptors(vq, dtype, R, packed):
+    announce(f"value_reduce out-of-bounds descriptors {dtype} R={R} packed={packed}")
+    extra = dict(n_groups=2, n_codes=64) if packed else {}
+    cfg = workloads.custom("bounds_vr", len(LENGTHS), 8, 2, LENGTHS, R, dtype, 32, **extra)
     inp = workloads.make_inputs(cfg)
     total = int(inp["total_tokens"])
     d = vq.dims_of(cfg)
@@ -133,7 +134,9 @@ def test_value_reduce_clamps_sequence_descriptors(vq, dtype, R):
                           torch.from_numpy(l_pass).cuda(), MAX_LEN, total, ws)
     torch.cuda.synchronize()
     s_cl, l_cl = descriptors(CLAMPED)
-    ref = oracle.value_reduce(oracle.dims_of(cfg), p, inp["v_codes"], inp["v_cb"], s_cl, l_cl, MAX_LEN)
+    od = oracle.dims_of(cfg)
+    vc = oracle.unpack_bits(od, inp["v_codes"], total) if packed else inp["v_codes"]
+    ref = oracle.value_reduce(od, p, vc, inp["v_cb"], s_cl, l_cl, MAX_LEN)
     g = got.cpu().numpy()
     assert np.all(g[3] == 0.0)
     err = rowwise_rel_err(g[:3], ref[:3])
