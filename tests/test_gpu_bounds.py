@@ -142,3 +142,27 @@ def test_value_reduce_clamps_sequence_descriptors(vq, dtype, R, packed):
     err = rowwise_rel_err(g[:3], ref[:3])
     print(f"value_reduce {dtype} R={R}: {err:.3e}", flush=True)
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_all_sequences_empty(vq, packed):
+    """max_len = 0 and total_tokens = 0: no code row is read and every output row is zero."""
+    announce(f"all sequences empty packed={packed}")
+    extra = dict(n_groups=2, n_codes=64) if packed else {}
+    R = 11 if packed else 2
+    cfg = workloads.custom("empty", 3, 8, 2, (0, 0, 0), R, "float16", 34, **extra)
+    inp = workloads.make_inputs(cfg)
+    d = vq.dims_of(cfg)
+    codes = torch.zeros(4096, dtype=torch.int32, device="cuda")  # never read
+    q = torch.from_numpy(inp["q"]).cuda()
+    k_cb, v_cb = torch.from_numpy(inp["k_cb"]).cuda(), torch.from_numpy(inp["v_cb"]).cuda()
+    s0 = torch.zeros(3, dtype=torch.int64, device="cuda")
+    l0 = torch.zeros(3, dtype=torch.int32, device="cuda")
+    rope = vq.rope_table(d, 1)
+    out = torch.full((3, 8, 128), 7.0, device="cuda")
+    vq.attn_decode(d, q, codes, codes, k_cb, v_cb, s0, l0, 0, 0, rope, 1, out=out)
+    p = torch.zeros(16, dtype=torch.float32, device="cuda")
+    vr = torch.full((3, 8, 128), 7.0, device="cuda")
+    vq.value_reduce(d, p, codes, v_cb, s0, l0, 0, 0, out=vr)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0.0) and torch.all(vr == 0.0)
