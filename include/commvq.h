@@ -195,7 +195,8 @@ int commvq_encode_greedy(const commvq_dims* d /* host */, const void* x, const v
  *   codebook_in   [Hkv][G][R][N][W] in dims->dtype
  *   codebook_out  same shape and type; must not overlap codebook_in (COMMVQ_EINVAL)
  * The residuals are formed in fp64 and summed exactly (int64 fixed point), so the result does not depend on
- * the order of the adds: repeated calls give identical codebooks, within one rounding of the exact mean.
+ * the order of the adds: repeated calls give identical codebooks, each entry within one ulp of dims->dtype
+ * of the exact mean.
  * n_tokens = 0 copies codebook_in (x and codes may then be NULL).
  * ------------------------------------------------------------------------------------------- */
 int commvq_codebook_update(const commvq_dims* d /* host */, const void* x, const uint8_t* codes,
