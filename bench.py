@@ -303,6 +303,19 @@ def codebook_tools_timing(reps: int = 3):
     }
 
 
+# workloads of bench.py --profile (one attention kernel per workload kind; 20 launches each)
+PROFILE_ALSO = ("llama8b_128k_r1", "pages_g64_r11_128k", "pages_g64_r21_128k")
+
+# The pages' only absolute timing of this path, next to the workload it is closest to: per-layer decode
+# latency at 8K context, naive (decode the codes, then attend) and with the commutative codebook
+# ("CommVQ: Commutative Vector Quantization for KV Cache Compression" summary page, measured-effects table;
+# the paper's Table 5 as the pith.science referee report describes it). No GPU, model or batch is named.
+PAGES_CONTEXT = {
+    "llama8b_8k_r2": {"per_layer_latency_us": {"naive": 2400.0, "commutative_codebook": 400.0},
+                      "hardware": "not named on the pages", "role": "context, not a target"},
+}
+
+
 def workload(name: str):
     return workloads.CONFIGS[name] if name in workloads.CONFIGS else workloads.PAGES_CONFIGS[name]
 
@@ -313,7 +326,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama8b_128k_r2", help="primary workload (value, roofline)")
-    ap.add_argument("--also", default="llama8b_128k_r1,pages_g64_r11_128k,pages_g64_r21_128k",
+    ap.add_argument("--also", default="llama8b_128k_r1,pages_g64_r11_128k,pages_g64_r21_128k,llama8b_8k_r2",
                     help="comma list of extra workloads reported in variants")
     ap.add_argument("--layers", type=int, default=0, help="distinct layer buffers to rotate (0: >= 1 GiB)")
     ap.add_argument("--no-graph", action="store_true")
@@ -330,8 +343,8 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.profile:
-        names = [args.config] + [s for s in args.also.split(",") if s and s != args.config]
+    if args.profile:  # a fixed set, in the dispatch order the profile summaries are read in
+        names = [args.config] + [s for s in PROFILE_ALSO if s != args.config]
         profile_run(names, max(args.steps, 1))
         return
     cfg = workloads.CONFIGS[args.config]
@@ -340,6 +353,8 @@ def main():
     for name in [s for s in args.also.split(",") if s and s != cfg.name]:
         variants[name], _ = run_config(workload(name), args.steps, args.warmup, args.layers, not args.no_graph,
                                        args.check)
+        if name in PAGES_CONTEXT:
+            variants[name]["pages_context"] = PAGES_CONTEXT[name]
 
     achieved = prim["bytes"]["codes"] / (prim["us_per_launch"] * 1e-6) * 1e-9
     traffic = read_traffic(cfg.name)
