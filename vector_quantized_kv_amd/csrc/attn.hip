@@ -236,26 +236,6 @@ __device__ __forceinline__ void value_groups(Args&&... args) {
   value_seq<T, 0>(std::make_integer_sequence<int, kGroups>{}, args...);
 }
 
-// Fill one codebook slot (16 groups x 256 codes, row = 8 values of T) with direct global->LDS 16-byte
-// loads; each wave moves its share. cb_kv points at codebook [kv][0][0][0][0]; r selects the residual.
-template <typename T, int R, int kW>
-__device__ __forceinline__ void load_table(const T* cb_kv, int r, unsigned char* dst, int wave, int lane) {
-  constexpr int kRowBytes = kGroupDim * sizeof(T);
-  constexpr int kChunksPerRow = kRowBytes / 16;
-  constexpr int kChunks = kGroups * kCodes * kChunksPerRow;
-  constexpr int kPerWave = kChunks / kW;
-#pragma unroll
-  for (int i = 0; i < kPerWave / 64; ++i) {
-    const int c = wave * kPerWave + i * 64 + lane;
-    const int rowi = c / kChunksPerRow, part = c % kChunksPerRow;
-    const int g = rowi >> 8, l = rowi & (kCodes - 1);
-    const unsigned char* gp =
-        reinterpret_cast<const unsigned char*>(cb_kv + ((static_cast<int64_t>(g) * R + r) * kCodes + l) * kGroupDim) +
-        part * 16;
-    __builtin_amdgcn_global_load_lds(gp, dst + (wave * kPerWave + i * 64) * 16, 16, 0, 0);
-  }
-}
-
 template <typename T, int R>
 __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnArgs a) {
   constexpr bool kF32 = std::is_same<T, float>::value;
@@ -748,16 +728,11 @@ __global__ void __launch_bounds__(Shape<T>::kWaves * 64) attn_kernel(const AttnA
 }  // namespace
 
 hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, hipStream_t s) {
+  if (dtype == COMMVQ_F16) return launch_attn_f16(R, B, a, s);
   dim3 grid(a.n_splits * a.n_kv_heads, B);
-  if (dtype == COMMVQ_F16) {
-    constexpr int kThreads = Shape<f16>::kWaves * 64;
-    if (R == 1) attn_kernel<f16, 1><<<grid, kThreads, 0, s>>>(a);
-    else attn_kernel<f16, 2><<<grid, kThreads, 0, s>>>(a);
-  } else {
-    constexpr int kThreads = Shape<float>::kWaves * 64;
-    if (R == 1) attn_kernel<float, 1><<<grid, kThreads, 0, s>>>(a);
-    else attn_kernel<float, 2><<<grid, kThreads, 0, s>>>(a);
-  }
+  constexpr int kThreads = Shape<float>::kWaves * 64;
+  if (R == 1) attn_kernel<float, 1><<<grid, kThreads, 0, s>>>(a);
+  else attn_kernel<float, 2><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -133,14 +133,35 @@ __device__ __forceinline__ void static_for(Fn&& f) {
 
 inline __device__ float2 cmul_conj(float2 x, float2 c) { return make_float2(x.x * c.x + x.y * c.y, x.y * c.x - x.x * c.y); }
 
+// Fill one codebook slot (16 groups x 256 codes, row = 8 values of T) with direct global->LDS 16-byte
+// loads; each wave moves its share. cb_kv points at codebook [kv][0][0][0][0]; r selects the residual.
+template <typename T, int R, int kW>
+__device__ __forceinline__ void load_table(const T* cb_kv, int r, unsigned char* dst, int wave, int lane) {
+  constexpr int kRowBytes = kGroupDim * sizeof(T);
+  constexpr int kChunksPerRow = kRowBytes / 16;
+  constexpr int kChunks = kGroups * kCodes * kChunksPerRow;
+  constexpr int kPerWave = kChunks / kW;
+#pragma unroll
+  for (int i = 0; i < kPerWave / 64; ++i) {
+    const int c = wave * kPerWave + i * 64 + lane;
+    const int rowi = c / kChunksPerRow, part = c % kChunksPerRow;
+    const int g = rowi >> 8, l = rowi & (kCodes - 1);
+    const unsigned char* gp =
+        reinterpret_cast<const unsigned char*>(cb_kv + ((static_cast<int64_t>(g) * R + r) * kCodes + l) * kGroupDim) +
+        part * 16;
+    __builtin_amdgcn_global_load_lds(gp, dst + (wave * kPerWave + i * 64) * 16, 16, 0, 0);
+  }
+}
+
 // Wave softmax over the wave's blocks (block i holds tokens (wave + kW i) * 64 + lane of the split): scales
-// the scores, masks tokens at or past nvalid, overwrites them with p, and publishes (m_w, l_w) per head.
+// the scores, masks tokens at or past nvalid, overwrites them with p, and returns (m_w, l_w) per head
+// (wave-uniform values).
 template <int kW>
-__device__ __forceinline__ void wave_softmax(f4 (&sc)[kMaxBlocks], const int my_blocks, const int wave, const int lane,
-                                             const int nvalid, const float scale, float (&wave_ml)[2][kW][kGqa]) {
+__device__ __forceinline__ void wave_softmax_regs(f4 (&sc)[kMaxBlocks], const int my_blocks, const int wave,
+                                                  const int lane, const int nvalid, const float scale,
+                                                  float (&m_w)[kGqa], float (&l_w)[kGqa]) {
   // m_w = max over the wave's valid tokens, p = e^{s - m_w}, l_w = sum p. A wave with no valid token
   // has m_w = -inf, p = 0, l_w = 0, and weight e^{m_w - M} = 0 in the workgroup combine.
-  float m_w[kGqa], l_w[kGqa];
 #pragma unroll
   for (int h = 0; h < kGqa; ++h) {
     float mx = -INFINITY;
@@ -160,6 +181,13 @@ __device__ __forceinline__ void wave_softmax(f4 (&sc)[kMaxBlocks], const int my_
     }
     l_w[h] = wave_sum(sm);
   }
+}
+// The same, publishing (m_w, l_w) in LDS for the workgroup epilogue.
+template <int kW>
+__device__ __forceinline__ void wave_softmax(f4 (&sc)[kMaxBlocks], const int my_blocks, const int wave, const int lane,
+                                             const int nvalid, const float scale, float (&wave_ml)[2][kW][kGqa]) {
+  float m_w[kGqa], l_w[kGqa];
+  wave_softmax_regs<kW>(sc, my_blocks, wave, lane, nvalid, scale, m_w, l_w);
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) {
@@ -171,13 +199,23 @@ __device__ __forceinline__ void wave_softmax(f4 (&sc)[kMaxBlocks], const int my_
 
 // Workgroup epilogue of a decode-attention work item (one split of one (sequence, KV head)): O holds this
 // wave's unnormalised p^T v in the quad layout of the value MFMAs, wave_ml every wave's (m_w, l_w).
+// With ml_regs set, (m_w, l_w) arrive in registers (wave_ml and is_last then point into the codebook space, past
+// the reduction buffer) and are published once every wave is done with the codebooks.
 template <int kW>
 __device__ __forceinline__ void attn_epilogue(const AttnArgs& a, unsigned char* lds, float (&wave_ml)[2][kW][kGqa],
                                               int& is_last, const int lane, const int tid, const int wave,
                                               f4 (&O)[2 * kGroups], const int b, const int kv, const int split,
-                                              const int L, const int S, const int64_t bh0, float* out_bh) {
+                                              const int L, const int S, const int64_t bh0, float* out_bh,
+                                              const float* ml_regs_m = nullptr, const float* ml_regs_l = nullptr) {
   constexpr int kThreads = kW * 64;
   lds_barrier();  // every wave is done with the value codebooks; their space is reused below
+  if (ml_regs_m != nullptr && lane == 0) {
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      wave_ml[0][wave][h] = ml_regs_m[h];
+      wave_ml[1][wave][h] = ml_regs_l[h];
+    }
+  }
 
   // O[c][h] sits in lane 16*rho + 4*b' + j (head h, dim 4c + j, one token quad per (rho, b')); each output
   // is the sum over the 16 lanes that share j. Two half-wave swap steps first fold the rows: each step pairs

@@ -1,0 +1,507 @@
+// Decode-step attention over a CommVQ cache with fp16 codebooks (byte layout: one index byte per group,
+// 16 groups of 8 dims, N = 256, R = 1 or 2) on gfx950: one fused kernel per call.
+//
+// What it computes (sources by page title and section):
+//   score_t = scale * sum_j Re( conj(q_j) * khat_{t,j} * e^{i t theta_j} )
+//   out     = sum_t softmax(score)_t * vhat_t
+// with khat, vhat the additive decodes (sum over R residual codebooks) of the stored code indices
+// ("1-bit quantization" tag page, CommVQ abstract; pith.science verdict for arXiv 2506.18879,
+// pith_extraction.key_machinery). Each key codeword block [[a,-b],[b,a]] commutes with the RoPE rotation,
+// so the rotation by position splits freely between the query and the key side: the part shared by a
+// 64-token block (e^{i 64 c theta}) goes on the query once per block, the per-token part e^{i f theta},
+// f = t mod 64 = lane, on the gathered codeword.
+//
+// Work item: one workgroup per (sequence b, KV head, split of `split_tokens` tokens), one per CU (it owns
+// the CU's LDS); 8 waves, each owning 64-token blocks (lane = token), up to 8 blocks per wave.
+//
+// Key scores are formed in fp32: the per-token rotation of the (residual-summed) codeword is computed in
+// fp32 from fp32 phases and contracted with the fp32 block query on the fp32 matrix core
+// (v_mfma_f32_4x4x1_16b_f32, query broadcast from one 4-lane block per dim). On this chip the fp32 MFMA does
+// not run beside VALU work of the SIMD (the fp16 ones do), and alternating the two costs extra cycles, so
+// the rotations and the MFMAs of a group are issued as separate bursts. fp16 operands would round the
+// key and the query to 11 bits, which at realistic logit ranges (score spreads of 10 and more) moves the
+// softmax by more than the 2e-3 output tolerance; in fp32 the key path is exact to a few fp32 ulps.
+// The fp32 phases of one lane (64 pairs) would take 128 registers, so they stay in LDS (32 KiB) and the key
+// pass runs group-major: a wave reads one group's phases once and applies them to 2 of its blocks (one
+// "sweep"); a full wave (8 blocks) makes four sweeps, shorter waves go block by block.
+//
+// LDS: slot 0 and slot 1 (64 KiB each: one residual codebook, 16 groups x 256 rows x 8 fp16) and the
+// phase table (32 KiB) fill the CU's 160 KiB. R = 1: slot 0 = key, slot 1 = value codebook, both loaded
+// in the prologue. R = 2: slots 0/1 = the two key codebooks; after the key pass both are refilled with the
+// value codebooks.
+//
+// Value pass (fp16 operands, fp32 accumulation; the softmax weights and value codewords are rounded
+// to fp16 once): R = 2 gathers both residual rows whole, sums them in fp16 and transposes each 4x4
+// (token x dim) tile of a lane quad with an identity MFMA; R = 1 reads each row with two transposing
+// 8-byte LDS reads, issued for the token of the transposed lane so that the delivered tile is the same
+// quad tile. Both then accumulate p^T x v with the 4x4x4 MFMA.
+// The workgroup combines its waves, writes (M, L, o[128]) per q head, and the last workgroup of each
+// (b, kv) merges the splits (attn_common.h).
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "attn_common.h"
+
+namespace commvq {
+namespace {
+
+constexpr int kW16 = 8;                              // waves per workgroup
+constexpr int kThreads16 = kW16 * 64;
+constexpr int kTab16 = kGroups * kCodes * 16;       // one residual codebook in LDS (fp16 rows of 8)
+constexpr int kPhaseBytes = kGroups * 2 * 64 * 16;  // fp32 fine phases [g][h][lane][2 pairs]
+constexpr int kSweep = 2;                            // blocks per key sweep
+constexpr int kValueLead = 4;                        // value records requested this many blocks ahead
+static_assert(2 * kTab16 + kPhaseBytes <= 160 * 1024, "codebook slots and phases fit the CU's LDS");
+
+// fp32 value of (fp16 lo/hi half of a) + (fp16 lo/hi half of b), rounded once (v_fma_mix with a unit
+// multiplier reads both halves as fp16 and adds in fp32).
+__device__ __forceinline__ float mix_add_lo(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ float mix_add_hi(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// fp32 4x4x1 MFMA with the A operand broadcast from block ABID: acc[m] += A[lane 4 ABID + m] * b.
+template <int ABID>
+__device__ __forceinline__ f4 mfma32_bcast(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 4, ABID, 0);
+}
+
+// Rotated key of one group: the lane's gathered row(s) (4 pairs (a, b) in fp16), summed over residuals in fp32,
+// times the lane's fine phases (p0 = pairs 4G, 4G+1, p1 = 4G+2, 4G+3, each (cos, sin)) in fp32:
+// w[2u] + i w[2u+1] = e^{i f theta_j} khat_j for pair j = 4G + u.
+template <int R>
+__device__ __forceinline__ void rotate_key(const uint4& r0, const uint4& r1, const float4& p0, const float4& p1,
+                                           float (&w)[8]) {
+  const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+  const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+  const float cs[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float c = cs[2 * u], s = cs[2 * u + 1];
+    if constexpr (R == 1) {
+      const h2 k = as_h2(w0[u]);  // fp16 operands read directly by v_fma_mix: no conversions
+      w[2 * u] = fmaf(static_cast<float>(k.x), c, -fmaf(static_cast<float>(k.y), s, 0.f));
+      w[2 * u + 1] = fmaf(static_cast<float>(k.y), c, fmaf(static_cast<float>(k.x), s, 0.f));
+    } else {
+      const float kr = mix_add_lo(w0[u], w1[u]), ki = mix_add_hi(w0[u], w1[u]);
+      w[2 * u] = fmaf(kr, c, -(ki * s));
+      w[2 * u + 1] = fmaf(ki, c, kr * s);
+    }
+  }
+}
+// Contraction of NB blocks' rotated keys of group G with their block queries: per pair j = 4G + u,
+// q''_re x w_re + q''_im x w_im, the query of pair j broadcast from block j mod 16 (the lanes holding pair
+// 16 (G / 4) + lane / 4). Consecutive MFMAs go to different blocks' accumulators.
+template <int G, int NB>
+__device__ __forceinline__ void contract_key(const float (&w)[NB][8], const float2 (&A)[NB], f4* acc) {
+  static_for<8>([&](auto dc) {
+    constexpr int d = decltype(dc)::value;
+    constexpr int abid = (4 * G + d / 2) & 15;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) acc[i] = mfma32_bcast<abid>((d & 1) ? A[i].y : A[i].x, w[i][d], acc[i]);
+  });
+}
+
+template <int G>
+__device__ __forceinline__ uint4 gather_row(const unsigned char* tab, const uint4& code) {
+  return *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + code_index(code, G) * 16);
+}
+
+// Value path, R = 2: each group's two residual rows are gathered whole and summed in fp16; an identity MFMA
+// transposes each 4-dim half within its lane quad (lane 4b + j receives dim j of the quad's 4 tokens, exactly,
+// in fp32), which converted back is the B operand of p^T x v for MFMA block b = the quad.
+template <int P>
+__device__ __forceinline__ void gather_pair2(const unsigned char* tab0, const unsigned char* tab1, const uint4& c0,
+                                             const uint4& c1, uint4 (&buf)[2][2]) {
+  buf[0][0] = gather_row<2 * P>(tab0, c0);
+  buf[0][1] = gather_row<2 * P>(tab1, c1);
+  buf[1][0] = gather_row<2 * P + 1>(tab0, c0);
+  buf[1][1] = gather_row<2 * P + 1>(tab1, c1);
+}
+template <int G>
+__device__ __forceinline__ void value_step_quad(const uint4& row, const h4& ident, const h4& pt,
+                                                f4 (&O)[2 * kGroups]) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  const f4 x0 = mfma(cat(as_h2(row.x), as_h2(row.y)), ident, z);
+  const f4 x1 = mfma(cat(as_h2(row.z), as_h2(row.w)), ident, z);
+  O[2 * G] = mfma(pt, to_h4(x0), O[2 * G]);
+  O[2 * G + 1] = mfma(pt, to_h4(x1), O[2 * G + 1]);
+}
+template <int P>
+__device__ __forceinline__ void value_pair2(const uint4 (&buf)[2][2], const h4& ident, const h4& pt,
+                                            f4 (&O)[2 * kGroups]) {
+  value_step_quad<2 * P>(add_rows(buf[0][0], buf[0][1]), ident, pt, O);
+  value_step_quad<2 * P + 1>(add_rows(buf[1][0], buf[1][1]), ident, pt, O);
+}
+
+// Value path, R = 1: each group's row is read as two transposing 8-byte reads. Within a 16-lane group, lane
+// a + 4k names the row of the token in lane 4a + k (its record was moved there by transpose_record), so lane
+// 4a + e receives dim e (and 4 + e) of tokens 4a .. 4a + 3: the B operand of p^T x v for the quad a.
+template <int Q>
+__device__ __forceinline__ void gather_quarter_tr(const unsigned char* tab, const uint4& code, uint4 (&buf)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const unsigned char* row = tab + (4 * Q + u) * kCodes * 16 + code_index(code, 4 * Q + u) * 16;
+    const h4 lo = lds_read_tr(row), hi = lds_read_tr(row + 8);
+    buf[u] = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                        __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+  }
+}
+template <int G>
+__device__ __forceinline__ void value_step(const uint4& tv, const h4& pt, f4 (&O)[2 * kGroups]) {
+  O[2 * G] = mfma(pt, cat(as_h2(tv.x), as_h2(tv.y)), O[2 * G]);
+  O[2 * G + 1] = mfma(pt, cat(as_h2(tv.z), as_h2(tv.w)), O[2 * G + 1]);
+}
+template <int Q>
+__device__ __forceinline__ void value_quarter(const uint4 (&buf)[4], const h4& pt, f4 (&O)[2 * kGroups]) {
+  value_step<4 * Q + 0>(buf[0], pt, O);
+  value_step<4 * Q + 1>(buf[1], pt, O);
+  value_step<4 * Q + 2>(buf[2], pt, O);
+  value_step<4 * Q + 3>(buf[3], pt, O);
+}
+// Record of the token in lane 16 (L / 16) + 4 (L mod 4) + (L / 4) mod 4 (a 4x4 transpose within each 16-lane
+// group), through the LDS crossbar (no LDS memory).
+__device__ __forceinline__ uint4 transpose_record(const uint4& r, int lane) {
+  const int src = ((lane & ~15) | ((lane & 3) << 2) | ((lane >> 2) & 3)) << 2;
+  return make_uint4(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.x)),
+                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.y)),
+                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.z)),
+                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.w)));
+}
+
+template <int R>
+__global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) {
+  constexpr int kW = kW16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTab16 + kPhaseBytes];
+  unsigned char* const slot0 = lds;
+  unsigned char* const slot1 = lds + kTab16;
+  const unsigned char* const phases = lds + 2 * kTab16;
+  // epilogue-only LDS (placed in the codebook slots, past the reduction buffer, once the passes are done)
+  auto& wave_ml = *reinterpret_cast<float(*)[2][kW][kGqa]>(lds + kW * kHeadDim * kGqa * sizeof(float));
+  int& is_last = *reinterpret_cast<int*>(lds + kW * kHeadDim * kGqa * sizeof(float) + sizeof(wave_ml));
+
+  // XCD-aware work order: the KV head is the fastest grid index. Workgroups are dealt to the 8 XCDs in
+  // turn, so with 8 KV heads each XCD serves one head and its L2 fetches only that head's codebooks.
+  const int kv = blockIdx.x % a.n_kv_heads, split = blockIdx.x / a.n_kv_heads, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t cb_stride = static_cast<int64_t>(kGroups) * R * kCodes * kGroupDim;
+  const f16* cb_k = static_cast<const f16*>(a.k_cb) + kv * cb_stride;
+  const f16* cb_v = static_cast<const f16*>(a.v_cb) + kv * cb_stride;
+  // sequence bounds (clamped), read before any memory operation so that they stay scalar loads
+  const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.max_len, a.total_tokens);
+  const int L = sb.len;
+  const int64_t seq_start = sb.start;
+
+  // ---------------------------------------------------------------------------------- prologue
+  // (1) Key codebooks (R = 1: and the value codebook) and the fp32 fine phases, straight into LDS. They depend
+  // only on the KV head, so they go out first.
+  load_table<f16, R, kW>(cb_k, 0, slot0, wave, lane);
+  if constexpr (R == 2) {
+    load_table<f16, R, kW>(cb_k, 1, slot1, wave, lane);
+  } else {
+    load_table<f16, R, kW>(cb_v, 0, slot1, wave, lane);
+  }
+  {
+    constexpr int kChunks = kPhaseBytes / 16;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine32gOffset);
+#pragma unroll
+    for (int i = 0; i < kChunks / kThreads16; ++i) {
+      const int c = (wave * (kChunks / kThreads16) + i) * 64;
+      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, const_cast<unsigned char*>(phases) + c * 16, 16, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int S = a.split_tokens;
+  const int t0 = split * S;
+  const int h0 = kv * kGqa;
+  const int64_t bh0 = static_cast<int64_t>(b) * a.n_q_heads + h0;
+  float* out_bh = a.out + bh0 * kHeadDim;
+  if (t0 >= L) {
+    if (split == 0)  // empty sequence: the output is zero
+      for (int i = tid; i < kGqa * kHeadDim; i += kThreads16) out_bh[i] = 0.f;
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // the direct-to-LDS loads land before the workgroup ends
+    return;
+  }
+  const int nvalid = min(S, L - t0);
+  const int nblocks = (nvalid + 63) >> 6;
+  const int my_blocks = (nblocks - wave + kW - 1) / kW;  // this wave owns blocks wave, wave + kW, ...
+  const int64_t row_base = seq_start + t0;
+  // token row of block i for this lane, clamped into the split so every load is in bounds
+  auto token_row = [&](int i) -> int64_t {
+    int tl = (wave + kW * i) * 64 + lane;
+    asm volatile("" : "+v"(tl));  // recomputed at every use rather than kept live
+    return row_base + min(tl, nvalid - 1);
+  };
+
+  // (2) The query pairs this lane supplies to the broadcast A operand: head qi = lane mod 4, pairs
+  // j = 16 k + quad (k = 0..3), and the coarse phases of those pairs for the wave's first block (row
+  // t0 / 64 + wave) and for row 1 (e^{i 64 theta}, from which the per-block steps follow).
+  const int quad = lane >> 2, qi = lane & 3;
+  const f16* qp = static_cast<const f16*>(a.q) + (bh0 + qi) * kHeadDim;
+  uint32_t qraw[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) qraw[k] = *reinterpret_cast<const uint32_t*>(qp + 2 * (16 * k + quad));
+  const float2* coarse = a.rope + kRopeCoarseOffset;
+  const int last_row = (L - 1) >> 6;  // rows past the sequence are never read (the table may end there)
+  const float2* crow0 = coarse + static_cast<int64_t>(min((t0 >> 6) + wave, last_row)) * kPairs;
+  const float2* crow1 = coarse + static_cast<int64_t>(min(1, last_row)) * kPairs;
+  float2 cph0[4], cph1[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    cph0[k] = crow0[16 * k + quad];
+    cph1[k] = crow1[16 * k + quad];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // (3) Key records of the first sweep (blocks 0, 1); later blocks' records are requested once the key pass has
+  // started, so that they do not share the HBM queue with the first ones. Records are clamped rows, so every load
+  // is in bounds.
+  uint4 code[kMaxBlocks], code1[kMaxBlocks];  // residual 0 and (R = 2) residual 1 of each block
+  auto request = [&](const uint8_t* base, int i) {
+    code[i] = load_code_record(base, a.total_tokens, kv, token_row(i), R, 0);
+    if constexpr (R == 2) code1[i] = load_code_record(base, a.total_tokens, kv, token_row(i), R, 1);
+  };
+#pragma unroll
+  for (int i = 0; i < kSweep; ++i) request(a.k_codes, i);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+  slot_barrier();  // every wave's codebook and phase loads have landed
+
+  // A operands. q'' = q * conj(e^{i 64 c theta}) for the block's coarse row c, in fp32: qc0 for the wave's
+  // first block; stepE = e^{i 512 theta} (row 1 squared three times: the wave's blocks are 8 rows apart)
+  // takes q'' from one block to the next.
+  float2 qc0[4], stepE[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    asm volatile("" : "+v"(qraw[k]));
+    const h2 hq = as_h2(qraw[k]);
+    qc0[k] = cmul_conj(make_float2(static_cast<float>(hq.x), static_cast<float>(hq.y)), cph0[k]);
+    float2 e = cph1[k];
+#pragma unroll
+    for (int sq = 0; sq < 3; ++sq) e = make_float2(e.x * e.x - e.y * e.y, 2.f * e.x * e.y);
+    stepE[k] = e;
+  }
+
+  // ------------------------------------------------------------------------------ key pass
+  f4 sc[kMaxBlocks];
+#pragma unroll
+  for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
+  const unsigned char* const ktab1 = R == 2 ? slot1 : slot0;
+  auto load_phases = [&](int g, float4 (&dst)[2]) {
+    dst[0] = *reinterpret_cast<const float4*>(phases + ((2 * g) * 64 + lane) * 16);
+    dst[1] = *reinterpret_cast<const float4*>(phases + ((2 * g + 1) * 64 + lane) * 16);
+  };
+  // One sweep: groups 0..15 over blocks kSweep s, kSweep s + 1. Per group the two rotations run as one VALU burst,
+  // then the next group's gathers and phases go out (the rows are consumed), then the 16 MFMAs as one burst over two
+  // accumulators, covering the gathers' latency. The wave's issue priority falls as it progresses, so the two waves
+  // that share a SIMD advance together.
+  auto sweep = [&](auto sc_) {
+    constexpr int s = decltype(sc_)::value;
+    uint4 rows[kSweep][2];
+    float4 ph[2];
+    float2 A[kSweep];
+    auto issue = [&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g < kGroups) {
+        load_phases(g, ph);
+#pragma unroll
+        for (int ii = 0; ii < kSweep; ++ii) {
+          rows[ii][0] = gather_row<g>(slot0, code[kSweep * s + ii]);
+          if constexpr (R == 2) rows[ii][1] = gather_row<g>(ktab1, code1[kSweep * s + ii]);
+        }
+      }
+    };
+    issue(std::integral_constant<int, 0>{});
+    static_for<kGroups>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      if constexpr (g % 4 == 0) {
+        __builtin_amdgcn_s_setprio(3 - (kGroups * s + g) * 4 / (kGroups * (kMaxBlocks / kSweep)));
+        // A operands of pairs 16 (g / 4) + quad for the sweep's blocks: q'' of block i is qc0 stepped i times
+        constexpr int k = g / 4;
+        float2 cur = qc0[k];
+#pragma unroll
+        for (int j = 0; j < kSweep * s; ++j) cur = cmul_conj(cur, stepE[k]);
+#pragma unroll
+        for (int j = 0; j < kSweep; ++j) {
+          A[j] = cur;
+          cur = cmul_conj(cur, stepE[k]);
+        }
+      }
+      float w[kSweep][8];
+#pragma unroll
+      for (int ii = 0; ii < kSweep; ++ii) rotate_key<R>(rows[ii][0], rows[ii][1], ph[0], ph[1], w[ii]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(std::integral_constant<int, g + 1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      contract_key<g, kSweep>(w, A, sc + kSweep * s);
+      __builtin_amdgcn_sched_barrier(0);  // the fp32 MFMAs stay one burst, apart from the next VALU burst
+    });
+  };
+  // One block alone (waves with fewer than 8 blocks): groups 0..15 with the phases read per group.
+  float2 curA[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) curA[k] = qc0[k];
+  auto single = [&](auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if (i < my_blocks) {
+      uint4 rows[2];
+      float4 ph[2];
+      auto issue = [&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        if constexpr (g < kGroups) {
+          load_phases(g, ph);
+          rows[0] = gather_row<g>(slot0, code[i]);
+          if constexpr (R == 2) rows[1] = gather_row<g>(ktab1, code1[i]);
+        }
+      };
+      issue(std::integral_constant<int, 0>{});
+      f4 acc[2] = {sc[i], (f4){0.f, 0.f, 0.f, 0.f}};  // groups alternate between two accumulators
+      static_for<kGroups>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        float w[1][8];
+        rotate_key<R>(rows[0], rows[1], ph[0], ph[1], w[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(std::integral_constant<int, g + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        const float2 A1[1] = {curA[g / 4]};
+        contract_key<g, 1>(w, A1, acc + (g & 1));
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      sc[i] = acc[0] + acc[1];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) curA[k] = cmul_conj(curA[k], stepE[k]);
+    }
+    // the block's key records are consumed: the value records of the first four blocks follow (the others are
+    // requested during the value pass, four blocks ahead)
+    if constexpr (i < kValueLead) request(a.v_codes, i);
+  };
+  if (my_blocks == kMaxBlocks) {
+    // each sweep first requests the next sweep's key records; the value records of the first four blocks follow
+    // their key records
+    static_for<kMaxBlocks / kSweep>([&](auto sc_) {
+      constexpr int s = decltype(sc_)::value;
+      if constexpr (kSweep * (s + 1) < kMaxBlocks) {
+#pragma unroll
+        for (int i = kSweep * (s + 1); i < kSweep * (s + 2); ++i) request(a.k_codes, i);
+      }
+      sweep(sc_);
+      if constexpr (kSweep * (s + 1) <= kValueLead) {
+#pragma unroll
+        for (int i = kSweep * s; i < kSweep * (s + 1); ++i) request(a.v_codes, i);
+      }
+    });
+  } else {
+#pragma unroll
+    for (int i = kSweep; i < kMaxBlocks; ++i) request(a.k_codes, i);
+    static_for<kMaxBlocks>(single);
+  }
+  __builtin_amdgcn_s_setprio(0);
+
+  // R = 2: once every wave is done with the key codebooks, both slots are refilled with the value codebooks
+  // (direct-to-LDS; no LDS read happens until they have landed).
+  if constexpr (R == 2) {
+    slot_barrier();
+    load_table<f16, R, kW>(cb_v, 0, slot0, wave, lane);
+    load_table<f16, R, kW>(cb_v, 1, slot1, wave, lane);
+  }
+
+  // ------------------------------------------------------------------------------ wave softmax
+  float m_w[kGqa], l_w[kGqa];
+  wave_softmax_regs<kW>(sc, my_blocks, wave, lane, nvalid, a.scale, m_w, l_w);
+  // p^T operands: lane 4b + j holds head j's weights for the 4 tokens of its quad (an exact transpose of the
+  // fp16 weights through an identity MFMA)
+  const h4 ident = identity_b(lane);
+  h4 pt[kMaxBlocks];
+  {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks; ++i) pt[i] = to_h4(mfma(to_h4(sc[i]), ident, z));
+  }
+  if constexpr (R == 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
+    lds_barrier();  // both value codebooks complete
+  }
+
+  // ------------------------------------------------------------------------------ value pass
+  f4 O[2 * kGroups];
+#pragma unroll
+  for (int c = 0; c < 2 * kGroups; ++c) O[c] = (f4){0.f, 0.f, 0.f, 0.f};
+  if constexpr (R == 2) {
+    // per group pair, the four rows of both residuals go out ahead of the previous pair's arithmetic
+    uint4 rows[kBufs][2][2];  // [buffer][group of the pair][residual]
+    constexpr int kPairsPerBlock = kGroups / 2;
+    auto issue = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < kPairsPerBlock * kMaxBlocks)
+        gather_pair2<m % kPairsPerBlock>(slot0, slot1, code[m / kPairsPerBlock], code1[m / kPairsPerBlock],
+                                         rows[m % kBufs]);
+    };
+    if (my_blocks > 0) static_for<kAhead>(issue);
+    static_for<kMaxBlocks>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_s_setprio(block_prio(i));
+      if constexpr (i + kValueLead < kMaxBlocks) request(a.v_codes, i + kValueLead);
+      if (i < my_blocks) {
+        static_for<kPairsPerBlock>([&](auto pc) {
+          constexpr int n = kPairsPerBlock * i + decltype(pc)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          issue(std::integral_constant<int, n + kAhead>{});
+          __builtin_amdgcn_sched_barrier(0);
+          value_pair2<n % kPairsPerBlock>(rows[n % kBufs], ident, pt[i], O);
+        });
+      }
+    });
+  } else {
+    uint4 rows[kBufs][4];  // gathered rows of quarters n .. n + kAhead
+    uint4 vrec[kMaxBlocks];  // value records moved to the transposed lanes
+    auto issue = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m < 4 * kMaxBlocks) {
+        if constexpr (m % 4 == 0) vrec[m / 4] = transpose_record(code[m / 4], lane_id());
+        gather_quarter_tr<m % 4>(slot1, vrec[m / 4], rows[m % kBufs]);
+      }
+    };
+    if (my_blocks > 0) static_for<kAhead>(issue);
+    static_for<kMaxBlocks>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      __builtin_amdgcn_s_setprio(block_prio(i));
+      if constexpr (i + kValueLead < kMaxBlocks) request(a.v_codes, i + kValueLead);
+      if (i < my_blocks) {
+        static_for<4>([&](auto qc) {
+          constexpr int n = 4 * i + decltype(qc)::value;
+          __builtin_amdgcn_sched_barrier(0);
+          issue(std::integral_constant<int, n + kAhead>{});
+          __builtin_amdgcn_sched_barrier(0);
+          value_quarter<n % 4>(rows[n % kBufs], pt[i], O);
+        });
+      }
+    });
+  }
+  __builtin_amdgcn_s_setprio(0);
+
+  // ------------------------------------------------------------------------ workgroup reduction
+  attn_epilogue<kW>(a, lds, wave_ml, is_last, lane_id(), wave * 64 + lane_id(), wave, O, b, kv, split, L, S, bh0,
+                    out_bh, m_w, l_w);
+}
+
+}  // namespace
+
+hipError_t launch_attn_f16(int R, int B, const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.n_splits * a.n_kv_heads, B);
+  if (R == 1) attn_f16_kernel<1><<<grid, kThreads16, 0, s>>>(a);
+  else attn_f16_kernel<2><<<grid, kThreads16, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace commvq

@@ -16,8 +16,9 @@ Layouts (shared by every consumer):
 with D = head_dim, G = n_groups, W = D / G, R = n_residuals, N = n_codes, T = total tokens.
 
 Distributions: codebook entries N(0, variance 0.25) drawn in float32 then rounded to the storage
-dtype (round to nearest even); q ~ N(0, 1) likewise; code indices uniform on [0, N). Draw order per
-seed: lengths (ragged only), k_cb, v_cb, q, k_codes, v_codes.
+dtype (round to nearest even); q ~ N(0, q_std^2) likewise (q_std = 1 unless a config widens the logit
+range); code indices uniform on [0, N). Draw order per seed: lengths (ragged only), k_cb, v_cb, q,
+k_codes, v_codes.
 """
 from __future__ import annotations
 
@@ -43,6 +44,7 @@ class Config:
     n_codes: int = 256
     rope_base: float = 500000.0
     ragged_range: Optional[tuple] = None  # (lo, hi) inclusive for ragged lengths
+    q_std: float = 1.0  # standard deviation of the query entries (wider logit ranges for larger values)
     description: str = ""
 
     @property
@@ -128,7 +130,7 @@ def make_inputs(cfg: Config, seed: Optional[int] = None) -> Dict[str, np.ndarray
     total = int(seq_len.sum())
     k_cb = (rng.standard_normal((Hkv, G, R, N, W), dtype=np.float32) * np.float32(0.5)).astype(dt)
     v_cb = (rng.standard_normal((Hkv, G, R, N, W), dtype=np.float32) * np.float32(0.5)).astype(dt)
-    q = rng.standard_normal((B, Hq, D), dtype=np.float32).astype(dt)
+    q = (rng.standard_normal((B, Hq, D), dtype=np.float32) * np.float32(cfg.q_std)).astype(dt)
     k_codes = rng.integers(0, N, size=(Hkv, R, total, G), dtype=np.uint8) if N == 256 else \
         rng.integers(0, N, size=(Hkv, R, total, G)).astype(np.uint8)
     v_codes = rng.integers(0, N, size=(Hkv, R, total, G), dtype=np.uint8) if N == 256 else \
