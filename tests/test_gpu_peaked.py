@@ -138,7 +138,27 @@ def test_peaked_byte_f32(vq, R, L, score_std, planted):
     assert err <= TOL["float32"]
 
 
-RAGGED = [("byte", 2, 6)]
+PACKED = [(R, L, s, pl) for R in (11, 21) for L in (8192, 131072) for s, pl in
+          ((3, False), (6, False), (12, False), (3, True), (12, True))]
+
+
+@pytest.mark.parametrize("R,L,score_std,planted", PACKED)
+def test_peaked_bit_packed(vq, R, L, score_std, planted):
+    kw = dict(n_residuals=R)
+    name = f"peak_g64_r{R}_{L}_s{score_std}{'_pl' if planted else ''}"
+    announce(f"{name}")
+    cfg = workloads.custom(name, 1, 32, 8, (L,), R, "float16", 500 + R + score_std + (50 if planted else 0),
+                           n_groups=2, n_codes=64, q_std=q_std_for(score_std, kw))
+    inp = workloads.make_inputs(cfg)
+    if planted:
+        inp = plant(cfg, inp, plant_positions(L))
+    got, ref = run_case(vq, cfg, inp)
+    err = rowwise_rel_err(got, ref)
+    print(f"{name}: max row-relative error {err:.3e} (tol {TOL['float16']})", flush=True)
+    assert err <= TOL["float16"]
+
+
+RAGGED = [("byte", 2, 6), ("bit_packed", 11, 6)]
 
 
 @pytest.mark.parametrize("layout,R,score_std", RAGGED)

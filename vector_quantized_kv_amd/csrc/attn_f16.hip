@@ -56,19 +56,6 @@ constexpr int kSweep = 2;                            // blocks per key sweep
 constexpr int kValueLead = 4;                        // value records requested this many blocks ahead
 static_assert(2 * kTab16 + kPhaseBytes <= 160 * 1024, "codebook slots and phases fit the CU's LDS");
 
-// fp32 value of (fp16 lo/hi half of a) + (fp16 lo/hi half of b), rounded once (v_fma_mix with a unit
-// multiplier reads both halves as fp16 and adds in fp32).
-__device__ __forceinline__ float mix_add_lo(uint32_t a, uint32_t b) {
-  float d;
-  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a), "v"(b));
-  return d;
-}
-__device__ __forceinline__ float mix_add_hi(uint32_t a, uint32_t b) {
-  float d;
-  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a), "v"(b));
-  return d;
-}
-
 // fp32 4x4x1 MFMA with the A operand broadcast from block ABID: acc[m] += A[lane 4 ABID + m] * b.
 template <int ABID>
 __device__ __forceinline__ f4 mfma32_bcast(float a, float b, f4 c) {
@@ -78,36 +65,60 @@ __device__ __forceinline__ f4 mfma32_bcast(float a, float b, f4 c) {
 // Rotated key of one group: the lane's gathered row(s) (4 pairs (a, b) in fp16), summed over residuals in fp32,
 // times the lane's fine phases (p0 = pairs 4G, 4G+1, p1 = 4G+2, 4G+3, each (cos, sin)) in fp32:
 // w[2u] + i w[2u+1] = e^{i f theta_j} khat_j for pair j = 4G + u.
-template <int R>
-__device__ __forceinline__ void rotate_key(const uint4& r0, const uint4& r1, const float4& p0, const float4& p1,
-                                           float (&w)[8]) {
-  const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-  const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+// R = 1 reads the fp16 codeword directly (v_fma_mix). R = 2 takes the residual sum from sum_rows (ksum: the
+// fp32 entries (a, b, a, b) of pairs 4G, 4G+1 and of 4G+2, 4G+3).
+__device__ __forceinline__ void rotate_f32(const f4 (&ksum)[2], const float4& p0, const float4& p1, float (&w)[8]) {
   const float cs[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const float c = cs[2 * u], s = cs[2 * u + 1];
-    if constexpr (R == 1) {
-      const h2 k = as_h2(w0[u]);  // fp16 operands read directly by v_fma_mix: no conversions
-      w[2 * u] = fmaf(static_cast<float>(k.x), c, -fmaf(static_cast<float>(k.y), s, 0.f));
-      w[2 * u + 1] = fmaf(static_cast<float>(k.y), c, fmaf(static_cast<float>(k.x), s, 0.f));
-    } else {
-      const float kr = mix_add_lo(w0[u], w1[u]), ki = mix_add_hi(w0[u], w1[u]);
-      w[2 * u] = fmaf(kr, c, -(ki * s));
-      w[2 * u + 1] = fmaf(ki, c, kr * s);
-    }
+    const float kr = ksum[u >> 1][2 * (u & 1)], ki = ksum[u >> 1][2 * (u & 1) + 1];
+    w[2 * u] = fmaf(kr, c, -(ki * s));
+    w[2 * u + 1] = fmaf(ki, c, kr * s);
+  }
+}
+__device__ __forceinline__ void rotate_f16(const uint4& r0, const float4& p0, const float4& p1, float (&w)[8]) {
+  const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+  const float cs[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float c = cs[2 * u], s = cs[2 * u + 1];
+    const h2 k = as_h2(w0[u]);  // fp16 operands read directly by v_fma_mix: no conversions
+    w[2 * u] = fmaf(static_cast<float>(k.x), c, -fmaf(static_cast<float>(k.y), s, 0.f));
+    w[2 * u + 1] = fmaf(static_cast<float>(k.y), c, fmaf(static_cast<float>(k.x), s, 0.f));
+  }
+}
+// Exact fp32 sum of two fp16 rows (R = 2) on the matrix core: with the identity as A, the 4x4x4 MFMA returns in
+// each lane its own 4 B values; accumulating the second residual's row adds it in fp32 (one rounding). fp16
+// MFMAs run beside the VALU rotations.
+__device__ __forceinline__ void sum_rows(const uint4& r0, const uint4& r1, const h4& ident, f4 (&ksum)[2]) {
+  const f4 z = {0.f, 0.f, 0.f, 0.f};
+  ksum[0] = mfma(ident, cat(as_h2(r1.x), as_h2(r1.y)), mfma(ident, cat(as_h2(r0.x), as_h2(r0.y)), z));
+  ksum[1] = mfma(ident, cat(as_h2(r1.z), as_h2(r1.w)), mfma(ident, cat(as_h2(r0.z), as_h2(r0.w)), z));
+}
+template <int R>
+__device__ __forceinline__ void rotate_key(const uint4& r0, const uint4& r1, const float4& p0, const float4& p1,
+                                           const h4& ident, float (&w)[8]) {
+  if constexpr (R == 1) {
+    rotate_f16(r0, p0, p1, w);
+  } else {
+    f4 ksum[2];
+    sum_rows(r0, r1, ident, ksum);
+    rotate_f32(ksum, p0, p1, w);
   }
 }
 // Contraction of NB blocks' rotated keys of group G with their block queries: per pair j = 4G + u,
 // q''_re x w_re + q''_im x w_im, the query of pair j broadcast from block j mod 16 (the lanes holding pair
-// 16 (G / 4) + lane / 4). Consecutive MFMAs go to different blocks' accumulators.
+// 16 (G / 4) + lane / 4). Each block accumulates into two chains (acc[2 i] for the real parts, acc[2 i + 1] for
+// the imaginary ones), so consecutive MFMAs never depend on each other.
 template <int G, int NB>
-__device__ __forceinline__ void contract_key(const float (&w)[NB][8], const float2 (&A)[NB], f4* acc) {
+__device__ __forceinline__ void contract_key(const float (&w)[NB][8], const float2 (&A)[NB], f4 (&acc)[2 * NB]) {
   static_for<8>([&](auto dc) {
     constexpr int d = decltype(dc)::value;
     constexpr int abid = (4 * G + d / 2) & 15;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) acc[i] = mfma32_bcast<abid>((d & 1) ? A[i].y : A[i].x, w[i][d], acc[i]);
+    for (int i = 0; i < NB; ++i)
+      acc[2 * i + (d & 1)] = mfma32_bcast<abid>((d & 1) ? A[i].y : A[i].x, w[i][d], acc[2 * i + (d & 1)]);
   });
 }
 
@@ -294,6 +305,7 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   }
 
   // ------------------------------------------------------------------------------ key pass
+  const h4 ident = identity_b(lane);  // identity MFMA operand (residual sums, transposes)
   f4 sc[kMaxBlocks];
 #pragma unroll
   for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -322,6 +334,9 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
         }
       }
     };
+    f4 acc[2 * kSweep];  // two chains per block, folded into sc at the end of the sweep
+#pragma unroll
+    for (int c = 0; c < 2 * kSweep; ++c) acc[c] = (f4){0.f, 0.f, 0.f, 0.f};
     issue(std::integral_constant<int, 0>{});
     static_for<kGroups>([&](auto gc) {
       constexpr int g = decltype(gc)::value;
@@ -339,14 +354,31 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
         }
       }
       float w[kSweep][8];
+      if constexpr (R == 1) {
 #pragma unroll
-      for (int ii = 0; ii < kSweep; ++ii) rotate_key<R>(rows[ii][0], rows[ii][1], ph[0], ph[1], w[ii]);
+        for (int ii = 0; ii < kSweep; ++ii) rotate_f16(rows[ii][0], ph[0], ph[1], w[ii]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(std::integral_constant<int, g + 1>{});  // the rows are consumed
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // the blocks' residual sums on the matrix core read the rows; the next group's gathers then go out ahead
+        // of the rotations
+        f4 ksum[kSweep][2];
+        const float4 p0 = ph[0], p1 = ph[1];
+#pragma unroll
+        for (int ii = 0; ii < kSweep; ++ii) sum_rows(rows[ii][0], rows[ii][1], ident, ksum[ii]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(std::integral_constant<int, g + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ii = 0; ii < kSweep; ++ii) rotate_f32(ksum[ii], p0, p1, w[ii]);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      issue(std::integral_constant<int, g + 1>{});
-      __builtin_amdgcn_sched_barrier(0);
-      contract_key<g, kSweep>(w, A, sc + kSweep * s);
+      contract_key<g, kSweep>(w, A, acc);
       __builtin_amdgcn_sched_barrier(0);  // the fp32 MFMAs stay one burst, apart from the next VALU burst
     });
+#pragma unroll
+    for (int ii = 0; ii < kSweep; ++ii) sc[kSweep * s + ii] = acc[2 * ii] + acc[2 * ii + 1];
   };
   // One block alone (waves with fewer than 8 blocks): groups 0..15 with the phases read per group.
   float2 curA[4];
@@ -366,19 +398,19 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
         }
       };
       issue(std::integral_constant<int, 0>{});
-      f4 acc[2] = {sc[i], (f4){0.f, 0.f, 0.f, 0.f}};  // groups alternate between two accumulators
+      f4 acc[2] = {(f4){0.f, 0.f, 0.f, 0.f}, (f4){0.f, 0.f, 0.f, 0.f}};  // real and imaginary chains
       static_for<kGroups>([&](auto gc) {
         constexpr int g = decltype(gc)::value;
         float w[1][8];
-        rotate_key<R>(rows[0], rows[1], ph[0], ph[1], w[0]);
+        rotate_key<R>(rows[0], rows[1], ph[0], ph[1], ident, w[0]);
         __builtin_amdgcn_sched_barrier(0);
         issue(std::integral_constant<int, g + 1>{});
         __builtin_amdgcn_sched_barrier(0);
         const float2 A1[1] = {curA[g / 4]};
-        contract_key<g, 1>(w, A1, acc + (g & 1));
+        contract_key<g, 1>(w, A1, acc);
         __builtin_amdgcn_sched_barrier(0);
       });
-      sc[i] = acc[0] + acc[1];
+      sc[i] = acc[0] + acc[1];  // (a single block: the two chains)
 #pragma unroll
       for (int k = 0; k < 4; ++k) curA[k] = cmul_conj(curA[k], stepE[k]);
     }
@@ -421,7 +453,6 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   wave_softmax_regs<kW>(sc, my_blocks, wave, lane, nvalid, a.scale, m_w, l_w);
   // p^T operands: lane 4b + j holds head j's weights for the 4 tokens of its quad (an exact transpose of the
   // fp16 weights through an identity MFMA)
-  const h4 ident = identity_b(lane);
   h4 pt[kMaxBlocks];
   {
     const f4 z = {0.f, 0.f, 0.f, 0.f};

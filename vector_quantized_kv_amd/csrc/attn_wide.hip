@@ -21,9 +21,14 @@
 // are shared. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual rows,
 // sums them in fp32 on the matrix core (an MFMA with the identity as A adds a lane's four fp16 values to
 // its fp32 accumulator), and then
-//   keys:   rounds the sum to fp16, rotates it by the fine phase and runs the two key MFMA steps;
+//   keys:   rotates the fp32 sum by the lane's fine phases in fp32 (phases read from a 32 KiB LDS table) and
+//           contracts it with the fp32 block query on the fp32 matrix core (v_mfma_f32_4x4x1_16b_f32, query
+//           broadcast from one 4-lane block per dim): no fp16 rounding on the key side, so wide logit ranges
+//           keep the attention within tolerance;
 //   values: sums with the identity as B instead, which transposes each 4x4 (token x dim) quad tile as it
-//           accumulates, then multiplies by p^T.
+//           accumulates, rounds once to fp16 and multiplies by p^T.
+// Residuals past R in the last pass of each kind use a zero matrix in place of the identity (their gathers
+// read a real row and add nothing).
 // Rows are stored with their 16-byte chunks permuted by the codeword (physical chunk = cc xor
 // ((l >> 1) & 7)), so the 16 lanes that share an LDS cycle land on random ones of the 16 bank groups
 // instead of the two that a 128-byte row stride would give them.
@@ -43,11 +48,12 @@ constexpr int kChunks = kWRow / 16;              // 16-byte chunks per row (8)
 constexpr int kUnits = kWG * kChunks;            // units (g, cc) per block (16)
 constexpr int kW = 8;                            // waves per workgroup
 constexpr int kThreads = kW * 64;
-constexpr int kZeroRow = 2 * kSlot;              // LDS offset of a 128-byte zero row
+constexpr int kPhase = 2 * kSlot;                // LDS offset of the fp32 fine phases [G][h][lane][2 pairs]
+constexpr int kPhaseBytes = kGroups * 2 * 64 * 16;
 constexpr int kWAhead = 1;                       // units whose gathers are in flight ahead of the current one
 constexpr int kWBufs = kWAhead + 1;
 static_assert(kSlot / 16 == kMaxBlocks * kThreads, "one staged 16-byte unit per thread per block");
-static_assert(kZeroRow >= (kIdx - 1) * kWTab, "zero-row stand-in offsets stay non-negative");
+static_assert(kPhase + kPhaseBytes <= 160 * 1024, "codebook slots and phases fit the CU's LDS");
 
 // Global source of 16-byte unit u of the slot holding residuals r0 .. r0 + kRes - 1 (unit u = table
 // f = 2 rho + g, codeword l, physical chunk pc). Residuals past R read residual R - 1 (never used).
@@ -60,51 +66,69 @@ __device__ __forceinline__ const unsigned char* slot_unit_src(const f16* cb_kv, 
          cc * 16;
 }
 
-// Sum of a unit's kRes residual chunks, in fp32 on the matrix core: with A = identity, lane 4b + j of
-// D receives its own B values plus C, so k0 (dims 0..3 of the chunk) and k1 (dims 4..7) accumulate the
-// lane's row chunks. The fp16 result feeds the key MFMA step of byte-layout group G.
+// fp32 4x4x1 MFMA with the A operand broadcast from block ABID: acc[m] += A[lane 4 ABID + m] * b.
+template <int ABID>
+__device__ __forceinline__ f4 mfma32_bcast(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 4, ABID, 0);
+}
+
+// Key unit of byte-layout group G (RoPE pairs 4G .. 4G+3): the sum of the unit's kRes residual chunks, in fp32 on
+// the matrix core (with A = identity, lane 4b + j of D receives its own B values plus C; idr[rho] is the zero
+// matrix for residuals past R), rotated by the lane's fine phases (p0: pairs 4G, 4G+1; p1: 4G+2, 4G+3, each
+// (cos, sin)) in fp32, then contracted with the block query q'' (pair j = 4G + u broadcast from block j mod 16):
+// q''_re x w_re into acc[0], q''_im x w_im into acc[1].
 template <int G>
-__device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[kRes], const h4& ident, const uint4 (&F)[kGroups],
-                                              const h4& A0, const h4& A1, f4& acc) {
+__device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[kRes], const h4 (&idr)[kRes], const float4& p0,
+                                              const float4& p1, const float2& A, f4 (&acc)[2]) {
   const f4 z = {0.f, 0.f, 0.f, 0.f};
-  f4 k0 = mfma(ident, cat(as_h2(rows[0].x), as_h2(rows[0].y)), z);
-  f4 k1 = mfma(ident, cat(as_h2(rows[0].z), as_h2(rows[0].w)), z);
+  f4 k0 = mfma(idr[0], cat(as_h2(rows[0].x), as_h2(rows[0].y)), z);
+  f4 k1 = mfma(idr[0], cat(as_h2(rows[0].z), as_h2(rows[0].w)), z);
 #pragma unroll
   for (int rho = 1; rho < kRes; ++rho) {
-    k0 = mfma(ident, cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), k0);
-    k1 = mfma(ident, cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), k1);
+    k0 = mfma(idr[rho], cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), k0);
+    k1 = mfma(idr[rho], cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), k1);
   }
-  // one v_cvt_pk_f16_f32 (round to nearest even) per pair
-  auto pk = [](float x, float y) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){x, y}, h2));
-  };
-  key_step<G>(make_uint4(pk(k0[0], k0[1]), pk(k0[2], k0[3]), pk(k1[0], k1[1]), pk(k1[2], k1[3])), F, A0, A1, acc);
+  const float cs[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+  float w[8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float c = cs[2 * u], s = cs[2 * u + 1];
+    const float kr = (u < 2 ? k0 : k1)[2 * (u & 1)], ki = (u < 2 ? k0 : k1)[2 * (u & 1) + 1];
+    w[2 * u] = fmaf(kr, c, -(ki * s));
+    w[2 * u + 1] = fmaf(ki, c, kr * s);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the fp32 MFMAs run as one burst (they do not overlap VALU work)
+  static_for<8>([&](auto dc) {
+    constexpr int d = decltype(dc)::value;
+    constexpr int abid = (4 * G + d / 2) & 15;
+    acc[d & 1] = mfma32_bcast<abid>((d & 1) ? A.y : A.x, w[d], acc[d & 1]);
+  });
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Value unit: with B = identity, lane 4b + j of D receives value j of each lane of its quad (dim j of the
 // quad's 4 tokens), so the residual sum accumulates already transposed; rounded to fp16 it is the B
 // operand of p^T x v for byte-layout group G.
 template <int G>
-__device__ __forceinline__ void wide_value_unit(const uint4 (&rows)[kRes], const h4& ident, const h4& pt,
+__device__ __forceinline__ void wide_value_unit(const uint4 (&rows)[kRes], const h4 (&idr)[kRes], const h4& pt,
                                                 f4 (&O)[2 * kGroups]) {
   const f4 z = {0.f, 0.f, 0.f, 0.f};
-  f4 x0 = mfma(cat(as_h2(rows[0].x), as_h2(rows[0].y)), ident, z);
-  f4 x1 = mfma(cat(as_h2(rows[0].z), as_h2(rows[0].w)), ident, z);
+  f4 x0 = mfma(cat(as_h2(rows[0].x), as_h2(rows[0].y)), idr[0], z);
+  f4 x1 = mfma(cat(as_h2(rows[0].z), as_h2(rows[0].w)), idr[0], z);
 #pragma unroll
   for (int rho = 1; rho < kRes; ++rho) {
-    x0 = mfma(cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), ident, x0);
-    x1 = mfma(cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), ident, x1);
+    x0 = mfma(cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), idr[rho], x0);
+    x1 = mfma(cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), idr[rho], x1);
   }
   O[2 * G] = mfma(pt, to_h4(x0), O[2 * G]);
   O[2 * G + 1] = mfma(pt, to_h4(x1), O[2 * G + 1]);
 }
 
 __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kSlot + kWRow];
-  __shared__ __attribute__((aligned(16))) uint4 fine_lds[kGroups * kFineRows];  // packed fp16 fine phases
-  __shared__ float wave_ml[2][kW][kGqa];
-  __shared__ int is_last;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kSlot + kPhaseBytes];
+  // epilogue-only LDS (placed in the codebook slots, past the reduction buffer, once the passes are done)
+  auto& wave_ml = *reinterpret_cast<float(*)[2][kW][kGqa]>(lds + kW * kHeadDim * kGqa * sizeof(float));
+  int& is_last = *reinterpret_cast<int*>(lds + kW * kHeadDim * kGqa * sizeof(float) + sizeof(wave_ml));
 
   const int kv = blockIdx.x % a.n_kv_heads, split = blockIdx.x / a.n_kv_heads, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -120,18 +144,15 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   const int64_t seq_start = sb.start;
 
   // ---------------------------------------------------------------------------------- prologue
-  // (0) the zero row that stands in for the rows of residuals past R in the last pass of each kind (an
-  // ordinary store, written before any direct-to-LDS load is in flight).
-  if (tid < kWRow / 16) reinterpret_cast<uint4*>(lds + kZeroRow)[tid] = make_uint4(0u, 0u, 0u, 0u);
-  // (1) fine phases and the codebook chunk of pass 0 (key residuals 0 .. kRes-1), straight into LDS.
+  // (1) fp32 fine phases (group-major, the byte layout's groups) and the codebook chunk of pass 0 (key
+  // residuals 0 .. kRes-1), straight into LDS.
   {
-    constexpr int kFineChunks = kGroups * kFineRows;
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine16Offset);
+    constexpr int kFineChunks = kPhaseBytes / 16;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine32gOffset);
 #pragma unroll
     for (int i = 0; i < kFineChunks / kThreads; ++i) {
       const int c = (wave * (kFineChunks / kThreads) + i) * 64;
-      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, reinterpret_cast<unsigned char*>(fine_lds) + c * 16, 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, lds + kPhase + c * 16, 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kMaxBlocks; ++i) {
@@ -162,22 +183,22 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     return row_base + min(tl, nvalid - 1);
   };
 
-  // (2) query pairs and coarse phases (rows of the wave's first block and of e^{i 64 theta})
+  // (2) the query pairs this lane supplies to the broadcast A operand (head lane mod 4, pairs 16 k + lane / 4)
+  // and their coarse phases for the wave's first block and for row 1 (e^{i 64 theta})
   const int quad = lane >> 2, qi = lane & 3;
   const f16* qp = static_cast<const f16*>(a.q) + (bh0 + qi) * kHeadDim;
   uint32_t qraw[4];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) qraw[2 * m + e] = *reinterpret_cast<const uint32_t*>(qp + 2 * (32 * m + 2 * quad + e));
+  for (int k = 0; k < 4; ++k) qraw[k] = *reinterpret_cast<const uint32_t*>(qp + 2 * (16 * k + quad));
   const float2* coarse = a.rope + kRopeCoarseOffset;
-  float4 cphase[2][2];
+  const int last_row = (L - 1) >> 6;
+  const float2* crow0 = coarse + static_cast<int64_t>(min((t0 >> 6) + wave, last_row)) * kPairs;
+  const float2* crow1 = coarse + static_cast<int64_t>(min(1, last_row)) * kPairs;
+  float2 cph0[4], cph1[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = i == 0 ? min((t0 >> 6) + wave, (L - 1) >> 6) : min(1, (L - 1) >> 6);
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-      cphase[i][m] = *reinterpret_cast<const float4*>(coarse + static_cast<int64_t>(row) * kPairs + 32 * m + 2 * quad);
+  for (int k = 0; k < 4; ++k) {
+    cph0[k] = crow0[16 * k + quad];
+    cph1[k] = crow1[16 * k + quad];
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -201,39 +222,23 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
 
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kPrologueRecords));
-  slot_barrier();  // (its lgkmcnt(0) also retires the zero-row store before the barrier)
-  uint4 F[kGroups];
-#pragma unroll
-  for (int g = 0; g < kGroups; ++g) F[g] = fine_lds[g * kFineRows + lane];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) asm volatile("" : "+v"(qraw[k]));
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-      asm volatile("" : "+v"(cphase[i][m].x), "+v"(cphase[i][m].y), "+v"(cphase[i][m].z), "+v"(cphase[i][m].w));
+  slot_barrier();
 
-  // A operands: q'' = q * conj(coarse phase of the block); the wave's blocks are kW rows apart, so
+  // A operands: q'' = q * conj(coarse phase of the block), fp32; the wave's blocks are kW rows apart, so
   // q''_{i+1} = q''_i * conj(E) with E = e^{i 64 kW theta} (row 1 squared log2(kW) times).
   float2 qc0[4], stepE[4];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const h2 q0 = as_h2(qraw[2 * m]), q1 = as_h2(qraw[2 * m + 1]);
-    const float4 c0 = cphase[0][m], c1 = cphase[1][m];
-    qc0[2 * m] = cmul_conj(make_float2(static_cast<float>(q0.x), static_cast<float>(q0.y)), make_float2(c0.x, c0.y));
-    qc0[2 * m + 1] =
-        cmul_conj(make_float2(static_cast<float>(q1.x), static_cast<float>(q1.y)), make_float2(c0.z, c0.w));
-    stepE[2 * m] = make_float2(c1.x, c1.y);
-    stepE[2 * m + 1] = make_float2(c1.z, c1.w);
+  for (int k = 0; k < 4; ++k) {
+    asm volatile("" : "+v"(qraw[k]));
+    const h2 hq = as_h2(qraw[k]);
+    qc0[k] = cmul_conj(make_float2(static_cast<float>(hq.x), static_cast<float>(hq.y)), cph0[k]);
+    float2 e = cph1[k];
+#pragma unroll
+    for (int sq = 1; sq < kW; sq *= 2) e = make_float2(e.x * e.x - e.y * e.y, 2.f * e.x * e.y);
+    stepE[k] = e;
   }
-#pragma unroll
-  for (int sq = 1; sq < kW; sq *= 2)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float2 e = stepE[k];
-      stepE[k] = make_float2(e.x * e.x - e.y * e.y, 2.f * e.x * e.y);
-    }
   const h4 ident = identity_b(lane);
+  const h4 zero4 = {(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
 
   // ------------------------------------------------------------------------- pass machinery
   // Staging: during pass p, each thread fetches one 16-byte unit per block of pass p + 1's codebook chunk
@@ -250,14 +255,13 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     *reinterpret_cast<uint4*>(lds + (pn & 1) * kSlot + (i * kThreads + tid) * 16) = stage;
   };
   // LDS offsets (without the table offset f * kWTab) of the rows of a block's kIdx indices in pass p.
-  auto addresses = [&](int c, int slot_off, int nres, const uint2 w, uint32_t (&adr)[kIdx]) {
+  auto addresses = [&](int c, int slot_off, const uint2 w, uint32_t (&adr)[kIdx]) {
     uint32_t x0, x1;
     packed_window(w.x, w.y, packed_window_shift(c), x0, x1);
     static_for<kIdx>([&](auto fc) {
       constexpr int f = decltype(fc)::value;
       const uint32_t idx = packed_index<f>(x0, x1);
-      const uint32_t real = slot_off + idx * kWRow + ((idx >> 1) & 7) * 16;
-      adr[f] = (f >> 1) < nres ? real : static_cast<uint32_t>(kZeroRow - f * kWTab);
+      adr[f] = slot_off + idx * kWRow + ((idx >> 1) & 7) * 16;  // (residuals past R: a real row, added with 0)
     });
   };
 
@@ -276,6 +280,9 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     const int p = kKey ? c : nch + c;
     const int slot_off = (p & 1) * kSlot;
     const int nres = min(kRes, R - kRes * c);
+    h4 idr[kRes];  // the identity for the pass's residuals, the zero matrix past R
+#pragma unroll
+    for (int rho = 0; rho < kRes; ++rho) idr[rho] = rho < nres ? ident : zero4;
     uint32_t adr[2][kIdx];
     uint4 rows[kWBufs][kRes];
     float2 cur[4];
@@ -284,7 +291,7 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     auto block_addresses = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i < kMaxBlocks) {
-        addresses(c, slot_off, nres, code[i], adr[i & 1]);
+        addresses(c, slot_off, code[i], adr[i & 1]);
         request_words(p + 1, i);
       }
     };
@@ -308,23 +315,20 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
       stage_load(p + 1, i);
       if (i < my_blocks) {
         if constexpr (kKey) {
-          const h4 A0 = {(f16)cur[0].x, (f16)cur[0].y, (f16)cur[1].x, (f16)cur[1].y};
-          const h4 A1 = {(f16)cur[2].x, (f16)cur[2].y, (f16)cur[3].x, (f16)cur[3].y};
-          f4 odd = {0.f, 0.f, 0.f, 0.f};
+          f4 acc[2] = {sc[i], (f4){0.f, 0.f, 0.f, 0.f}};  // real-part and imaginary-part chains
+          float4 ph[2];
           auto unit = [&](auto uc) {
             constexpr int u = decltype(uc)::value, n = kUnits * i + u;
             constexpr int G = (u / kChunks) * 8 + u % kChunks;  // byte-layout group of (g, cc)
+            ph[0] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G) * 64 + lane) * 16);
+            ph[1] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G + 1) * 64 + lane) * 16);
             __builtin_amdgcn_sched_barrier(0);
             issue(std::integral_constant<int, n + kWAhead>{});
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (u % 2 == 0) {
-              wide_key_unit<G>(rows[n % kWBufs], ident, F, A0, A1, sc[i]);
-            } else {
-              wide_key_unit<G>(rows[n % kWBufs], ident, F, A0, A1, odd);
-            }
+            wide_key_unit<G>(rows[n % kWBufs], idr, ph[0], ph[1], cur[G / 4], acc);
           };
           static_for<kUnits>(unit);
-          sc[i] += odd;
+          sc[i] = acc[0] + acc[1];
 #pragma unroll
           for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
         } else {
@@ -334,7 +338,7 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             issue(std::integral_constant<int, n + kWAhead>{});
             __builtin_amdgcn_sched_barrier(0);
-            wide_value_unit<G>(rows[n % kWBufs], ident, pth[i], O);
+            wide_value_unit<G>(rows[n % kWBufs], idr, pth[i], O);
           };
           static_for<kUnits>(unit);
         }
@@ -348,7 +352,8 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
 
   for (int c = 0; c < nch; ++c) pass(std::integral_constant<int, 0>{}, c);
 
-  wave_softmax<kW>(sc, my_blocks, wave, lane, nvalid, a.scale, wave_ml);
+  float m_w[kGqa], l_w[kGqa];
+  wave_softmax_regs<kW>(sc, my_blocks, wave, lane, nvalid, a.scale, m_w, l_w);
   {
     const f4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -360,7 +365,7 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   for (int c = 0; c < nch; ++c) pass(std::integral_constant<int, 1>{}, c);
 
   attn_epilogue<kW>(a, lds, wave_ml, is_last, lane_id(), wave * 64 + lane_id(), wave, O, b, kv, split, L, S, bh0,
-                    out_bh);
+                    out_bh, m_w, l_w);
 }
 
 }  // namespace
