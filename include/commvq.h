@@ -41,7 +41,8 @@
  *
  * Conventions for every call:
  *   - Pointers are device pointers unless marked (host). Buffers are owned by the caller; the library
- *     keeps no state, allocates nothing, frees nothing and never synchronizes.
+ *     allocates nothing, frees nothing and never synchronizes. Its only state is the static per-GPU scratch
+ *     of commvq_attn_decode_noalloc.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default stream) and runs
  *     asynchronously. Device faults surface at the caller's next synchronization.
  *   - All argument checks run on the host before any launch; a failing call launches nothing and has
@@ -142,6 +143,25 @@ int commvq_attn_decode(const commvq_dims* d /* host */, const void* q, const uin
                        const int32_t* seq_len, int32_t max_len /* host */, int64_t total_tokens /* host */,
                        const void* rope_table, int32_t rope_positions /* host */, void* workspace,
                        size_t ws_bytes /* host */, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * commvq_attn_decode without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments, checks,
+ * kernels and result as commvq_attn_decode; the split partials and arrival counters live instead in a static
+ * device array of the library, 8 MiB per GPU, which each GPU the library runs on holds from the first call
+ * on that device until the process ends (that first call also clears its 64 KiB counter head with a small
+ * fill kernel on `stream`). The call allocates nothing and frees nothing.
+ * Limits: batch x n_kv_heads <= 16384 (COMMVQ_EUNSUPPORTED beyond) and the call's partials (per (b, q head,
+ * split) 8 + 512 bytes, the commvq_attn_decode_workspace_size layout) within 8 MiB - 64 KiB
+ * (COMMVQ_EWORKSPACE beyond, with the bytes needed in the detail string).
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU race (serialize them,
+ * e.g. on one stream). Every completed call leaves the counters zero for the next.
+ * ------------------------------------------------------------------------------------------- */
+int commvq_attn_decode_noalloc(const commvq_dims* d /* host */, const void* q, const uint8_t* k_codes,
+                               const uint8_t* v_codes, const void* k_codebook, const void* v_codebook,
+                               const int64_t* seq_start, const int32_t* seq_len, int32_t max_len /* host */,
+                               int64_t total_tokens /* host */, const void* rope_table,
+                               int32_t rope_positions /* host */, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Value reduce with given weights, in the reordered form of the pages (pith.science verdict,

@@ -21,7 +21,7 @@ EXPORTED_SYMBOLS = (
     "commvq_status_string", "commvq_last_error_detail", "commvq_rope_table_size", "commvq_rope_table",
     "commvq_qcodebook_table", "commvq_attn_decode_workspace_size", "commvq_attn_decode",
     "commvq_value_reduce_workspace_size", "commvq_value_reduce", "commvq_encode_greedy", "commvq_codebook_update",
-    "commvq_debug_unpack",
+    "commvq_debug_unpack", "commvq_attn_decode_noalloc",
 )
 
 
@@ -74,6 +74,8 @@ def lib():
         L.commvq_attn_decode_workspace_size.argtypes, L.commvq_attn_decode_workspace_size.restype = [D, i32], sz
         L.commvq_attn_decode.argtypes = [D, P, P, P, P, P, P, P, i32, i64, P, i32, P, sz, P, P]
         L.commvq_attn_decode.restype = ctypes.c_int
+        L.commvq_attn_decode_noalloc.argtypes = [D, P, P, P, P, P, P, P, i32, i64, P, i32, P, P]
+        L.commvq_attn_decode_noalloc.restype = ctypes.c_int
         L.commvq_value_reduce_workspace_size.argtypes, L.commvq_value_reduce_workspace_size.restype = [D, i32], sz
         L.commvq_value_reduce.argtypes = [D, P, P, P, P, P, i32, i64, P, sz, P, P]
         L.commvq_value_reduce.restype = ctypes.c_int
@@ -159,6 +161,18 @@ def attn_decode(d: Dims, q, k_codes, v_codes, k_codebook, v_codebook, seq_start,
                                   _ptr(rope), int(rope_positions), _ptr(workspace), workspace.numel() *
                                   workspace.element_size(), _ptr(out), _stream(stream))
     _check(st, "attn_decode")
+    return out
+
+
+def attn_decode_noalloc(d: Dims, q, k_codes, v_codes, k_codebook, v_codebook, seq_start, seq_len, max_len: int,
+                        total_tokens: int, rope, rope_positions: int, out, stream=None):
+    """Decode-step attention through commvq_attn_decode_noalloc (the library's static scratch; no workspace).
+    `out` [B][Hq][D] fp32 must be given: nothing is allocated on this path."""
+    st = lib().commvq_attn_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_codebook),
+                                          _ptr(v_codebook), _ptr(seq_start), _ptr(seq_len), int(max_len),
+                                          int(total_tokens), _ptr(rope), int(rope_positions), _ptr(out),
+                                          _stream(stream))
+    _check(st, "attn_decode_noalloc")
     return out
 
 

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcommvq.so")
-SOURCES = ["api.cpp", "kernels.hip", "attn.hip", "attn_f16.hip", "attn_wide.hip"]
+SOURCES = ["api.cpp", "kernels.hip", "attn.hip", "attn_f16.hip", "attn_wide.hip", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

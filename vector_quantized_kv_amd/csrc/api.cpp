@@ -5,7 +5,6 @@
 #include <string.h>
 
 #include <cmath>
-#include <string>
 
 #include "commvq_internal.h"
 
@@ -13,20 +12,18 @@ using namespace commvq;
 
 namespace {
 
-thread_local std::string g_detail;
+thread_local char g_detail[512];  // detail of this thread's last failing call (a fixed buffer: nothing allocates)
 
 int fail(int status, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
   va_end(ap);
-  g_detail = buf;
   return status;
 }
 
 int ok() {
-  g_detail.clear();
+  g_detail[0] = '\0';
   return COMMVQ_OK;
 }
 
@@ -98,6 +95,65 @@ AttnWs attn_ws(const commvq_dims* d, int32_t max_len) {
 }
 size_t attn_ws_bytes(const commvq_dims* d, int32_t max_len) { return attn_ws(d, max_len).bytes; }
 
+
+// Argument checks shared by both attention entry points (every check runs before any HIP call).
+int check_attn_args(const commvq_dims* d, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
+                    const void* k_codebook, const void* v_codebook, const int64_t* seq_start, const int32_t* seq_len,
+                    int32_t max_len, int64_t total_tokens, const void* rope_table, int32_t rope_positions,
+                    const float* out) {
+  if (int st = check_dims(d)) return st;
+  if (!q || !k_codes || !v_codes || !k_codebook || !v_codebook || !seq_start || !seq_len || !rope_table || !out)
+    return fail(COMMVQ_EINVAL, "a required pointer is NULL");
+  if (max_len < 0) return fail(COMMVQ_EINVAL, "max_len = %d must be >= 0", max_len);
+  if (total_tokens < 0) return fail(COMMVQ_EINVAL, "total_tokens = %lld must be >= 0", (long long)total_tokens);
+  if (max_len > 0 && total_tokens < 1) return fail(COMMVQ_EINVAL, "total_tokens must be >= 1 when max_len > 0");
+  if (rope_positions < max_len)
+    return fail(COMMVQ_EINVAL, "rope_positions = %d < max_len = %d", rope_positions, max_len);
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(rope_table) || !aligned16(k_codebook) ||
+      !aligned16(v_codebook))
+    return fail(COMMVQ_EINVAL, "k_codes, v_codes, both codebooks and rope_table must be 16-byte aligned");
+  const int32_t split_tokens = attn_split_tokens(d->dtype, max_len, d->batch, d->n_kv_heads);
+  if (attn_n_splits(max_len, split_tokens) > kAttnMaxSplits)
+    return fail(COMMVQ_EUNSUPPORTED, "max_len = %d needs more than %d splits of %d tokens", max_len, kAttnMaxSplits,
+                split_tokens);
+  return COMMVQ_OK;
+}
+
+// Launch of either layout's attention kernel with the workspace regions given (arrival counters, (m, l) and
+// o partials); the arguments have been checked.
+int launch_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
+                       const void* k_codebook, const void* v_codebook, const int64_t* seq_start,
+                       const int32_t* seq_len, int32_t max_len, int64_t total_tokens, const void* rope_table,
+                       void* counters, void* part_ml, void* part_o, float* out, void* stream) {
+  const int32_t split_tokens = attn_split_tokens(d->dtype, max_len, d->batch, d->n_kv_heads);
+  AttnArgs a;
+  a.q = q;
+  a.k_codes = k_codes;
+  a.v_codes = v_codes;
+  a.k_cb = k_codebook;
+  a.v_cb = v_codebook;
+  a.seq_start = seq_start;
+  a.seq_len = seq_len;
+  a.total_tokens = total_tokens;
+  a.max_len = max_len;
+  a.rope = static_cast<const float2*>(rope_table);
+  a.split_tokens = split_tokens;
+  a.n_splits = static_cast<int32_t>(attn_n_splits(max_len, split_tokens));
+  a.n_q_heads = d->n_q_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.scale = d->softmax_scale;
+  a.n_residuals = d->n_residuals;
+  a.record_words = wide_record_words(d->n_residuals);
+  a.counters = static_cast<uint32_t*>(counters);
+  a.part_ml = static_cast<float2*>(part_ml);
+  a.part_o = static_cast<float*>(part_o);
+  a.out = out;
+  if (packed_family(d))
+    return hip_status(launch_attn_wide(d->batch, a, static_cast<hipStream_t>(stream)), "attn_decode launch");
+  return hip_status(launch_attn(d->dtype, d->n_residuals, d->batch, a, static_cast<hipStream_t>(stream)),
+                    "attn_decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -113,7 +169,7 @@ const char* commvq_status_string(int status) {
   }
 }
 
-const char* commvq_last_error_detail(void) { return g_detail.c_str(); }
+const char* commvq_last_error_detail(void) { return g_detail; }
 
 size_t commvq_rope_table_size(const commvq_dims* d, int32_t n_positions) {
   if (check_dims(d) != COMMVQ_OK || n_positions < 1) return 0;
@@ -149,51 +205,41 @@ int commvq_attn_decode(const commvq_dims* d, const void* q, const uint8_t* k_cod
                        const void* k_codebook, const void* v_codebook, const int64_t* seq_start,
                        const int32_t* seq_len, int32_t max_len, int64_t total_tokens, const void* rope_table,
                        int32_t rope_positions, void* workspace, size_t ws_bytes, float* out, void* stream) {
-  if (int st = check_dims(d)) return st;
-  if (!q || !k_codes || !v_codes || !k_codebook || !v_codebook || !seq_start || !seq_len || !rope_table || !out)
-    return fail(COMMVQ_EINVAL, "a required pointer is NULL");
-  if (max_len < 0) return fail(COMMVQ_EINVAL, "max_len = %d must be >= 0", max_len);
-  if (total_tokens < 0) return fail(COMMVQ_EINVAL, "total_tokens = %lld must be >= 0", (long long)total_tokens);
-  if (max_len > 0 && total_tokens < 1) return fail(COMMVQ_EINVAL, "total_tokens must be >= 1 when max_len > 0");
-  if (rope_positions < max_len)
-    return fail(COMMVQ_EINVAL, "rope_positions = %d < max_len = %d", rope_positions, max_len);
-  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(rope_table) || !aligned16(k_codebook) ||
-      !aligned16(v_codebook))
-    return fail(COMMVQ_EINVAL, "k_codes, v_codes, both codebooks and rope_table must be 16-byte aligned");
+  if (int st = check_attn_args(d, q, k_codes, v_codes, k_codebook, v_codebook, seq_start, seq_len, max_len,
+                               total_tokens, rope_table, rope_positions, out))
+    return st;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(COMMVQ_EINVAL, "workspace must be 256-byte aligned");
   const size_t need = attn_ws_bytes(d, max_len);
   if (!workspace || ws_bytes < need) return fail(COMMVQ_EWORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
-  const int32_t split_tokens = attn_split_tokens(d->dtype, max_len, d->batch, d->n_kv_heads);
-  if (attn_n_splits(max_len, split_tokens) > kAttnMaxSplits)
-    return fail(COMMVQ_EUNSUPPORTED, "max_len = %d needs more than %d splits of %d tokens", max_len, kAttnMaxSplits,
-                split_tokens);
   const AttnWs w = attn_ws(d, max_len);
-  AttnArgs a;
-  a.q = q;
-  a.k_codes = k_codes;
-  a.v_codes = v_codes;
-  a.k_cb = k_codebook;
-  a.v_cb = v_codebook;
-  a.seq_start = seq_start;
-  a.seq_len = seq_len;
-  a.total_tokens = total_tokens;
-  a.max_len = max_len;
-  a.rope = static_cast<const float2*>(rope_table);
-  a.split_tokens = split_tokens;
-  a.n_splits = static_cast<int32_t>(attn_n_splits(max_len, split_tokens));
-  a.n_q_heads = d->n_q_heads;
-  a.n_kv_heads = d->n_kv_heads;
-  a.scale = d->softmax_scale;
-  a.n_residuals = d->n_residuals;
-  a.record_words = wide_record_words(d->n_residuals);
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.part_ml = reinterpret_cast<float2*>(static_cast<unsigned char*>(workspace) + w.ml_offset);
-  a.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + w.o_offset);
-  a.out = out;
-  if (packed_family(d))
-    return hip_status(launch_attn_wide(d->batch, a, static_cast<hipStream_t>(stream)), "attn_decode launch");
-  return hip_status(launch_attn(d->dtype, d->n_residuals, d->batch, a, static_cast<hipStream_t>(stream)),
-                    "attn_decode launch");
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  return launch_attn_decode(d, q, k_codes, v_codes, k_codebook, v_codebook, seq_start, seq_len, max_len,
+                            total_tokens, rope_table, ws, ws + w.ml_offset, ws + w.o_offset, out, stream);
+}
+
+int commvq_attn_decode_noalloc(const commvq_dims* d, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
+                               const void* k_codebook, const void* v_codebook, const int64_t* seq_start,
+                               const int32_t* seq_len, int32_t max_len, int64_t total_tokens, const void* rope_table,
+                               int32_t rope_positions, float* out, void* stream) {
+  if (int st = check_attn_args(d, q, k_codes, v_codes, k_codebook, v_codebook, seq_start, seq_len, max_len,
+                               total_tokens, rope_table, rope_positions, out))
+    return st;
+  const size_t counters = static_cast<size_t>(d->batch) * d->n_kv_heads * sizeof(uint32_t);
+  if (counters > kNoAllocCounterBytes)
+    return fail(COMMVQ_EUNSUPPORTED, "batch x n_kv_heads = %zu exceeds the %zu arrival counters of the static scratch",
+                counters / sizeof(uint32_t), kNoAllocCounterBytes / sizeof(uint32_t));
+  // same partial layout as the caller-owned workspace, after the fixed counter head
+  const AttnWs w = attn_ws(d, max_len);
+  const size_t need = kNoAllocCounterBytes + (w.bytes - w.ml_offset);
+  if (need > kNoAllocScratchBytes)
+    return fail(COMMVQ_EWORKSPACE, "the call needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kNoAllocScratchBytes);
+  void* base = nullptr;
+  if (int st = hip_status(noalloc_scratch(&base, static_cast<hipStream_t>(stream)), "static scratch")) return st;
+  unsigned char* ws = static_cast<unsigned char*>(base);
+  unsigned char* parts = ws + kNoAllocCounterBytes;
+  return launch_attn_decode(d, q, k_codes, v_codes, k_codebook, v_codebook, seq_start, seq_len, max_len,
+                            total_tokens, rope_table, ws, parts, parts + (w.o_offset - w.ml_offset), out, stream);
 }
 
 size_t commvq_value_reduce_workspace_size(const commvq_dims* d, int32_t max_len) {

@@ -26,6 +26,10 @@ constexpr int kRopeCoarseOffset = kRopeFine32gOffset + kFineRows * kPairs;
 constexpr int kAttnMaxBlocksPerWave = 8;  // 64-token blocks per wave per split
 constexpr int kCounterBytes = 256;  // attention workspace head: per-(b, kv) arrival counters
 constexpr int kAttnMaxSplits = 8192;  // splits per sequence the last-workgroup merge can hold in LDS
+// commvq_attn_decode_noalloc: static device scratch per GPU (8 MiB), of which a fixed 64 KiB head holds the
+// arrival counters (16384 (sequence, KV head) pairs at most) and the rest the split partials
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(8) << 20;
+constexpr size_t kNoAllocCounterBytes = static_cast<size_t>(64) << 10;
 constexpr int kCUs = 256;             // compute units the split sizing aims to fill (one workgroup each)
 
 // Bit-packed family (one index per 64 dims): G = 2 groups, N = 64 codewords, 6-bit indices packed per
@@ -109,6 +113,9 @@ hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, 
                          void* out, hipStream_t s);
 hipError_t launch_attn(int dtype, int R, int B, const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f16(int R, int B, const AttnArgs& a, hipStream_t s);
+// Device address of this device's static scratch (noalloc.hip); the first call on a device also zeroes its
+// counter head on `stream`.
+hipError_t noalloc_scratch(void** out, hipStream_t stream);
 hipError_t launch_attn_wide(int B, const AttnArgs& a, hipStream_t s);
 hipError_t launch_value_reduce(int dtype, bool packed, int R, int B, const ValueReduceArgs& a, float* out,
                                hipStream_t s);
