@@ -1,7 +1,7 @@
 """commvq_attn_decode_noalloc (static device scratch, no workspace) against commvq_attn_decode.
 
 Both entry points run the same kernels on the same inputs; only where the split partials and arrival counters
-live differs. Each call is compared with the workspace entry point's output at the C-A10 tolerance (per
+live differs. Each call is compared with the workspace entry point's output at the parity tolerance (per
 (b, q head) row, max |a - b| / max |b|: 2e-3 fp16, 1e-5 fp32). Two calls in a row go through the static
 scratch, the second with a smaller input (fewer sequences, KV heads and tokens), so the second call finds the
 first one's partials in the array and counters that the first call must have left zero.
