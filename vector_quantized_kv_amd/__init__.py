@@ -105,10 +105,23 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream=None):
+def _launch_stream(stream=None):
+    """The stream a call is enqueued on: `stream`, else torch's current stream."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return torch.cuda.current_stream() if stream is None else stream
+
+
+def _stream(stream=None):
+    return ctypes.c_void_p(_launch_stream(stream).cuda_stream)
+
+
+def _on(stream=None):
+    """Context that makes the launch stream current while the binding allocates outputs and temporaries: the
+    caching allocator then ties them to that stream (a temporary freed on return is reused only by later work
+    on the same stream, which runs after the kernel), and the workspace zero-fill runs on it, ahead of the
+    kernel that reads it."""
+    import torch
+    return torch.cuda.stream(_launch_stream(stream))
 
 
 def _torch_dtype(d: Dims):
@@ -122,7 +135,8 @@ def rope_table(d: Dims, n_positions: int, device="cuda", stream=None):
     nbytes = lib().commvq_rope_table_size(ctypes.byref(d), int(n_positions))
     if nbytes == 0:
         _check(lib().commvq_rope_table(ctypes.byref(d), int(n_positions), None, 0, None), "rope_table")
-    t = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    with _on(stream):
+        t = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
     _check(lib().commvq_rope_table(ctypes.byref(d), int(n_positions), ctypes.c_void_p(t.data_ptr()), nbytes,
                                    _stream(stream)), "rope_table")
     return t
@@ -131,8 +145,9 @@ def rope_table(d: Dims, n_positions: int, device="cuda", stream=None):
 def qcodebook_table(d: Dims, q, k_codebook, out=None, stream=None):
     import torch
     if out is None:
-        out = torch.empty((d.batch, d.n_q_heads, d.n_groups, d.n_residuals, d.n_codes, d.head_dim // d.n_groups),
-                          dtype=_torch_dtype(d), device=q.device)
+        with _on(stream):
+            out = torch.empty((d.batch, d.n_q_heads, d.n_groups, d.n_residuals, d.n_codes,
+                               d.head_dim // d.n_groups), dtype=_torch_dtype(d), device=q.device)
     _check(lib().commvq_qcodebook_table(ctypes.byref(d), _ptr(q), _ptr(k_codebook), _ptr(out), _stream(stream)),
            "qcodebook_table")
     return out
@@ -152,10 +167,11 @@ def attn_decode(d: Dims, q, k_codes, v_codes, k_codebook, v_codebook, seq_start,
                 total_tokens: int, rope, rope_positions: int, workspace=None, out=None, stream=None):
     """Decode-step attention; returns out [B][Hq][D] fp32 (see commvq_attn_decode)."""
     import torch
-    if out is None:
-        out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = attn_workspace(d, max_len, q.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = attn_workspace(d, max_len, q.device)
     st = lib().commvq_attn_decode(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_codebook),
                                   _ptr(v_codebook), _ptr(seq_start), _ptr(seq_len), int(max_len), int(total_tokens),
                                   _ptr(rope), int(rope_positions), _ptr(workspace), workspace.numel() *
@@ -184,10 +200,12 @@ def value_reduce(d: Dims, p, v_codes, v_codebook, seq_start, seq_len, max_len: i
                  workspace=None, out=None, stream=None):
     """out[b][h] = sum_t p[b][h][t] * vhat_t via code bins (see commvq_value_reduce)."""
     import torch
-    if out is None:
-        out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=p.device)
-    if workspace is None:
-        workspace = torch.empty(max(value_reduce_workspace_size(d, max_len), 16), dtype=torch.uint8, device=p.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=p.device)
+        if workspace is None:
+            workspace = torch.empty(max(value_reduce_workspace_size(d, max_len), 16), dtype=torch.uint8,
+                                    device=p.device)
     st = lib().commvq_value_reduce(ctypes.byref(d), _ptr(p), _ptr(v_codes), _ptr(v_codebook), _ptr(seq_start),
                                    _ptr(seq_len), int(max_len), int(total_tokens), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
@@ -203,11 +221,13 @@ def encode_greedy(d: Dims, x, codebook, codes=None, first_row: int = 0, stream=N
     n = int(x.shape[1])
     packed = d.n_codes < 256
     if codes is None:
-        if packed:
-            words = (6 * d.n_residuals * d.n_groups + 31) // 32
-            codes = torch.zeros((d.n_kv_heads, n, words), dtype=torch.int32, device=x.device)
-        else:
-            codes = torch.zeros((d.n_kv_heads, d.n_residuals, n, d.n_groups), dtype=torch.uint8, device=x.device)
+        with _on(stream):
+            if packed:
+                words = (6 * d.n_residuals * d.n_groups + 31) // 32
+                codes = torch.zeros((d.n_kv_heads, n, words), dtype=torch.int32, device=x.device)
+            else:
+                codes = torch.zeros((d.n_kv_heads, d.n_residuals, n, d.n_groups), dtype=torch.uint8,
+                                    device=x.device)
     rows = int(codes.shape[1] if packed else codes.shape[2])
     _check(lib().commvq_encode_greedy(ctypes.byref(d), _ptr(x), _ptr(codebook), n, _ptr(codes), rows,
                                       int(first_row), _stream(stream)), "encode_greedy")
@@ -220,7 +240,8 @@ def codebook_update(d: Dims, x, codes, codebook_in, codebook_out=None, stream=No
     import torch
     n = int(x.shape[1])
     if codebook_out is None:
-        codebook_out = torch.empty_like(codebook_in)
+        with _on(stream):
+            codebook_out = torch.empty_like(codebook_in)
     _check(lib().commvq_codebook_update(ctypes.byref(d), _ptr(x), _ptr(codes), n, _ptr(codebook_in),
                                         _ptr(codebook_out), _stream(stream)), "codebook_update")
     return codebook_out
@@ -240,8 +261,9 @@ def fit_codebook(d: Dims, x, codebook, iterations: int, stream=None):
 def debug_unpack(d: Dims, codes, total_tokens: int, out=None, stream=None):
     import torch
     if out is None:
-        out = torch.empty((d.n_kv_heads, d.n_residuals, int(total_tokens), d.n_groups), dtype=torch.int32,
-                          device=codes.device)
+        with _on(stream):
+            out = torch.empty((d.n_kv_heads, d.n_residuals, int(total_tokens), d.n_groups), dtype=torch.int32,
+                              device=codes.device)
     _check(lib().commvq_debug_unpack(ctypes.byref(d), _ptr(codes), int(total_tokens), _ptr(out), _stream(stream)),
            "debug_unpack")
     return out
