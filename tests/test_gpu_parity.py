@@ -148,6 +148,35 @@ def test_value_reduce_matches_oracle(vq, dtype, R, signed):
     assert err <= TOL[dtype]
 
 
+SOFTMAX_P = [("float32", 2, 3.0), ("float32", 1, 3.0), ("float32", 2, 6.0), ("float16", 2, 3.0)]
+
+
+@pytest.mark.parametrize("dtype,R,score_std", SOFTMAX_P)
+def test_value_reduce_softmax_weights(vq, dtype, R, score_std):
+    """Softmax-shaped weights (scores of standard deviation 3 or 6 over each sequence): a few weights near the
+    split maximum and many orders of magnitude below it, the case where the fixed-point bins round most."""
+    announce(f"value_reduce softmax p {dtype} R={R} std={score_std}")
+    cfg = workloads.custom("vr_sm", 3, 8, 2, (5000, 700, 3072), R, dtype, 24 + R)
+    inp = workloads.make_inputs(cfg)
+    L = int(inp["max_len"])
+    rng = np.random.default_rng(25 + R)
+    s = rng.normal(0.0, score_std, size=(3, 8, L))
+    p = np.zeros((3, 8, L), dtype=np.float32)
+    for b, n in enumerate(int(x) for x in inp["seq_len"]):
+        e = np.exp(s[b, :, :n] - s[b, :, :n].max(-1, keepdims=True))
+        p[b, :, :n] = (e / e.sum(-1, keepdims=True)).astype(np.float32)
+    d = vq.dims_of(cfg)
+    dt = torch.float16 if dtype == "float16" else torch.float32
+    got = vq.value_reduce(d, torch.from_numpy(p).cuda(), torch.from_numpy(inp["v_codes"]).cuda(),
+                          torch.from_numpy(inp["v_cb"]).cuda().to(dt), torch.from_numpy(inp["seq_start"]).cuda(),
+                          torch.from_numpy(inp["seq_len"]).cuda(), L, int(inp["total_tokens"]))
+    torch.cuda.synchronize()
+    ref = oracle.value_reduce(oracle.dims_of(cfg), p, inp["v_codes"], inp["v_cb"], inp["seq_start"], inp["seq_len"], L)
+    err = rowwise_rel_err(got.cpu().numpy(), ref)
+    print(f"value_reduce softmax p {dtype} R={R} std={score_std}: {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
 def test_rope_table_matches_fp64(vq):
     announce("rope_table")
     d = vq.make_dims(1, 4, 1, 1)

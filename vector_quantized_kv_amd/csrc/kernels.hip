@@ -109,18 +109,34 @@ hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, 
 }
 
 // ----------------------------------------------------------------------------------- value bins
-// Fixed-point bins: LDS float atomics are slow on this chip, integer ones are not; weights are
-// scaled by `fx_scale` (so |w * fx_scale| <= 2^20) and rounded, which keeps a 1024-token split's bin
-// sums inside int32. bins layout [kGqa][kGroups][R][kCodes].
+// Fixed-point bins: LDS float atomics are slow on this chip, integer ones are not. Per (split, head) the
+// weights are scaled by a power of two, fx_scale = 2^(20 - e) with max|w| < 2^e, so |w * fx_scale| < 2^20
+// exactly and a 1024-token split's bin sums stay inside int32. Pass 0 bins rint(w * fx_scale); the fp32
+// path adds pass 1, which bins rint((w * fx_scale - rint(w * fx_scale)) * 2^20), the rounding residual of
+// pass 0 at 2^20 times the resolution (every step exact, as the scale is a power of two). A weight is thus
+// represented to 2^-21 of the split's max|w| (fp16 storage) or 2^-41 (fp32). bins layout [kGqa][kGroups][R][kCodes].
+__device__ __forceinline__ int32_t fixed_point(float w, float fx_scale, int pass) {
+  const float x = w * fx_scale;
+  const float hi = rintf(x);
+  return static_cast<int32_t>(pass == 0 ? hi : rintf((x - hi) * 1048576.f));
+}
+
+__device__ __forceinline__ float fixed_point_scale(float max_abs) {
+  if (!(max_abs > 0.f)) return 1.f;
+  int e;
+  frexpf(max_abs, &e);  // max_abs = m 2^e, m in [0.5, 1)
+  return ldexpf(1.f, 20 - e);
+}
+
 template <int R, int TPT>
 __device__ __forceinline__ void bin_weights(int32_t* bins, const uint4 (&vc)[TPT][R], const float (&w)[TPT][kGqa],
-                                            const bool (&valid)[TPT], const float (&fx_scale)[kGqa]) {
+                                            const bool (&valid)[TPT], const float (&fx_scale)[kGqa], int pass) {
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
     if (!valid[k]) continue;
     int32_t fx[kGqa];
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<int32_t>(rintf(w[k][h] * fx_scale[h]));
+    for (int h = 0; h < kGqa; ++h) fx[h] = fixed_point(w[k][h], fx_scale[h], pass);
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
 #pragma unroll
@@ -132,33 +148,33 @@ __device__ __forceinline__ void bin_weights(int32_t* bins, const uint4 (&vc)[TPT
   }
 }
 
-// o[h][8g+w] = sum_r sum_l bins[h][g][r][l] * CV[g][r][l][w] / fx_scale[h]; thread handles 2 outputs.
+// acc[i] += weight * sum_r sum_l bins[h][g][r][l] * CV[g][r][l][w] for output d = (tid + 256 i) & 127 of head
+// h = (tid + 256 i) >> 7 (o = 8 g + w); each thread handles 2 outputs.
 template <typename T, int R>
-__device__ __forceinline__ void contract_bins(const int32_t* bins, const T* vcb, const float (&fx_scale)[kGqa],
-                                              float* part_base /* [kGqa] rows of kPartFloats */,
-                                              int64_t part_row_stride) {
+__device__ __forceinline__ void contract_bins(const int32_t* bins, const T* vcb, float weight, float (&acc)[2]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int idx = tid + 256 * i, h = idx >> 7, d = idx & 127, g = d >> 3, w = d & 7;
-    float acc = 0.f;
+    float sum = 0.f;
     for (int r = 0; r < R; ++r) {
       const int32_t* bb = bins + ((h * kGroups + g) * R + r) * kCodes;
       const T* cv = vcb + ((static_cast<int64_t>(g) * R + r) * kCodes) * kGroupDim + w;
-      for (int l = 0; l < kCodes; ++l) acc = fmaf(static_cast<float>(bb[l]), ld(cv + l * kGroupDim), acc);
+      for (int l = 0; l < kCodes; ++l) sum = fmaf(static_cast<float>(bb[l]), ld(cv + l * kGroupDim), sum);
     }
-    part_base[h * part_row_stride + 4 + d] = acc / fx_scale[h];
+    acc[i] = fmaf(sum, weight, acc[i]);
   }
 }
 
 // ----------------------------------------------------------------------------------- value reduce
 // The reordered value reduce of the pages: weights are binned by value code (bin_weights), then the
 // bins are contracted with the value codebook (contract_bins). One workgroup per (sequence, KV head,
-// 1024-token split); partial outputs are summed by combine_sum_kernel. Fixed-point scale per head is
-// 2^20 / max|p| over the split, so any finite weights bin exactly up to that relative resolution.
+// 1024-token split); partial outputs are summed by combine_sum_kernel. Any finite weights bin exactly up
+// to the fixed-point resolution above (one pass for fp16 storage, two for fp32).
 template <typename T, int R>
 __global__ void __launch_bounds__(256) value_reduce_kernel(const ValueReduceArgs a) {
   constexpr int TPT = kSplitTokens / 256;
+  constexpr int kPasses = sizeof(T) == 4 ? 2 : 1;
   __shared__ float red[4][kGqa];
   __shared__ __attribute__((aligned(16))) int32_t work[kGqa * kGroups * R * kCodes];
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -184,7 +200,6 @@ __global__ void __launch_bounds__(256) value_reduce_kernel(const ValueReduceArgs
       vc[k][r] = valid[k] ? load_code_record(a.v_codes, a.total_tokens, kv, row0 + tid + 256 * k, R, r)
                           : make_uint4(0, 0, 0, 0);
   }
-  for (int i = tid; i < kGqa * kGroups * R * kCodes; i += 256) work[i] = 0;
 #pragma unroll
   for (int h = 0; h < kGqa; ++h) {
     float mx = 0.f;
@@ -196,16 +211,25 @@ __global__ void __launch_bounds__(256) value_reduce_kernel(const ValueReduceArgs
   __syncthreads();
   float fx_scale[kGqa];
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h) {
-    const float mx = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
-    fx_scale[h] = mx > 0.f ? 1048576.f / mx : 1.f;
+  for (int h = 0; h < kGqa; ++h)
+    fx_scale[h] = fixed_point_scale(fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h])));
+  const T* vcb = static_cast<const T*>(a.v_cb) + static_cast<int64_t>(kv) * kGroups * R * kCodes * kGroupDim;
+  float acc[2] = {0.f, 0.f};
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass > 0) __syncthreads();  // every thread has finished reading the previous pass's bins
+    for (int i = tid; i < kGqa * kGroups * R * kCodes; i += 256) work[i] = 0;
+    __syncthreads();
+    bin_weights<R, TPT>(work, vc, w, valid, fx_scale, pass);
+    __syncthreads();
+    contract_bins<T, R>(work, vcb, pass == 0 ? 1.f : 1.f / 1048576.f, acc);
   }
-  bin_weights<R, TPT>(work, vc, w, valid, fx_scale);
-  __syncthreads();
   float* part = a.part + ((static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits + split) * kPartFloats;
   const int64_t row_stride = static_cast<int64_t>(a.n_splits) * kPartFloats;
-  const T* vcb = static_cast<const T*>(a.v_cb) + static_cast<int64_t>(kv) * kGroups * R * kCodes * kGroupDim;
-  contract_bins<T, R>(work, vcb, fx_scale, part, row_stride);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int idx = tid + 256 * i, h = idx >> 7, d = idx & 127;
+    part[h * row_stride + 4 + d] = acc[i] / fx_scale[h];
+  }
 }
 
 __global__ void __launch_bounds__(128) combine_sum_kernel(const float* part, const ValueReduceArgs a, float* out) {
@@ -219,7 +243,8 @@ __global__ void __launch_bounds__(128) combine_sum_kernel(const float* part, con
   out[static_cast<int64_t>(bh) * kHeadDim + d] = acc;
 }
 
-// Bit-packed records (G = 2, N = 64, W = 64, R up to 32): the same split, fixed-point bins and partials.
+// Bit-packed records (G = 2, N = 64, W = 64, R up to 32, fp16 storage): the same split, one-pass fixed-point
+// bins and partials.
 // Bins [kGqa][2][R][64] (64 KiB at R = 32); each token reads its R x 2 indices field by field.
 __global__ void __launch_bounds__(256) value_reduce_bits_kernel(const ValueReduceArgs a, int R) {
   constexpr int TPT = kSplitTokens / 256;
@@ -258,16 +283,14 @@ __global__ void __launch_bounds__(256) value_reduce_bits_kernel(const ValueReduc
   __syncthreads();
   float fx_scale[kGqa];
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h) {
-    const float mx = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
-    fx_scale[h] = mx > 0.f ? 1048576.f / mx : 1.f;
-  }
+  for (int h = 0; h < kGqa; ++h)
+    fx_scale[h] = fixed_point_scale(fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h])));
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
     if (!valid[k]) continue;
     int32_t fx[kGqa];
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<int32_t>(rintf(w[k][h] * fx_scale[h]));
+    for (int h = 0; h < kGqa; ++h) fx[h] = fixed_point(w[k][h], fx_scale[h], 0);
     const uint32_t* rec = words + (static_cast<int64_t>(kv) * a.total_tokens + row0 + tid + 256 * k) * Wd;
     for (int r = 0; r < R; ++r)
 #pragma unroll
