@@ -93,9 +93,10 @@ const char* commvq_last_error_detail(void);
 
 /* ---------------------------------------------------------------------------------------------
  * RoPE phase table: e^{i * t * theta_j} for positions t = 0 .. n_positions-1, stored as two levels in
- * three sections, each entry computed in fp64 and rounded once:
+ * four sections, each entry computed in fp64 and rounded once:
  *   fine[j][f]   = e^{i f theta_j}, f < 64, pair-major, complex fp32 (re, im)        (32 KiB)
  *   fine16[g][f][u] = the same phases for pair j = 4g + u, packed fp16 (re, im)      (16 KiB)
+ *   fine32g[g][h][f][p] = the same phases for pair j = 4g + 2h + p, complex fp32     (32 KiB)
  *   coarse[c][j] = e^{i 64 c theta_j}, c < ceil(n_positions / 64), complex fp32     (512 B per row)
  * The rotation of a key at position t is coarse[t >> 6][j] * fine[j][t & 63]
  * ("pith.science verdict", key_machinery: the block-diagonal rotation R_m of each 2-D sub-vector).
@@ -119,11 +120,19 @@ int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const
                            void* stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Decode-step attention over the compressed cache. For every (b, h):
+ * Decode-step attention over the compressed cache (pith.science verdict for arXiv 2506.18879,
+ * key_machinery: keys are additive codes whose 2x2 codeword blocks commute with the RoPE rotation, so the
+ * query meets the codebook once per step; forward_implications: values are weighted by the softmax before
+ * the codebook product; CommVQ summary page, Approach). For every (b, h):
  *   s_t   = softmax_scale * sum_j Re( conj(q_j) * khat_{t,j} * e^{i t theta_j} ),  t < L_b
  *   khat_{t,j} = sum_r k_codebook[kv][g][r][k_codes[kv][r][seq_start[b]+t][g]][2u..2u+1]   (j = 4g+u)
  *   out[b][h] = sum_t softmax(s)_t * vhat_t,  vhat_t = sum_r v_codebook[kv][g][r][v_codes[kv][r][..][g]]
  * No key or value is dequantized to memory. Sequences with L_b = 0 produce zeros.
+ * Arithmetic: codewords are read in dtype; the residual sum, the key rotation, the scores, the softmax and
+ * the value accumulation run in fp32 for both dtypes (fp16 storage included), so the error does not grow
+ * with the logit range: results stay within 2e-3 (fp16 storage) and 1e-5 (fp32) of the exact value per
+ * output row, relative to the row's largest entry, for score spreads up to a standard deviation of 12 and
+ * tokens that dominate the softmax.
  * rope_table: from commvq_rope_table with rope_positions >= max_len.
  * max_len (host) should be >= every seq_len[b], and seq_start[b] + seq_len[b] <= total_tokens (host),
  * the row count of the code arrays. The kernels cannot report a descriptor that breaks these bounds (it
@@ -171,6 +180,11 @@ int commvq_attn_decode_noalloc(const commvq_dims* d /* host */, const void* q, c
  * v_codes: the byte planes [Hkv][R][T][G], or (bit-packed layout) the token records [Hkv][T][words].
  * p: [B][Hq][max_len] fp32, any finite real values, used as given (no renormalisation); entries at
  * t >= L_b are ignored. workspace: commvq_value_reduce_workspace_size(d, max_len) bytes.
+ * Resolution: the bins are integer fixed point per (b, h, 1024-token split of t): each weight is rounded to
+ * a multiple of 2^-20 * 2^e, where 2^e is the power of two just above the split's max |p| (fp16 storage),
+ * and its rounding residual once more at 2^-40 * 2^e (fp32 storage). A weight below half that step (about
+ * 2^-21, resp. 2^-41, of the split's largest) thus contributes nothing, and every other one is represented
+ * to that absolute step; the result does not depend on the order of the adds.
  * seq_start / seq_len are clamped as in commvq_attn_decode (length at most max_len and the rows left).
  * ------------------------------------------------------------------------------------------- */
 size_t commvq_value_reduce_workspace_size(const commvq_dims* d /* host */, int32_t max_len);

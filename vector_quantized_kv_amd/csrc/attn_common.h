@@ -1,5 +1,5 @@
-// Device pieces shared by the two attention kernels (byte-index and bit-packed records): fp16 vector
-// types, MFMA wrappers, the fine-phase rotation, workgroup barriers, the key MFMA step and the epilogue
+// Device pieces shared by the attention kernels (byte layout in fp16 and fp32 storage, bit-packed records):
+// fp16 vector types, MFMA wrappers, workgroup barriers, codebook staging, the wave softmax and the epilogue
 // (workgroup combine of the waves' partial outputs, split partials, last-workgroup merge).
 #pragma once
 
@@ -34,15 +34,6 @@ __device__ __forceinline__ f4 mfma(h4 a, h4 b, f4 c) { return __builtin_amdgcn_m
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ h4 cat(h2 a, h2 b) { return (h4){a.x, a.y, b.x, b.y}; }
 __device__ __forceinline__ h4 to_h4(f4 x) { return (h4){(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]}; }
-
-// k * e^{i phi} for packed fp16 complex numbers (re in the low half, im in the high half), with
-// f = (cos, sin): t = k.im * f = (k.im cos, k.im sin), then w = k.re * f + (-t.im, t.re). Every half
-// broadcast, swap and negation applies to k or t (values used once), so they fold into operand
-// modifiers of the two packed instructions and f is used as stored.
-__device__ __forceinline__ h2 crot(h2 k, h2 f) {
-  const h2 t = (h2){k.y, k.y} * f;
-  return (h2){k.x, k.x} * f + (h2){-t.y, t.x};
-}
 
 struct Split2 {  // fp32 value as fp16 hi + lo
   f16 hi, lo;
@@ -93,19 +84,6 @@ __device__ __forceinline__ h4 lds_read_tr(const void* p) {
 __device__ __forceinline__ h4 identity_b(int lane) {
   const int j = lane & 3;
   return (h4){(f16)(j == 0), (f16)(j == 1), (f16)(j == 2), (f16)(j == 3)};
-}
-
-// key step of group G from its gathered row: rotate by the fine phase, two MFMA steps
-template <int G>
-__device__ __forceinline__ void key_step(const uint4& row, const uint4 (&F)[kGroups], const h4& A0, const h4& A1,
-                                         f4& acc) {
-  const h2 w0 = crot(as_h2(row.x), as_h2(F[G].x));
-  const h2 w1 = crot(as_h2(row.y), as_h2(F[G].y));
-  const h2 w2 = crot(as_h2(row.z), as_h2(F[G].z));
-  const h2 w3 = crot(as_h2(row.w), as_h2(F[G].w));
-  const h4 A = (G < 8) ? A0 : A1;
-  acc = mfma_bcast<(2 * G) & 15>(A, cat(w0, w1), acc);
-  acc = mfma_bcast<(2 * G + 1) & 15>(A, cat(w2, w3), acc);
 }
 
 // fp16 block loops are software pipelines over units (a quarter or a pair of groups): the gathers of unit
