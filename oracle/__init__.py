@@ -21,15 +21,25 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# COMMVQ_ORACLE_SANITIZE=1: build and load the oracle with AddressSanitizer and UndefinedBehaviorSanitizer
+# (the sanitizer runtimes must then be preloaded into the Python process)
+_SANITIZE = os.environ.get("COMMVQ_ORACLE_SANITIZE") == "1"
+_SAN_LIB = os.path.join(os.path.dirname(_HERE), "_build", "liboracle_san.so")
+_SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc into liboracle.so (plain C, fp64, pthreads)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: Optional[bool] = None) -> str:
+    """Compile oracle.c with gcc into liboracle.so (plain C, fp64, pthreads), or with sanitize (default: the
+    COMMVQ_ORACLE_SANITIZE setting) into _build/liboracle_san.so."""
+    san = _SANITIZE if sanitize is None else sanitize
+    out = _SAN_LIB if san else _LIB
+    if force or not os.path.exists(out):
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        tmp = out + ".tmp"
+        flags = _SAN_FLAGS if san else ["-O2"]
+        subprocess.check_call(["gcc", *flags, "-std=c11", "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 class Dims(ctypes.Structure):
@@ -44,9 +54,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=False)
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(build(force=False))
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         D = ctypes.POINTER(Dims)

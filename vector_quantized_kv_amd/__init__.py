@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libcommvq.so")
+# COMMVQ_LIBRARY names another build of the same C ABI (the host-only sanitizer build, which has no device
+# code and fails every launch with COMMVQ_EHIP); by default the in-tree libcommvq.so is loaded.
+LIB_PATH = os.environ.get("COMMVQ_LIBRARY") or os.path.join(PKG, "libcommvq.so")
 
 F16, F32 = 1, 2
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4

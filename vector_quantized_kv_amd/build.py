@@ -37,5 +37,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+HOST_CHECK_LIB = os.path.join(ROOT, "_build", "libcommvq_hostcheck.so")
+HOST_CHECK_SOURCES = ["api.cpp", "host_stubs.cpp"]
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build_host_check() -> str:
+    """Host-only build of the C ABI (argument checks, sizing, error reporting) with AddressSanitizer and
+    UndefinedBehaviorSanitizer, compiled by g++ with every device launch replaced by a stub that reports
+    hipErrorNoDevice (csrc/host_stubs.cpp). Load it with COMMVQ_LIBRARY and the sanitizer runtimes preloaded."""
+    os.makedirs(os.path.dirname(HOST_CHECK_LIB), exist_ok=True)
+    tmp = HOST_CHECK_LIB + ".tmp"
+    cmd = ["g++", "-std=c++17", "-fPIC", "-shared", *SANITIZE_FLAGS, "-D__HIP_PLATFORM_AMD__", "-I",
+           "/opt/rocm/include", "-I", INCLUDE, "-I", CSRC, "-o", tmp] + \
+          [os.path.join(CSRC, s) for s in HOST_CHECK_SOURCES]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout + proc.stderr)
+        raise RuntimeError("g++ failed building the host-check library")
+    os.replace(tmp, HOST_CHECK_LIB)
+    return HOST_CHECK_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
