@@ -169,11 +169,12 @@ def attn_decode(d: Dims, q, k_codes, v_codes, k_codebook, v_codebook, seq_start,
                 total_tokens: int, rope, rope_positions: int, workspace=None, out=None, stream=None):
     """Decode-step attention; returns out [B][Hq][D] fp32 (see commvq_attn_decode)."""
     import torch
-    with _on(stream):
-        if out is None:
-            out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=q.device)
-        if workspace is None:
-            workspace = attn_workspace(d, max_len, q.device)
+    if out is None or workspace is None:
+        with _on(stream):
+            if out is None:
+                out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=q.device)
+            if workspace is None:
+                workspace = attn_workspace(d, max_len, q.device)
     st = lib().commvq_attn_decode(ctypes.byref(d), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_codebook),
                                   _ptr(v_codebook), _ptr(seq_start), _ptr(seq_len), int(max_len), int(total_tokens),
                                   _ptr(rope), int(rope_positions), _ptr(workspace), workspace.numel() *
@@ -202,12 +203,13 @@ def value_reduce(d: Dims, p, v_codes, v_codebook, seq_start, seq_len, max_len: i
                  workspace=None, out=None, stream=None):
     """out[b][h] = sum_t p[b][h][t] * vhat_t via code bins (see commvq_value_reduce)."""
     import torch
-    with _on(stream):
-        if out is None:
-            out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=p.device)
-        if workspace is None:
-            workspace = torch.empty(max(value_reduce_workspace_size(d, max_len), 16), dtype=torch.uint8,
-                                    device=p.device)
+    if out is None or workspace is None:
+        with _on(stream):
+            if out is None:
+                out = torch.empty((d.batch, d.n_q_heads, d.head_dim), dtype=torch.float32, device=p.device)
+            if workspace is None:
+                workspace = torch.empty(max(value_reduce_workspace_size(d, max_len), 16), dtype=torch.uint8,
+                                        device=p.device)
     st = lib().commvq_value_reduce(ctypes.byref(d), _ptr(p), _ptr(v_codes), _ptr(v_codebook), _ptr(seq_start),
                                    _ptr(seq_len), int(max_len), int(total_tokens), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))

@@ -271,48 +271,64 @@ __device__ __forceinline__ void attn_epilogue(const AttnArgs& a, unsigned char* 
   // The partials are read with device-scope (agent) loads, which read through to the coherence point the
   // partial stores wrote through to; this replaces an acquire fence, which on this chip invalidates the
   // whole L2.
-  // Each thread owns outputs (h, d) and combines the splits itself: per chunk of splits it issues every
-  // load at once (its partial o_s[d] and the head's (m_s, l_s)), so a chunk costs one memory round trip;
-  // a running maximum rescales earlier chunks (one chunk covers up to 32 splits, 128K tokens).
+  // Per chunk of up to kChunk splits, one memory round trip: the first kGqa * kChunk threads each load one
+  // (m_s, l_s) into LDS (the reduction buffer, free again), and every thread loads the partial o_s[d] of its
+  // output (h, d) for every split of the chunk; after the barrier each thread combines its output, a running
+  // maximum rescaling earlier chunks (one chunk covers 32 splits: 128K tokens at the largest split).
   constexpr int kChunk = 32;
   constexpr int kOut = kGqa * kHeadDim / kThreads;
+  static_assert(kGqa * kChunk <= kThreads, "one (m, l) load per thread");
+  float2* ml_lds = reinterpret_cast<float2*>(lds);
+  float M[kOut], num[kOut], den[kOut];
 #pragma unroll
   for (int k = 0; k < kOut; ++k) {
-    const int o = tid + kThreads * k;
-    const int h = o >> 7, d = o & 127;
-    const float* po = a.part_o + (bh0 + h) * ns_alloc * kHeadDim + d;
-    const float2* pml = a.part_ml + (bh0 + h) * ns_alloc;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += kChunk) {
-      float v[kChunk];
-      float2 ml[kChunk];
+    M[k] = -INFINITY;
+    num[k] = 0.f;
+    den[k] = 0.f;
+  }
+  for (int s0 = 0; s0 < ns; s0 += kChunk) {
+    if (s0 > 0) __syncthreads();  // every thread is done with the previous chunk's (m, l)
+    if (tid < kGqa * kChunk) {
+      const int h = tid / kChunk, u = tid % kChunk;
+      const float* pm = reinterpret_cast<const float*>(a.part_ml + (bh0 + h) * ns_alloc + s0 + u);
+      ml_lds[tid] = s0 + u < ns ? make_float2(__hip_atomic_load(pm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                                              __hip_atomic_load(pm + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                : make_float2(-INFINITY, 0.f);
+    }
+    float v[kOut][kChunk];
 #pragma unroll
-      for (int u = 0; u < kChunk; ++u) {
-        const bool ok = s0 + u < ns;
-        const float* pm = reinterpret_cast<const float*>(pml + s0 + u);
-        v[u] = ok ? __hip_atomic_load(po + static_cast<int64_t>(s0 + u) * kHeadDim, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT)
-                  : 0.f;
-        ml[u] = ok ? make_float2(__hip_atomic_load(pm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                                 __hip_atomic_load(pm + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                   : make_float2(-INFINITY, 0.f);
-      }
-      float mc = M;
+    for (int k = 0; k < kOut; ++k) {
+      const int o = tid + kThreads * k;
+      const int h = o >> 7, d = o & 127;
+      const float* po = a.part_o + ((bh0 + h) * ns_alloc + s0) * kHeadDim + d;
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        v[k][u] = s0 + u < ns ? __hip_atomic_load(po + static_cast<int64_t>(u) * kHeadDim, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : 0.f;
+    }
+    __syncthreads();  // the chunk's (m, l) are in LDS
+#pragma unroll
+    for (int k = 0; k < kOut; ++k) {
+      const int h = (tid + kThreads * k) >> 7;
+      const float2* ml = ml_lds + h * kChunk;
+      float mc = M[k];
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) mc = fmaxf(mc, ml[u].x);  // finite: split 0 always has tokens
-      const float r = __expf(M - mc);  // 0 on the first chunk
-      num *= r;
-      den *= r;
+      const float r = __expf(M[k] - mc);  // 0 on the first chunk
+      num[k] *= r;
+      den[k] *= r;
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) {
         const float w = __expf(ml[u].x - mc);  // 0 past the last split
-        num = fmaf(w, v[u], num);
-        den = fmaf(w, ml[u].y, den);
+        num[k] = fmaf(w, v[k][u], num[k]);
+        den[k] = fmaf(w, ml[u].y, den[k]);
       }
-      M = mc;
+      M[k] = mc;
     }
-    out_bh[o] = num / den;
   }
+#pragma unroll
+  for (int k = 0; k < kOut; ++k) out_bh[tid + kThreads * k] = num[k] / den[k];
   if (tid == 0) __hip_atomic_store(a.counters + b * a.n_kv_heads + kv, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -25,10 +25,9 @@
 // pass runs group-major: a wave reads one group's phases once and applies them to 2 of its blocks (one
 // "sweep"); a full wave (8 blocks) makes four sweeps, shorter waves go block by block.
 //
-// LDS: slot 0 and slot 1 (64 KiB each: one residual codebook, 16 groups x 256 rows x 8 fp16) and the
-// phase table (32 KiB) fill the CU's 160 KiB. R = 1: slot 0 = key, slot 1 = value codebook, both loaded
-// in the prologue. R = 2: slots 0/1 = the two key codebooks; after the key pass both are refilled with the
-// value codebooks.
+// LDS: two residual codebooks (64 KiB each: 16 groups x 256 rows x 8 fp16) and the phase table (32 KiB) fill
+// the CU's 160 KiB (map below). R = 1: key and value codebook, both loaded in the prologue. R = 2: the two key
+// codebooks, replaced by the two value codebooks in two halves (groups 0-7, then 8-15) as the passes move on.
 //
 // Value pass (fp16 operands, fp32 accumulation; the softmax weights and value codewords are rounded
 // to fp16 once): R = 2 gathers both residual rows whole, sums them in fp16 and transposes each 4x4
@@ -50,11 +49,10 @@ namespace {
 
 constexpr int kW16 = 8;                              // waves per workgroup
 constexpr int kThreads16 = kW16 * 64;
-constexpr int kTab16 = kGroups * kCodes * 16;       // one residual codebook in LDS (fp16 rows of 8)
+
 constexpr int kPhaseBytes = kGroups * 2 * 64 * 16;  // fp32 fine phases [g][h][lane][2 pairs]
 constexpr int kSweep = 2;                            // blocks per key sweep
 constexpr int kValueLead = 4;                        // value records requested this many blocks ahead
-static_assert(2 * kTab16 + kPhaseBytes <= 160 * 1024, "codebook slots and phases fit the CU's LDS");
 
 // fp32 4x4x1 MFMA with the A operand broadcast from block ABID: acc[m] += A[lane 4 ABID + m] * b.
 template <int ABID>
@@ -189,14 +187,61 @@ __device__ __forceinline__ uint4 transpose_record(const uint4& r, int lane) {
                     __builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.w)));
 }
 
+// LDS map (bytes). Codebook rows are 16 bytes (8 fp16), 4 KiB per (residual, group).
+//   R = 2: region A [0, 64 KiB) holds groups 0-7 of both residuals (residual r at r x 32 KiB), the fp32 phases
+//          [64, 96 KiB), region B [96, 160 KiB) groups 8-15 (residual r at 96 KiB + r x 32 KiB). The key codebooks
+//          are replaced by the value codebooks half by half: region A once every wave is past group 7 of its last
+//          key unit, region B once the key pass is over.
+//   R = 1: key codebook [0, 64 KiB), phases [64, 96 KiB), value codebook [96, 160 KiB).
+// Offsets below 64 KiB go into the LDS instructions' offset field; region B and the R = 1 value codebook are
+// addressed from one base register (kHiBase), so a row address costs one or two VALU operations.
+constexpr int kKiB = 1024;
+// Staged (R = 2): the key pass starts once groups 0-7 have landed and the codebooks are swapped half by half
+// as above. Unstaged (R = 1): the prologue waits for every codebook. (Timed per launch on MI355X: staging saves
+// about 0.3 us at 8K tokens and is even at 128K for R = 2; for R = 1, whose value codebook is loaded up front
+// anyway, the extra barrier in the first key unit costs about 0.5 us at 128K.)
+template <int R>
+constexpr bool kStagedTables = R == 2;
+constexpr int kPhaseOff = 64 * kKiB;
+constexpr int kHiBase = 96 * kKiB;
+static_assert(kHiBase + 64 * kKiB <= 160 * kKiB, "codebooks and phases fit the CU's LDS");
+template <int R>
+constexpr int key_row_off(int r, int g) {
+  return R == 2 ? (g < 8 ? 0 : kHiBase) + r * 32 * kKiB + (g & 7) * 4 * kKiB : g * 4 * kKiB;
+}
+template <int R>
+constexpr int value_row_off(int r, int g) {
+  return R == 2 ? key_row_off<2>(r, g) : kHiBase + g * 4 * kKiB;
+}
+
+// Row idx of the table at LDS offset kOff (hi = kHiBase, held in a register).
+template <int kOff>
+__device__ __forceinline__ uint4 lds_row(const unsigned char* lds, int hi, uint32_t idx) {
+  if constexpr (kOff < kHiBase) {
+    return *reinterpret_cast<const uint4*>(lds + kOff + idx * 16);
+  } else {
+    return *reinterpret_cast<const uint4*>(lds + hi + (kOff - kHiBase) + idx * 16);
+  }
+}
+
+// Direct global->LDS copy of groups g0 .. g0 + kN - 1 of residual r's codebook [G][R][N][8] into LDS at dst
+// (4 KiB per group); every wave moves its share.
+template <int R, int kN>
+__device__ __forceinline__ void load_groups(const f16* cb_kv, int r, int g0, unsigned char* dst, int wave, int lane) {
+  constexpr int kPerWave = kN * kCodes / kW16;
+#pragma unroll
+  for (int i = 0; i < kPerWave / 64; ++i) {
+    const int c = wave * kPerWave + i * 64 + lane, g = g0 + (c >> 8), l = c & (kCodes - 1);
+    const f16* src = cb_kv + ((static_cast<int64_t>(g) * R + r) * kCodes + l) * kGroupDim;
+    __builtin_amdgcn_global_load_lds(src, dst + (wave * kPerWave + i * 64) * 16, 16, 0, 0);
+  }
+}
+
 template <int R>
 __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) {
   constexpr int kW = kW16;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTab16 + kPhaseBytes];
-  unsigned char* const slot0 = lds;
-  unsigned char* const slot1 = lds + kTab16;
-  const unsigned char* const phases = lds + 2 * kTab16;
-  // epilogue-only LDS (placed in the codebook slots, past the reduction buffer, once the passes are done)
+  __shared__ __attribute__((aligned(16))) unsigned char lds[160 * kKiB];
+  // epilogue-only LDS (in region A, past the reduction buffer, once the passes are done)
   auto& wave_ml = *reinterpret_cast<float(*)[2][kW][kGqa]>(lds + kW * kHeadDim * kGqa * sizeof(float));
   int& is_last = *reinterpret_cast<int*>(lds + kW * kHeadDim * kGqa * sizeof(float) + sizeof(wave_ml));
 
@@ -214,21 +259,18 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   const int64_t seq_start = sb.start;
 
   // ---------------------------------------------------------------------------------- prologue
-  // (1) Key codebooks (R = 1: and the value codebook) and the fp32 fine phases, straight into LDS. They depend
-  // only on the KV head, so they go out first.
-  load_table<f16, R, kW>(cb_k, 0, slot0, wave, lane);
-  if constexpr (R == 2) {
-    load_table<f16, R, kW>(cb_k, 1, slot1, wave, lane);
-  } else {
-    load_table<f16, R, kW>(cb_v, 0, slot1, wave, lane);
-  }
+  // (1) The key codebook rows of groups 0-7 and the fp32 fine phases, straight into LDS; they depend only on the
+  // KV head, so they go out first. Groups 8-15 (and the R = 1 value codebook) follow the first records and land
+  // while the first key unit works on groups 0-7.
+  load_groups<R, 8>(cb_k, 0, 0, lds + key_row_off<R>(0, 0), wave, lane);
+  if constexpr (R == 2) load_groups<R, 8>(cb_k, 1, 0, lds + key_row_off<R>(1, 0), wave, lane);
   {
     constexpr int kChunks = kPhaseBytes / 16;
     const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine32gOffset);
 #pragma unroll
     for (int i = 0; i < kChunks / kThreads16; ++i) {
       const int c = (wave * (kChunks / kThreads16) + i) * 64;
-      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, const_cast<unsigned char*>(phases) + c * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, lds + kPhaseOff + c * 16, 16, 0, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -286,8 +328,35 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
 #pragma unroll
   for (int i = 0; i < kSweep; ++i) request(a.k_codes, i);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-  slot_barrier();  // every wave's codebook and phase loads have landed
+  // (4) Key rows of groups 8-15 (and the R = 1 value codebook): published by the barrier before any wave reads
+  // group 8 (publish_hi below).
+  load_groups<R, 8>(cb_k, 0, 8, lds + key_row_off<R>(0, 8), wave, lane);
+  if constexpr (R == 2) {
+    load_groups<R, 8>(cb_k, 1, 8, lds + key_row_off<R>(1, 8), wave, lane);
+  } else {
+    load_groups<R, 16>(cb_v, 0, 0, lds + value_row_off<R>(0, 0), wave, lane);
+  }
+  constexpr int kHiLoads = kStagedTables<R> ? (R == 2 ? 2 * 8 : 8 + 16) * kCodes / kThreads16 : 0;
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kHiLoads));
+  slot_barrier();  // every wave's groups 0-7, phases, query, coarse rows and first records have landed
+  // Publishes the loads issued in (4): each wave waits for its own (n = loads it has issued since), then the
+  // barrier. Called once by every wave, before its first read of group 8.
+  auto publish_hi = [&](auto nc) {
+    if constexpr (kStagedTables<R>) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_at_most(decltype(nc)::value));
+      slot_barrier();
+    }
+  };
+  // R = 2: once every wave is past group 7 of its last key unit, region A is refilled with the value rows of
+  // groups 0-7. Called once by every wave.
+  auto refill_lo = [&]() {
+    if constexpr (R == 2) {
+      slot_barrier();
+      load_groups<R, 8>(cb_v, 0, 0, lds + value_row_off<R>(0, 0), wave, lane);
+      load_groups<R, 8>(cb_v, 1, 0, lds + value_row_off<R>(1, 0), wave, lane);
+    }
+  };
 
   // A operands. q'' = q * conj(e^{i 64 c theta}) for the block's coarse row c, in fp32: qc0 for the wave's
   // first block; stepE = e^{i 512 theta} (row 1 squared three times: the wave's blocks are 8 rows apart)
@@ -303,16 +372,25 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
     for (int sq = 0; sq < 3; ++sq) e = make_float2(e.x * e.x - e.y * e.y, 2.f * e.x * e.y);
     stepE[k] = e;
   }
+  // base registers: kHiBase, and this lane's phase column (the fp32 phases of pairs 4g + 2h, 4g + 2h + 1 at
+  // lane f sit at kPhaseOff + ((2g + h) * 64 + f) * 16)
+  int hi = kHiBase, ph_lane = kPhaseOff + lane * 16;
+  asm volatile("" : "+v"(hi), "+v"(ph_lane));
 
   // ------------------------------------------------------------------------------ key pass
   const h4 ident = identity_b(lane);  // identity MFMA operand (residual sums, transposes)
   f4 sc[kMaxBlocks];
 #pragma unroll
   for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
-  const unsigned char* const ktab1 = R == 2 ? slot1 : slot0;
-  auto load_phases = [&](int g, float4 (&dst)[2]) {
-    dst[0] = *reinterpret_cast<const float4*>(phases + ((2 * g) * 64 + lane) * 16);
-    dst[1] = *reinterpret_cast<const float4*>(phases + ((2 * g + 1) * 64 + lane) * 16);
+  auto load_phases = [&](auto gc, float4 (&dst)[2]) {
+    constexpr int g = decltype(gc)::value;
+    dst[0] = *reinterpret_cast<const float4*>(lds + ph_lane + (2 * g) * 1024);
+    dst[1] = *reinterpret_cast<const float4*>(lds + ph_lane + (2 * g + 1) * 1024);
+  };
+  auto key_rows = [&](auto gc, const uint4& c0, const uint4& c1, uint4 (&dst)[2]) {
+    constexpr int g = decltype(gc)::value;
+    dst[0] = lds_row<key_row_off<R>(0, g)>(lds, hi, code_index(c0, g));
+    if constexpr (R == 2) dst[1] = lds_row<key_row_off<R>(1, g)>(lds, hi, code_index(c1, g));
   };
   // One sweep: groups 0..15 over blocks kSweep s, kSweep s + 1. Per group the two rotations run as one VALU burst,
   // then the next group's gathers and phases go out (the rows are consumed), then the 16 MFMAs as one burst over two
@@ -326,13 +404,15 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
     auto issue = [&](auto gc) {
       constexpr int g = decltype(gc)::value;
       if constexpr (g < kGroups) {
-        load_phases(g, ph);
+        load_phases(gc, ph);
 #pragma unroll
-        for (int ii = 0; ii < kSweep; ++ii) {
-          rows[ii][0] = gather_row<g>(slot0, code[kSweep * s + ii]);
-          if constexpr (R == 2) rows[ii][1] = gather_row<g>(ktab1, code1[kSweep * s + ii]);
-        }
+        for (int ii = 0; ii < kSweep; ++ii) key_rows(gc, code[kSweep * s + ii], code1[kSweep * s + ii], rows[ii]);
       }
+    };
+    // before group 8's rows: sweep 0 publishes the high rows; the last sweep hands region A to the value rows
+    auto at_group8 = [&]() {
+      if constexpr (s == 0) publish_hi(std::integral_constant<int, kSweep * R>{});
+      if constexpr (s == kMaxBlocks / kSweep - 1) refill_lo();
     };
     f4 acc[2 * kSweep];  // two chains per block, folded into sc at the end of the sweep
 #pragma unroll
@@ -358,6 +438,7 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
 #pragma unroll
         for (int ii = 0; ii < kSweep; ++ii) rotate_f16(rows[ii][0], ph[0], ph[1], w[ii]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (g == 7) at_group8();
         issue(std::integral_constant<int, g + 1>{});  // the rows are consumed
         __builtin_amdgcn_sched_barrier(0);
       } else {
@@ -368,6 +449,7 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
 #pragma unroll
         for (int ii = 0; ii < kSweep; ++ii) sum_rows(rows[ii][0], rows[ii][1], ident, ksum[ii]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (g == 7) at_group8();
         issue(std::integral_constant<int, g + 1>{});
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -392,9 +474,8 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
       auto issue = [&](auto gc) {
         constexpr int g = decltype(gc)::value;
         if constexpr (g < kGroups) {
-          load_phases(g, ph);
-          rows[0] = gather_row<g>(slot0, code[i]);
-          if constexpr (R == 2) rows[1] = gather_row<g>(ktab1, code1[i]);
+          load_phases(gc, ph);
+          key_rows(gc, code[i], code1[i], rows);
         }
       };
       issue(std::integral_constant<int, 0>{});
@@ -404,6 +485,10 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
         float w[1][8];
         rotate_key<R>(rows[0], rows[1], ph[0], ph[1], ident, w[0]);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (g == 7) {
+          if constexpr (i == 0) publish_hi(std::integral_constant<int, (kMaxBlocks - kSweep) * R>{});
+          if (i == my_blocks - 1) refill_lo();
+        }
         issue(std::integral_constant<int, g + 1>{});
         __builtin_amdgcn_sched_barrier(0);
         const float2 A1[1] = {curA[g / 4]};
@@ -436,16 +521,21 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   } else {
 #pragma unroll
     for (int i = kSweep; i < kMaxBlocks; ++i) request(a.k_codes, i);
+    if (my_blocks == 0) {  // a wave without tokens still takes part in both hand-overs
+      publish_hi(std::integral_constant<int, (kMaxBlocks - kSweep) * R>{});
+      refill_lo();
+    }
     static_for<kMaxBlocks>(single);
   }
   __builtin_amdgcn_s_setprio(0);
 
-  // R = 2: once every wave is done with the key codebooks, both slots are refilled with the value codebooks
-  // (direct-to-LDS; no LDS read happens until they have landed).
+  // R = 2: once every wave is done with the key rows of groups 8-15 (and its region A value loads have landed),
+  // region B is refilled with the value rows of groups 8-15; they are published inside the value pass.
   if constexpr (R == 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     slot_barrier();
-    load_table<f16, R, kW>(cb_v, 0, slot0, wave, lane);
-    load_table<f16, R, kW>(cb_v, 1, slot1, wave, lane);
+    load_groups<R, 8>(cb_v, 0, 8, lds + value_row_off<R>(0, 8), wave, lane);
+    load_groups<R, 8>(cb_v, 1, 8, lds + value_row_off<R>(1, 8), wave, lane);
   }
 
   // ------------------------------------------------------------------------------ wave softmax
@@ -459,48 +549,66 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
 #pragma unroll
     for (int i = 0; i < kMaxBlocks; ++i) pt[i] = to_h4(mfma(to_h4(sc[i]), ident, z));
   }
-  if constexpr (R == 2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-    lds_barrier();  // both value codebooks complete
-  }
 
   // ------------------------------------------------------------------------------ value pass
   f4 O[2 * kGroups];
 #pragma unroll
   for (int c = 0; c < 2 * kGroups; ++c) O[c] = (f4){0.f, 0.f, 0.f, 0.f};
   if constexpr (R == 2) {
-    // per group pair, the four rows of both residuals go out ahead of the previous pair's arithmetic
-    uint4 rows[kBufs][2][2];  // [buffer][group of the pair][residual]
+    // Units are (block, group pair); pairs 0-3 read region A, pairs 4-7 region B. Order: blocks 0 and 1 on pairs
+    // 0-3, then (region B published) blocks 0 and 1 on pairs 4-7, then blocks 2..7 whole. Per unit the four rows of
+    // both residuals go out kAhead units ahead of the arithmetic.
     constexpr int kPairsPerBlock = kGroups / 2;
-    auto issue = [&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      if constexpr (m < kPairsPerBlock * kMaxBlocks)
-        gather_pair2<m % kPairsPerBlock>(slot0, slot1, code[m / kPairsPerBlock], code1[m / kPairsPerBlock],
-                                         rows[m % kBufs]);
+    constexpr int kUnits = kPairsPerBlock * kMaxBlocks;
+    constexpr int kLoUnits = 2 * kPairsPerBlock / 2;  // units before the region B hand-over
+    auto unit_block = [](int u) {
+      return u < 2 * kPairsPerBlock ? (u % kPairsPerBlock) / (kPairsPerBlock / 2) : u / kPairsPerBlock;
+    };
+    auto unit_pair = [](int u) {
+      return u < 2 * kPairsPerBlock ? (u / kPairsPerBlock) * (kPairsPerBlock / 2) + u % (kPairsPerBlock / 2)
+                                    : u % kPairsPerBlock;
+    };
+    uint4 rows[kBufs][2][2];  // [buffer][group of the pair][residual]
+    auto issue = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      if constexpr (u < kUnits) {
+        constexpr int i = unit_block(u), p = unit_pair(u);
+        rows[u % kBufs][0][0] = lds_row<value_row_off<R>(0, 2 * p)>(lds, hi, code_index(code[i], 2 * p));
+        rows[u % kBufs][0][1] = lds_row<value_row_off<R>(1, 2 * p)>(lds, hi, code_index(code1[i], 2 * p));
+        rows[u % kBufs][1][0] = lds_row<value_row_off<R>(0, 2 * p + 1)>(lds, hi, code_index(code[i], 2 * p + 1));
+        rows[u % kBufs][1][1] = lds_row<value_row_off<R>(1, 2 * p + 1)>(lds, hi, code_index(code1[i], 2 * p + 1));
+      }
     };
     if (my_blocks > 0) static_for<kAhead>(issue);
-    static_for<kMaxBlocks>([&](auto ic) {
-      constexpr int i = decltype(ic)::value;
-      __builtin_amdgcn_s_setprio(block_prio(i));
-      if constexpr (i + kValueLead < kMaxBlocks) request(a.v_codes, i + kValueLead);
+    static_for<kUnits>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int i = unit_block(u), p = unit_pair(u);
+      // a block's value records: block i asks for those of block i + kValueLead when it starts
+      constexpr bool kFirstOfBlock = u < 2 * kPairsPerBlock ? u % kPairsPerBlock == 0 || u == kPairsPerBlock / 2
+                                                            : u % kPairsPerBlock == 0;
+      if constexpr (kFirstOfBlock && i + kValueLead < kMaxBlocks) request(a.v_codes, i + kValueLead);
+      if constexpr (u == kLoUnits) {
+        // region B: each wave's value loads (issued before the records of blocks 4 and 5), then the barrier
+        publish_hi(std::integral_constant<int, 2 * R>{});
+        if (my_blocks > 0) static_for<kAhead>([&](auto jc) { issue(std::integral_constant<int, u + decltype(jc)::value>{}); });
+      }
       if (i < my_blocks) {
-        static_for<kPairsPerBlock>([&](auto pc) {
-          constexpr int n = kPairsPerBlock * i + decltype(pc)::value;
-          __builtin_amdgcn_sched_barrier(0);
-          issue(std::integral_constant<int, n + kAhead>{});
-          __builtin_amdgcn_sched_barrier(0);
-          value_pair2<n % kPairsPerBlock>(rows[n % kBufs], ident, pt[i], O);
-        });
+        __builtin_amdgcn_s_setprio(block_prio(u / kPairsPerBlock));
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (u + kAhead < kLoUnits || u >= kLoUnits) issue(std::integral_constant<int, u + kAhead>{});
+        __builtin_amdgcn_sched_barrier(0);
+        value_pair2<p>(rows[u % kBufs], ident, pt[i], O);
       }
     });
   } else {
+    const unsigned char* vtab = lds + hi;
     uint4 rows[kBufs][4];  // gathered rows of quarters n .. n + kAhead
     uint4 vrec[kMaxBlocks];  // value records moved to the transposed lanes
     auto issue = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
       if constexpr (m < 4 * kMaxBlocks) {
         if constexpr (m % 4 == 0) vrec[m / 4] = transpose_record(code[m / 4], lane_id());
-        gather_quarter_tr<m % 4>(slot1, vrec[m / 4], rows[m % kBufs]);
+        gather_quarter_tr<m % 4>(vtab, vrec[m / 4], rows[m % kBufs]);
       }
     };
     if (my_blocks > 0) static_for<kAhead>(issue);
