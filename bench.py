@@ -7,9 +7,14 @@ unpack, RoPE phases, key scores, split softmax, value reduce, combine) on the Ll
 layer's codes, codebooks and query (>= 1 GiB in total) so the 256 MB Infinity Cache cannot serve
 the code stream. Inputs are synthetic (workloads.make_inputs) and resident in HBM before timing.
 
-Prints one JSON line. The timed region is K steps between two device synchronizations; the
-per-launch kernel duration for the roofline comes from HIP events recorded on the launch stream.
-cpu_baseline times the fp64 oracle on the host on a bounded sample of the same workload.
+Before anything is timed, every layer copy is launched once and the workload runs for 1 s (untimed), so that
+buffers have been touched and the GPU clocks have settled; then the W warmup steps. The timed region is K
+back-to-back steps between two device synchronizations, bracketed by HIP events on the launch stream: its
+average is the kernel's duration for the roofline (rocprofv3's kernel trace of the same command agrees).
+Each launch is also timed alone between its own two events (us_per_launch_isolated, an upper bound: the
+events add a few microseconds). Measurement probes (libcommvq_probes.so) give the HBM read rate a plain
+streaming kernel reaches and the LDS random-gather ceiling. cpu_baseline times the fp64 oracle on the host
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -31,30 +36,44 @@ import workloads  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 # LDS: 256 CUs x 256 B per clock x 2.4 GHz (a broadcast ds_read_b128 wave instruction, 1 KiB, takes 4 clocks
-# per CU); random 16-byte gathers measured at 12.04 clocks per 1 KiB wave instruction (bank conflicts)
+# per CU). The random 16-byte gathers the kernels make run slower (bank conflicts): their ceiling is measured
+# live by commvq_probe_lds_gather (lds_gather_probe below).
 LDS_PEAK_TBPS = 256 * 256 * 2.4e9 / 1e12
-LDS_GATHER_TBPS = 256 * 1024 / 12.04 * 2.4e9 / 1e12
+CLOCK_GHZ = 2.4
+# MI355X fp32 vector peak as published (it counts packed fp32 instructions, which this build does not use:
+# without them the VALU fp32 rate is half, 78.6 TFLOP/s)
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 PROFILES = os.path.join(ROOT, "profiles")
-# sources that determine each attention kernel's memory traffic (split sizing, layout, kernel body)
+# the attention kernel of each workload family, as rocprofv3 names it, and the sources that determine it
 _CSRC = os.path.join(ROOT, "vector_quantized_kv_amd", "csrc")
-KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
-                  ("attn.hip", "attn_common.h", "commvq_internal.h", "device_common.h", "api.cpp")]
-WIDE_KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in
-                       ("attn_wide.hip", "attn_common.h", "commvq_internal.h", "device_common.h", "api.cpp")]
-KERNEL_NAME = "attn_kernel"
+_COMMON = ("attn_common.h", "commvq_internal.h", "device_common.h", "api.cpp")
+KERNELS = {
+    "f16": ("attn_f16_kernel", [os.path.join(_CSRC, f) for f in ("attn_f16.hip",) + _COMMON]),
+    "f32": ("attn_f32_kernel", [os.path.join(_CSRC, f) for f in ("attn.hip",) + _COMMON]),
+    "wide": ("attn_wide_kernel", [os.path.join(_CSRC, f) for f in ("attn_wide.hip",) + _COMMON]),
+}
 
 
-def kernel_source_hash(sources=None) -> str:
+def kernel_kind(cfg) -> str:
+    return "wide" if cfg.packed else ("f16" if cfg.dtype == "float16" else "f32")
+
+
+def kernel_label(cfg) -> str:
+    name = KERNELS[kernel_kind(cfg)][0]
+    return name if cfg.packed else f"{name}<{cfg.n_residuals}>"
+
+
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for p in sources or KERNEL_SOURCES:
+    for p in KERNELS[kind][1]:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(config_name: str, sources=None):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches the current kernels."""
-    path = os.path.join(PROFILES, f"traffic_attn_decode_{config_name}.txt")
+def read_traffic(cfg):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it matches the current kernel."""
+    path = os.path.join(PROFILES, f"traffic_attn_decode_{cfg.name}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -63,7 +82,7 @@ def read_traffic(config_name: str, sources=None):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources):
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(kernel_kind(cfg)):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -81,6 +100,19 @@ def algorithmic_bytes(cfg, total_tokens: int) -> dict:
     return {"codes": codes, "codebooks": codebooks, "q_out": q + out, "total": codes + codebooks + q + out}
 
 
+def host_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(), "cpus_available": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(cfg, inp, budget_s: float = 12.0) -> dict:
     import oracle
     cores = len(os.sched_getaffinity(0))
@@ -95,32 +127,99 @@ def cpu_baseline(cfg, inp, budget_s: float = 12.0) -> dict:
         if t_total * threads >= budget_s or runs >= 20:
             break
     per_run = t_total / runs
-    return {"value": d_tokens / per_run, "unit": "KV tokens/s per layer", "cores": threads, "kind": "oracle",
-            "sample": f"{runs} full decode steps of one layer ({cfg.name}: {d_tokens} tokens x "
-                      f"{cfg.n_kv_heads} KV heads), fp64, {threads} host threads; {per_run:.3f} s per step"}
+    res = {"value": d_tokens / per_run, "unit": "KV tokens/s per layer", "cores": threads, "kind": "oracle",
+           "sample": f"{runs} full decode steps of one layer ({cfg.name}: {d_tokens} tokens x "
+                     f"{cfg.n_kv_heads} KV heads), fp64, {threads} host threads; {per_run:.3f} s per step"}
+    res.update(host_info())
+    # the same oracle on one thread, on the small workloads the tests use
+    single = {}
+    for name in ("tiny_1k_r2_f32", "llama8b_8k_r2"):
+        c = workloads.CONFIGS[name]
+        x = workloads.make_inputs(c)
+        t0 = time.perf_counter()
+        oracle.run_config(c, x, n_threads=1)
+        dt = time.perf_counter() - t0
+        single[name] = {"s_per_step": dt, "kv_tokens_per_s": int(x["total_tokens"]) / dt}
+    res["single_thread"] = single
+    return res
 
 
-def read_stream_gbps(nbytes: int = 1 << 30, reps: int = 10) -> float:
-    """Achievable HBM read rate on this machine: torch.sum over a 1 GiB fp32 tensor (one read pass each)."""
+def probes_lib():
+    import ctypes
+    from vector_quantized_kv_amd import build as vbuild
+    L = ctypes.CDLL(vbuild.PROBES_LIB)
+    L.commvq_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+    L.commvq_probe_lds_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return L
+
+
+def settle(launch, seconds: float = 1.0):
+    """Keeps the GPU busy with `launch` for `seconds` of wall time (untimed): the device raises its clocks
+    over the first tens of milliseconds of load, and a kernel timed before that runs up to 15% slower."""
     import torch
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        x.sum()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        launch(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def _timed_ms(fn, reps: int) -> float:
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        x.sum()
+        fn()
     b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    del x
-    return nbytes / (ms * 1e-3) * 1e-9
+    return a.elapsed_time(b) / reps
+
+
+def read_stream_probe(nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """HBM read rate a plain streaming kernel reaches on this device (commvq_probe_read_stream: 16-byte
+    non-temporal loads, 2048 workgroups of 256 threads, over a 1 GiB buffer)."""
+    import torch
+    L = probes_lib()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        assert L.commvq_probe_read_stream(buf.data_ptr(), nbytes, 2048, sink.data_ptr(), s) == 0
+    settle(lambda i: run(), 0.5)
+    ms = _timed_ms(run, reps)
+    del buf
+    return {"GBps": nbytes / (ms * 1e-3) * 1e-9, "bytes": nbytes, "kernel": "read_stream_kernel"}
+
+
+def lds_gather_probe(iters: int = 256, blocks: int = 1024, reps: int = 5) -> dict:
+    """Random 16-byte LDS row gathers (commvq_probe_lds_gather: one workgroup of 8 waves per CU, each wave
+    gathering from a 64 KiB table of 16 groups x 256 rows, a random row per lane): the ceiling of the
+    attention kernels' codebook reads."""
+    import torch
+    L = probes_lib()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        assert L.commvq_probe_lds_gather(iters, blocks, sink.data_ptr(), s) == 0
+    settle(lambda i: run(), 0.5)
+    ms = _timed_ms(run, reps)
+    gathers = blocks * 8 * iters * 16  # wave instructions, 1 KiB each
+    tbps = gathers * 1024 / (ms * 1e-3) * 1e-12
+    return {"TBps": tbps, "clk_per_wave_gather_per_cu_at_2.4GHz": 256 * 1024 * CLOCK_GHZ * 1e9 / (tbps * 1e12),
+            "kernel": "lds_gather_kernel", "gathers": gathers}
 
 
 def profile_run(names, launches: int):
-    """Few launches per workload (for rocprofv3), plus a 1 GiB device copy whose FETCH_SIZE / WRITE_SIZE
-    calibrate the counters (it reads and writes exactly 1 GiB)."""
+    """Few launches per workload (for rocprofv3), after one setup launch per layer copy, plus a 1 GiB device copy
+    whose FETCH_SIZE / WRITE_SIZE calibrate the counters (it reads and writes exactly 1 GiB), plus the probes."""
     import torch
     import vector_quantized_kv_amd as vq
     for name in names:
@@ -132,10 +231,20 @@ def profile_run(names, launches: int):
         rope = vq.rope_table(d, int(base["max_len"]))
         Ls = [vq.Layer(d, base if i == 0 else workloads.make_inputs(cfg, seed=cfg.seed + 1000 * i), rope=rope,
                        rope_positions=int(base["max_len"])) for i in range(layers)]
-        for i in range(launches):
-            Ls[i % layers].attn_decode()
+        for ly in Ls:  # every layer copy once (setup; also the first touch of its buffers)
+            ly.attn_decode()
         torch.cuda.synchronize()
-        print(f"profile: {name} {launches} launches over {layers} layer copies", flush=True)
+        settle(lambda i: Ls[i % layers].attn_decode())
+        # as bench.py times launches: each between two HIP events on the launch stream
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for i in range(launches):
+            ev[i][0].record(stream)
+            Ls[i % layers].attn_decode()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        print(f"profile: {name} {layers} setup launches, 1 s of launches, then {launches} launches over {layers} "
+              "layer copies", flush=True)
         del Ls
         torch.cuda.empty_cache()
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -144,9 +253,14 @@ def profile_run(names, launches: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print("profile: 3 copies of 1 GiB (calibration)", flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
+    read_stream_probe(reps=3)
+    lds_gather_probe(reps=3)
+    print("profile: probes (read stream and LDS gathers: 0.5 s of launches, then 1 + 3 more each)", flush=True)
 
 
-def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check: bool):
+def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check: bool, gather_tbps: float):
     import torch
     import vector_quantized_kv_amd as vq
 
@@ -173,6 +287,12 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
         check_err = float((np.abs(got - ref).max(-1) / np.abs(ref).max(-1)).max())
 
     stream = torch.cuda.current_stream()
+    # setup (untimed): every rotated layer copy is launched once (first touch of its buffers), then the workload
+    # runs for 1 s so that the GPU clocks have settled, then the W warmup steps
+    for ly in Ls:
+        ly.attn_decode()
+    torch.cuda.synchronize()
+    settle(lambda i: Ls[i % layers].attn_decode())
     for i in range(warmup):
         Ls[i % layers].attn_decode()
     torch.cuda.synchronize()
@@ -188,7 +308,8 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
 
-    # per-launch kernel duration for the roofline: HIP events on the launch stream around each call
+    # each launch alone between its own two events: an upper bound on the kernel's duration (the events add
+    # their own per-launch work, a few microseconds); reported beside the timed region's average
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
@@ -222,17 +343,20 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
         torch.cuda.synchronize()
         graph_ms = a.elapsed_time(b) / (reps * layers)
 
+    # the kernel's average duration (one launch per step): the timed region over K, HIP events on the launch
+    # stream (rocprofv3's kernel trace of the same command agrees with it)
     per_step_ms = total_ms / steps
-    print(f"[bench] {cfg.name}: {layers} layers, {launch_ms * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
+    print(f"[bench] {cfg.name}: {layers} layers, {per_step_ms * 1e3:.1f} us per step ({launch_ms * 1e3:.1f} us per "
+          "launch timed alone)", file=sys.stderr, flush=True)
     L = total
     res = {
         "config": cfg.name, "tokens": L, "layers_rotated": layers, "ms_per_step": per_step_ms,
-        "us_per_layer_eager": per_step_ms * 1e3, "us_per_launch": launch_ms * 1e3,
+        "us_per_layer_eager": per_step_ms * 1e3, "us_per_launch_isolated": launch_ms * 1e3,
         "us_per_layer_graph": None if graph_ms is None else graph_ms * 1e3,
         "kv_tokens_per_s_per_layer": L / (per_step_ms * 1e-3),
-        "code_stream_GBps": per_layer["codes"] / (launch_ms * 1e-3) * 1e-9,
-        "compulsory_GBps": per_layer["total"] / (launch_ms * 1e-3) * 1e-9,
-        "pct_hbm_peak_code_stream": 100.0 * per_layer["codes"] / (launch_ms * 1e-3) * 1e-9 / HBM_PEAK_GBPS,
+        "code_stream_GBps": per_layer["codes"] / (per_step_ms * 1e-3) * 1e-9,
+        "compulsory_GBps": per_layer["total"] / (per_step_ms * 1e-3) * 1e-9,
+        "pct_hbm_peak_code_stream": 100.0 * per_layer["codes"] / (per_step_ms * 1e-3) * 1e-9 / HBM_PEAK_GBPS,
         "bytes": per_layer, "max_row_rel_err_vs_oracle": check_err,
     }
     # Every token gathers, per residual and group, its codeword row from LDS for keys and again for values
@@ -240,13 +364,13 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
     # kernels. The whole launch, fixed costs included, is counted against it.
     gathered = 2 * cfg.n_kv_heads * L * cfg.n_residuals * cfg.n_groups * cfg.group_dim * \
         (2 if cfg.dtype == "float16" else 4)
-    tbps = gathered / (launch_ms * 1e-3) * 1e-12
+    tbps = gathered / (per_step_ms * 1e-3) * 1e-12
     res["lds_roofline"] = {"bound": "lds", "gathered_bytes_per_launch": gathered, "achieved": tbps,
                            "unit": "TB/s", "peak": LDS_PEAK_TBPS, "frac": tbps / LDS_PEAK_TBPS,
-                           "random_gather_ceiling": LDS_GATHER_TBPS,
-                           "frac_of_random_gather_ceiling": tbps / LDS_GATHER_TBPS}
-    if cfg.packed:
-        res["hbm_traffic_bytes_per_launch"] = read_traffic(cfg.name, WIDE_KERNEL_SOURCES)
+                           "random_gather_ceiling": gather_tbps,
+                           "frac_of_random_gather_ceiling": tbps / gather_tbps}
+    res["kernel"] = kernel_label(cfg)
+    res["hbm_traffic_bytes_per_launch"] = read_traffic(cfg)
     del Ls
     torch.cuda.empty_cache()
     return res, base
@@ -292,15 +416,16 @@ def codebook_tools_timing(reps: int = 3):
     encb_flops = float(Hkv) * n * 2 * Rb * 64 * 64 * 3
     return {
         "shape": f"{n} tokens x {Hkv} KV heads, R={R}, fp16",
-        # the library is built without packed-fp32 instructions, so its fp32 VALU peak is half the published
-        # 157.3 TFLOP/s: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz = 78.6 TFLOP/s
+        # against the published fp32 vector peak (157.3 TFLOP/s, which assumes packed fp32 instructions; this
+        # build does not use them, so 0.5 is the most it can reach)
         "encode_greedy": {"ms": t_enc * 1e3, "tokens_per_s": n / t_enc, "bound": "alu",
-                          "achieved_tflops": enc_flops / t_enc * 1e-12, "peak_tflops": 78.6,
-                          "frac": enc_flops / t_enc * 1e-12 / 78.6},
+                          "achieved_tflops": enc_flops / t_enc * 1e-12, "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+                          "frac": enc_flops / t_enc * 1e-12 / FP32_VECTOR_PEAK_TFLOPS},
         "codebook_update": {"ms": t_upd * 1e3, "tokens_per_s": n / t_upd},
         "encode_greedy_bit_packed_r21": {"ms": t_encb * 1e3, "tokens_per_s": n / t_encb, "bound": "alu",
-                                         "achieved_tflops": encb_flops / t_encb * 1e-12, "peak_tflops": 78.6,
-                                         "frac": encb_flops / t_encb * 1e-12 / 78.6},
+                                         "achieved_tflops": encb_flops / t_encb * 1e-12,
+                                         "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+                                         "frac": encb_flops / t_encb * 1e-12 / FP32_VECTOR_PEAK_TFLOPS},
         "codebook_update_bit_packed_r21": {"ms": t_updb * 1e3, "tokens_per_s": n / t_updb},
     }
 
@@ -318,6 +443,137 @@ PAGES_CONTEXT = {
 }
 
 
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    paths = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not paths:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(paths[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _dispatches(rows, value_key=None):
+    """[(kernel name, value or duration ns)] in dispatch order, one entry per dispatch."""
+    out = {}
+    for r in rows:
+        did = int(r.get("Dispatch_Id") or r.get("Dispatch_ID") or r.get("Correlation_Id"))
+        name = r["Kernel_Name"]
+        if value_key is None:
+            v = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        else:
+            v = float(r[value_key])
+            if did in out:
+                v += out[did][1]  # a counter summed over its instances
+        out[did] = (name, v)
+    return [out[k] for k in sorted(out)]
+
+
+PROFILE_LAUNCHES = 20  # launches per workload in the bench.py --profile runs the summaries are made from
+
+
+def write_profiles(bench_kt_dir: str, kt_dir: str, fetch_dir: str, write_dir: str, bench_steps: int):
+    """profiles/ summaries. (1) rocprofv3 --kernel-trace --stats of the bench command for the headline workload:
+    the --stats line of its kernel and the average of the last `bench_steps` dispatches (the launches bench.py
+    times one by one between HIP events, for the roofline). (2) Three rocprofv3 runs of `bench.py --profile
+    --steps 20`: per workload the attention dispatches (duration from the kernel trace; FETCH_SIZE and WRITE_SIZE
+    per dispatch scaled by what the same counters read for the run's 1 GiB device copies), and the probes."""
+    launches = PROFILE_LAUNCHES
+    names = ["llama8b_128k_r2"] + [n for n in PROFILE_ALSO if n != "llama8b_128k_r2"]
+    cfgs = [workload(n) for n in names]
+    trace = _dispatches(_csv_rows(kt_dir, "kernel_trace.csv"))
+    fetch = _dispatches(_csv_rows(fetch_dir, "counter_collection.csv"), "Counter_Value")
+    write = _dispatches(_csv_rows(write_dir, "counter_collection.csv"), "Counter_Value")
+
+    def copies(seq):
+        return [x for x in seq if "copyBuffer" in x[0]][-3:]
+
+    tokens = {c.name: sum(c.lengths) for c in cfgs}  # (the profiled workloads have fixed lengths)
+
+    def per_workload(seq):
+        # each workload starts with its RoPE table (one rope_table_kernel dispatch); its profiled launches are the
+        # last `launches` attention dispatches before the next workload
+        segs, cur = [], None
+        for x in seq:
+            if "rope_table_kernel" in x[0]:
+                cur = []
+                segs.append(cur)
+            elif cur is not None and "attn_" in x[0] and "_kernel" in x[0]:
+                cur.append(x)
+        assert len(segs) == len(cfgs), (len(segs), len(cfgs))
+        return {c.name: seg[-launches:] for c, seg in zip(cfgs, segs)}
+    kt, fe, wr = per_workload(trace), per_workload(fetch), per_workload(write)
+    fscale = 1048576.0 / np.mean([v for _, v in copies(fetch)])
+    wscale = 1048576.0 / np.mean([v for _, v in copies(write)])
+    cmd_kt = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/kt -o kt --output-format csv -- "
+              f"python3 /root/repo/bench.py --profile --steps {launches}")
+    lines = ["# rocprofv3 kernel statistics: decode attention kernels and measurement probes", "",
+             "Command (one GPU, committed files only):", "", "    " + cmd_kt, "",
+             f"bench.py --profile launches every layer copy of each workload once (setup), keeps the workload running "
+             f"for 1 s (the GPU clocks settle), then times {launches} launches rotating over >= 1 GiB of layer copies "
+             "(the code stream comes from HBM; each launch between two HIP events, as bench.py times them); then three "
+             "1 GiB device copies and the two probes. Summary written by `bench.py --write-profiles`.", "",
+             "| workload | kernel | source sha256/16 | dispatches | average us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for c in cfgs:
+        d = np.array([v for _, v in kt[c.name]]) * 1e-3
+        lines.append(f"| {c.name} | {kernel_label(c)} | {kernel_source_hash(kernel_kind(c))} | {len(d)} | "
+                     f"{d.mean():.2f} | {d.min():.2f} | {d.max():.2f} |")
+    probes = [(n, v) for n, v in trace if "read_stream_kernel" in n or "lds_gather_kernel" in n]
+    lines += ["", "| probe | dispatches | average us | what it measures |", "|---|---|---|---|"]
+    for key, what in (("read_stream_kernel", "1 GiB streaming read: HBM read rate = 1 GiB / duration"),
+                      ("lds_gather_kernel", "1024 WGs x 8 waves x 256 x 16 random 16-byte LDS gathers (1 KiB per "
+                                            "wave instruction): gather ceiling = bytes / duration")):
+        d = np.array([v for n, v in probes if key in n]) * 1e-3
+        if d.size:
+            lines.append(f"| {key} | {len(d)} | {d.mean():.2f} | {what} |")
+    # (1) the bench command itself
+    prim = workloads.CONFIGS["llama8b_128k_r2"]
+    label = kernel_label(prim)
+    stats = [r for r in _csv_rows(bench_kt_dir, "kernel_stats.csv") if f"attn_f16_kernel<{prim.n_residuals}>" in r["Name"]]
+    btrace = [v for n, v in _dispatches(_csv_rows(bench_kt_dir, "kernel_trace.csv"))
+              if f"attn_f16_kernel<{prim.n_residuals}>" in n]
+    timed = np.array(btrace[-bench_steps:]) * 1e-3
+    cmd_b = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/bench -o bench --output-format csv -- "
+             f"python3 /root/repo/bench.py --also '' --no-graph --no-cpu-baseline --steps {bench_steps}")
+    head = ["# rocprofv3 kernel statistics: decode attention kernels and measurement probes", "",
+            f"## The bench command ({prim.name}, {label})", "", "    " + cmd_b, ""]
+    if stats:
+        r = stats[0]
+        head += [f"--stats (every dispatch of {label} in the run: setup, 1 s of clock settling, warmup, the "
+                 f"{bench_steps} back-to-back steps and the {bench_steps} event-timed launches): "
+                 f"{r['Calls']} calls, average {float(r['AverageNs']) * 1e-3:.2f} us, "
+                 f"min {float(r['MinNs']) * 1e-3:.2f} us, max {float(r['MaxNs']) * 1e-3:.2f} us.", ""]
+    head += [f"The last {len(timed)} dispatches (the launches bench.py times one by one for the roofline): "
+             f"average {timed.mean():.2f} us, min {timed.min():.2f} us, max {timed.max():.2f} us.", "",
+             "## Per workload (bench.py --profile)", ""]
+    lines = head + lines[2:]
+    with open(os.path.join(PROFILES, "attn_kernels_128k.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    for c in cfgs:
+        algo = algorithmic_bytes(c, tokens[c.name])["codes"]
+        fk = float(np.mean([v for _, v in fe[c.name]]))
+        wk = float(np.mean([v for _, v in wr[c.name]]))
+        hbm = (fk * fscale + wk * wscale) * 1024
+        txt = [f"# HBM traffic of {kernel_label(c)} on {c.name}, per dispatch", "",
+               "Commands (two passes, one counter each; committed files only):", "",
+               "    cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE -d <out>/fetch -o fetch --output-format csv -- "
+               f"python3 /root/repo/bench.py --profile --steps {launches}",
+               "    cd /tmp && TMPDIR=/tmp rocprofv3 --pmc WRITE_SIZE -d <out>/write -o write --output-format csv -- "
+               f"python3 /root/repo/bench.py --profile --steps {launches}", "",
+               "Calibration: the same runs end with three device copies of exactly 1 GiB; FETCH_SIZE is scaled by "
+               f"{fscale:.4f} and WRITE_SIZE by {wscale:.4f} so that each reads 1048576 KiB for them.", "",
+               f"kernel_source_sha256_16: {kernel_source_hash(kernel_kind(c))}",
+               f"dispatches: {len(fe[c.name])}",
+               f"fetch_kib_per_dispatch: {fk:.1f}", f"write_kib_per_dispatch: {wk:.1f}",
+               f"fetch_scale: {fscale:.4f}", f"write_scale: {wscale:.4f}",
+               f"hbm_bytes_per_launch: {hbm:.0f}", f"algorithmic_code_bytes_per_launch: {algo}",
+               f"traffic_over_algorithmic: {hbm / algo:.3f}"]
+        with open(os.path.join(PROFILES, f"traffic_attn_decode_{c.name}.txt"), "w") as f:
+            f.write("\n".join(txt) + "\n")
+    print(f"wrote profiles for {', '.join(names)}")
+
+
 def workload(name: str):
     return workloads.CONFIGS[name] if name in workloads.CONFIGS else workloads.PAGES_CONFIGS[name]
 
@@ -328,7 +584,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="llama8b_128k_r2", help="primary workload (value, roofline)")
-    ap.add_argument("--also", default="llama8b_128k_r1,pages_g64_r11_128k,pages_g64_r21_128k,llama8b_8k_r2",
+    ap.add_argument("--also", default="llama8b_128k_r1,llama8b_32k_r1,ragged16_r2,pages_g64_r11_128k,"
+                                      "pages_g64_r21_128k,llama8b_8k_r2",
                     help="comma list of extra workloads reported in variants")
     ap.add_argument("--layers", type=int, default=0, help="distinct layer buffers to rotate (0: >= 1 GiB)")
     ap.add_argument("--no-graph", action="store_true")
@@ -336,7 +593,14 @@ def main():
     ap.add_argument("--check", action="store_true", help="compare layer 0 with the oracle")
     ap.add_argument("--profile", action="store_true",
                     help="no timing: a few launches of --config and --also workloads plus a 1 GiB copy, for rocprofv3")
+    ap.add_argument("--write-profiles", nargs=4, metavar=("BENCH_KT_DIR", "KT_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: write the profiles/ summaries from the csv output of rocprofv3 runs: --kernel-trace "
+                         "--stats of `bench.py --also '' --no-graph --no-cpu-baseline --steps K` (K = --steps), and "
+                         "three runs of bench.py --profile (--kernel-trace --stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE)")
     args = ap.parse_args()
+    if args.write_profiles:
+        write_profiles(*args.write_profiles, bench_steps=args.steps)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -350,16 +614,19 @@ def main():
         profile_run(names, max(args.steps, 1))
         return
     cfg = workloads.CONFIGS[args.config]
-    prim, base = run_config(cfg, args.steps, args.warmup, args.layers, not args.no_graph, args.check)
+    stream_probe = read_stream_probe()
+    gather_probe = lds_gather_probe()
+    prim, base = run_config(cfg, args.steps, args.warmup, args.layers, not args.no_graph, args.check,
+                            gather_probe["TBps"])
     variants = {cfg.name: prim}
     for name in [s for s in args.also.split(",") if s and s != cfg.name]:
         variants[name], _ = run_config(workload(name), args.steps, args.warmup, args.layers, not args.no_graph,
-                                       args.check)
+                                       args.check, gather_probe["TBps"])
         if name in PAGES_CONTEXT:
             variants[name]["pages_context"] = PAGES_CONTEXT[name]
 
-    achieved = prim["bytes"]["codes"] / (prim["us_per_launch"] * 1e-6) * 1e-9
-    traffic = read_traffic(cfg.name)
+    achieved = prim["bytes"]["codes"] / (prim["ms_per_step"] * 1e-3) * 1e-9
+    traffic = read_traffic(cfg)
     line = {
         "metric": "decode-attn KV tokens/s per layer at 128K ctx, 1/2-bit; % of HBM roofline",
         "value": prim["kv_tokens_per_s_per_layer"],
@@ -374,12 +641,11 @@ def main():
                    "groups": cfg.n_groups, "codes": cfg.n_codes, "layers_rotated": prim["layers_rotated"]},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": f"{KERNEL_NAME} (fused decode attention, one launch per layer)",
+                     "kernel": f"{kernel_label(cfg)} (fused decode attention, one launch per layer)",
                      "algorithmic_bytes_per_launch": prim["bytes"]["codes"]},
         "variants": variants,
-        "hbm_read_stream_GBps": read_stream_gbps(),
-        "kernel_source_sha256_16": kernel_source_hash(),
-        "wide_kernel_source_sha256_16": kernel_source_hash(WIDE_KERNEL_SOURCES),
+        "probes": {"hbm_read_stream": stream_probe, "lds_random_gather": gather_probe},
+        "kernel_source_sha256_16": {kind: kernel_source_hash(kind) for kind in KERNELS},
     }
     line["codebook_tools"] = codebook_tools_timing()
     if not args.no_cpu_baseline:

@@ -11,8 +11,8 @@ import vector_quantized_kv_amd as vq
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_symbols():
-    with open(os.path.join(ROOT, "include", "commvq.h")) as f:
+def declared_symbols(header="commvq.h"):
+    with open(os.path.join(ROOT, "include", header)) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(commvq_[a-z0-9_]+)\s*\(", text)))
@@ -25,6 +25,26 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(vq.EXPORTED_SYMBOLS)
+
+
+def test_probe_library_exports_its_header():
+    """The benchmark's measurement probes live in a library of their own, not in the attention ABI."""
+    from vector_quantized_kv_amd import build as vbuild
+    if not os.path.exists(vbuild.PROBES_LIB):
+        pytest.skip("libcommvq_probes.so not built")
+    L = ctypes.CDLL(vbuild.PROBES_LIB)
+    names = declared_symbols("commvq_probes.h")
+    assert names == ["commvq_probe_lds_gather", "commvq_probe_read_stream"]
+    for n in names:
+        assert hasattr(L, n), n
+        assert not hasattr(vq.lib(), n), n
+    # host checks reject bad arguments before any launch
+    L.commvq_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+    L.commvq_probe_lds_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.commvq_probe_read_stream(None, 16, 1, 0x1000, None) != 0
+    assert L.commvq_probe_read_stream(0x1000, 15, 1, 0x1000, None) != 0
+    assert L.commvq_probe_lds_gather(0, 1, 0x1000, None) != 0
 
 
 def test_dims_struct_layout_matches_header():

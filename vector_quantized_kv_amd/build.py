@@ -20,21 +20,33 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# measurement probes for the benchmark (HBM read stream, LDS random gathers): a library of their own
+PROBES_LIB = os.path.join(PKG, "libcommvq_probes.so")
+PROBES_SOURCES = ["probes.hip"]
+
+
+def _hipcc(sources, out: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp] + [os.path.join(CSRC, s) for s in sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [ln for ln in (proc.stdout + proc.stderr).splitlines() if "packed-fp32-ops" not in ln]
     if proc.returncode != 0:
         sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError("hipcc failed building libcommvq.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libcommvq.so (the C ABI and every kernel of the path) and libcommvq_probes.so (measurement
+    probes used by the benchmark); returns the path of libcommvq.so."""
+    _hipcc(PROBES_SOURCES, PROBES_LIB, verbose)
+    return _hipcc(SOURCES, LIB, verbose)
 
 
 HOST_CHECK_LIB = os.path.join(ROOT, "_build", "libcommvq_hostcheck.so")
