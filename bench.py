@@ -444,11 +444,18 @@ PAGES_CONTEXT = {
 
 
 def _csv_rows(directory: str, suffix: str):
+    """Rows of the rocprofv3 csv file *<suffix> (or *<suffix>.gz) under directory."""
     import csv
     import glob
-    paths = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    import gzip
+    import io
+    paths = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True) +
+                   glob.glob(os.path.join(directory, "**", f"*{suffix}.gz"), recursive=True))
     if not paths:
         raise SystemExit(f"no *{suffix} under {directory}")
+    if paths[0].endswith(".gz"):
+        with gzip.open(paths[0], "rt", newline="") as f:
+            return list(csv.DictReader(io.StringIO(f.read())))
     with open(paths[0], newline="") as f:
         return list(csv.DictReader(f))
 
@@ -472,6 +479,67 @@ def _dispatches(rows, value_key=None):
 PROFILE_LAUNCHES = 20  # launches per workload in the bench.py --profile runs the summaries are made from
 
 
+def _profiled_dispatches(seq, cfgs, launches: int) -> dict:
+    """Per workload of a bench.py --profile run, its profiled attention dispatches: each workload starts with its
+    RoPE table (one rope_table_kernel dispatch), and its profiled launches are the last `launches` attention
+    dispatches before the next workload."""
+    segs, cur = [], None
+    for x in seq:
+        if "rope_table_kernel" in x[0]:
+            cur = []
+            segs.append(cur)
+        elif cur is not None and "attn_" in x[0] and "_kernel" in x[0]:
+            cur.append(x)
+    assert len(segs) == len(cfgs), (len(segs), len(cfgs))
+    return {c.name: seg[-launches:] for c, seg in zip(cfgs, segs)}
+
+
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS "
+    "SQ_WAIT_INST_ANY SQ_VALU_MFMA_BUSY_CYCLES",
+    "SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INST_LEVEL_LDS "
+    "SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL",
+)
+
+
+def write_counters(dirs):
+    """profiles/sq_counters_attn_128k.md from two rocprofv3 --pmc runs of bench.py --profile (SQ_PASSES)."""
+    import collections
+    names = ["llama8b_128k_r2"] + [n for n in PROFILE_ALSO if n != "llama8b_128k_r2"]
+    cfgs = [workload(n) for n in names]
+    vals = collections.defaultdict(dict)
+    for d in dirs:
+        rows = _csv_rows(d, "counter_collection.csv")
+        for counter in sorted({r["Counter_Name"] for r in rows}):
+            seq = _dispatches([r for r in rows if r["Counter_Name"] == counter], "Counter_Value")
+            for name, disp in _profiled_dispatches(seq, cfgs, PROFILE_LAUNCHES).items():
+                vals[counter][name] = float(np.mean([v for _, v in disp]))
+    lines = ["# SQ counters of the attention kernels at 128K context", "",
+             "Commands (two passes, one GPU, committed files only):", ""]
+    for i, cs in enumerate(SQ_PASSES):
+        lines.append(f"    cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {cs} -d <out>/sq{i} -o sq{i} --output-format csv -- "
+                     f"python3 /root/repo/bench.py --profile --steps {PROFILE_LAUNCHES}")
+    lines += ["", "Per-dispatch averages over each workload's profiled launches (rocprofv3 sums each counter over "
+              "the shader engines). Written by `bench.py --write-counters`.", ""]
+    lines += [f"kernel_source_sha256_16 ({KERNELS[k][0]}): {kernel_source_hash(k)}" for k in ("f16", "wide")]
+    lines += ["", "| counter | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for counter in sorted(vals):
+        lines.append(f"| {counter} | " + " | ".join(f"{vals[counter].get(n, float('nan')):.4g}" for n in names) + " |")
+
+    def ratio(a, b):
+        return " | ".join(f"{vals[a][n] / vals[b][n]:.3f}" if vals.get(a, {}).get(n) and vals.get(b, {}).get(n)
+                          else "-" for n in names)
+    lines += ["", "Derived:", "", "| ratio | " + " | ".join(names) + " |", "|---|" + "---|" * len(names),
+              f"| LDS bank-conflict cycles / LDS active cycles | {ratio('SQ_LDS_BANK_CONFLICT', 'SQ_LDS_IDX_ACTIVE')} |",
+              f"| LDS active cycles / CU-busy cycles | {ratio('SQ_LDS_IDX_ACTIVE', 'SQ_BUSY_CU_CYCLES')} |",
+              f"| MFMA-busy cycles / CU-busy cycles | {ratio('SQ_VALU_MFMA_BUSY_CYCLES', 'SQ_BUSY_CU_CYCLES')} |",
+              f"| VALU instructions / LDS instructions | {ratio('SQ_INSTS_VALU', 'SQ_INSTS_LDS')} |",
+              f"| VALU instructions / MFMA instructions | {ratio('SQ_INSTS_VALU', 'SQ_INSTS_MFMA')} |"]
+    with open(os.path.join(PROFILES, "sq_counters_attn_128k.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/sq_counters_attn_128k.md")
+
+
 def write_profiles(bench_kt_dir: str, kt_dir: str, fetch_dir: str, write_dir: str, bench_steps: int):
     """profiles/ summaries. (1) rocprofv3 --kernel-trace --stats of the bench command for the headline workload:
     the --stats line of its kernel and the average of the last `bench_steps` dispatches (the launches bench.py
@@ -491,17 +559,7 @@ def write_profiles(bench_kt_dir: str, kt_dir: str, fetch_dir: str, write_dir: st
     tokens = {c.name: sum(c.lengths) for c in cfgs}  # (the profiled workloads have fixed lengths)
 
     def per_workload(seq):
-        # each workload starts with its RoPE table (one rope_table_kernel dispatch); its profiled launches are the
-        # last `launches` attention dispatches before the next workload
-        segs, cur = [], None
-        for x in seq:
-            if "rope_table_kernel" in x[0]:
-                cur = []
-                segs.append(cur)
-            elif cur is not None and "attn_" in x[0] and "_kernel" in x[0]:
-                cur.append(x)
-        assert len(segs) == len(cfgs), (len(segs), len(cfgs))
-        return {c.name: seg[-launches:] for c, seg in zip(cfgs, segs)}
+        return _profiled_dispatches(seq, cfgs, launches)
     kt, fe, wr = per_workload(trace), per_workload(fetch), per_workload(write)
     fscale = 1048576.0 / np.mean([v for _, v in copies(fetch)])
     wscale = 1048576.0 / np.mean([v for _, v in copies(write)])
@@ -597,7 +655,13 @@ def main():
                     help="no GPU: write the profiles/ summaries from the csv output of rocprofv3 runs: --kernel-trace "
                          "--stats of `bench.py --also '' --no-graph --no-cpu-baseline --steps K` (K = --steps), and "
                          "three runs of bench.py --profile (--kernel-trace --stats, --pmc FETCH_SIZE, --pmc WRITE_SIZE)")
+    ap.add_argument("--write-counters", nargs=2, metavar=("SQ0_DIR", "SQ1_DIR"),
+                    help="no GPU: write profiles/sq_counters_attn_128k.md from two rocprofv3 --pmc runs of "
+                         "bench.py --profile (the two counter sets of SQ_PASSES)")
     args = ap.parse_args()
+    if args.write_counters:
+        write_counters(args.write_counters)
+        return
     if args.write_profiles:
         write_profiles(*args.write_profiles, bench_steps=args.steps)
         return
