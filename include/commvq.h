@@ -93,9 +93,8 @@ const char* commvq_last_error_detail(void);
 
 /* ---------------------------------------------------------------------------------------------
  * RoPE phase table: e^{i * t * theta_j} for positions t = 0 .. n_positions-1, stored as two levels in
- * four sections, each entry computed in fp64 and rounded once:
+ * three sections, each entry computed in fp64 and rounded once to fp32:
  *   fine[j][f]   = e^{i f theta_j}, f < 64, pair-major, complex fp32 (re, im)        (32 KiB)
- *   fine16[g][f][u] = the same phases for pair j = 4g + u, packed fp16 (re, im)      (16 KiB)
  *   fine32g[g][h][f][p] = the same phases for pair j = 4g + 2h + p, complex fp32     (32 KiB)
  *   coarse[c][j] = e^{i 64 c theta_j}, c < ceil(n_positions / 64), complex fp32     (512 B per row)
  * The rotation of a key at position t is coarse[t >> 6][j] * fine[j][t & 63]

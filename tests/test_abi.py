@@ -126,7 +126,7 @@ def test_workspace_sizes():
     assert vq.value_reduce_workspace_size(d, 2048) == 2 * 32 * 2 * 132 * 4
     # RoPE table: fine fp32 pair-major (64 x 64 x 8 B), fine fp16 (64 x 64 x 4 B), fine fp32 group-major
     # (64 x 64 x 8 B), coarse (ceil(n/64) x 64 x 8 B)
-    assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (4096 + 2048 + 4096 + 2048 * 64) * 8
+    assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (4096 + 4096 + 2048 * 64) * 8
     assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 0) == 0
 
 

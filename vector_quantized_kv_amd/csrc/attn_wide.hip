@@ -1,6 +1,7 @@
 // Decode-step attention over a CommVQ cache in the pages' own code shape, on gfx950.
 //
-// Same computation as attn_kernel (score = scale * sum_j Re(conj(q_j) khat_{t,j} e^{i t theta_j}),
+// Same computation as the byte-layout kernels
+// (score = scale * sum_j Re(conj(q_j) khat_{t,j} e^{i t theta_j}),
 // out = softmax-weighted sum of vhat), for the setting the CommVQ pages evaluate: one code index shared by
 // the 64 dims of a half head (G = 2 groups of 64 dims), N = 64 codewords per residual codebook (6-bit
 // indices), and many residual rounds. The average is R log2(N) / g bits per scalar (pith.science verdict
@@ -14,11 +15,11 @@
 // pass p + 1 is staged through registers into the other slot. Scores and the value accumulators are
 // linear in the residuals, so each pass adds its chunk's share to the MFMA accumulators.
 //
-// Work item, lanes and MFMA layouts are those of attn_kernel: lane = token of a 64-token block, 4 GQA
-// heads per KV head, the per-64-token RoPE phase on the query and the per-lane phase on the keys. A
-// 16-byte chunk cc of the 128-byte row of group g holds RoPE pairs 32 g + 4 cc .. + 3, exactly the pairs
-// of the byte layout's group 8 g + cc, so the key MFMA step, the p^T operands, the softmax and the epilogue
-// are shared. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual rows,
+// Work item, lanes and MFMA layouts are those of the fp16 byte-layout kernel (attn_f16.hip): lane = token of a
+// 64-token block, 4 GQA heads per KV head, the per-64-token RoPE phase on the query and the per-lane phase on
+// the keys. A 16-byte chunk cc of the 128-byte row of group g holds RoPE pairs 32 g + 4 cc .. + 3, exactly
+// the pairs of the byte layout's group 8 g + cc, so the key contraction's query operand, the p^T operands,
+// the softmax and the epilogue are the byte layout's. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual rows,
 // sums them in fp32 on the matrix core (an MFMA with the identity as A adds a lane's four fp16 values to
 // its fp32 accumulator), and then
 //   keys:   rotates the fp32 sum by the lane's fine phases in fp32 (phases read from a 32 KiB LDS table) and

@@ -17,11 +17,9 @@ constexpr int kGqa = 4;         // q heads per KV head
 constexpr int kSplitTokens = 1024;  // value_reduce: tokens per (sequence, KV head) work item
 constexpr int kPartFloats = 132;    // per (b, q head, split): m, l, 2 pad, o[128]
 constexpr int kFineRows = 64;       // RoPE table: fine rows e^{i f theta}, f < 64
-// RoPE table sections, in float2 units: fine fp32 [j][f]; fine packed fp16 [g][f][u] with j = 4g + u
-// (4 bytes per entry); fine fp32 group-major [g][h][f][p] with j = 4g + 2h + p (16 bytes per (g, h, f):
-// a lane's phases of two pairs); coarse fp32 [c][j]
-constexpr int kRopeFine16Offset = kFineRows * kPairs;
-constexpr int kRopeFine32gOffset = kRopeFine16Offset + kFineRows * kPairs / 2;
+// RoPE table sections, in float2 units: fine fp32 [j][f]; fine fp32 group-major [g][h][f][p] with
+// j = 4g + 2h + p (16 bytes per (g, h, f): a lane's phases of two pairs); coarse fp32 [c][j]
+constexpr int kRopeFine32gOffset = kFineRows * kPairs;
 constexpr int kRopeCoarseOffset = kRopeFine32gOffset + kFineRows * kPairs;
 constexpr int kAttnMaxBlocksPerWave = 8;  // 64-token blocks per wave per split
 constexpr int kCounterBytes = 256;  // attention workspace head: per-(b, kv) arrival counters

@@ -23,14 +23,14 @@ __device__ __forceinline__ float ld(const T* p) {
 }
 
 // ------------------------------------------------------------------------------------ RoPE table
-// One thread per entry, over four sections: fine fp32 pair-major (entry j * 64 + f = e^{i f theta_j}),
-// fine packed fp16 group-major (entry (g * 64 + f) * 4 + u for pair j = 4g + u, (cos, sin) rounded once
-// from fp64), fine fp32 group-major (entry ((g * 2 + h) * 64 + f) * 2 + p for pair j = 4g + 2h + p), coarse
-// fp32 position-major (entry c * 64 + j = e^{i 64 c theta_j}).
+// One thread per entry, over three sections, each (cos, sin) computed in fp64 and rounded once to fp32: fine
+// pair-major (entry j * 64 + f = e^{i f theta_j}), fine group-major (entry ((g * 2 + h) * 64 + f) * 2 + p for
+// pair j = 4g + 2h + p: a lane's phases of two pairs in one 16-byte read), coarse position-major (entry
+// c * 64 + j = e^{i 64 c theta_j}).
 __global__ void rope_table_kernel(double base, int64_t n_coarse, float2* out) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   constexpr int64_t kFine = static_cast<int64_t>(kFineRows) * kPairs;
-  if (idx >= 3 * kFine + n_coarse * kPairs) return;
+  if (idx >= 2 * kFine + n_coarse * kPairs) return;
   int j;
   double pos;
   if (idx < kFine) {
@@ -38,34 +38,22 @@ __global__ void rope_table_kernel(double base, int64_t n_coarse, float2* out) {
     pos = static_cast<double>(idx % kFineRows);
   } else if (idx < 2 * kFine) {
     const int k = static_cast<int>(idx - kFine);
-    j = 4 * (k >> 8) + (k & 3);
-    pos = static_cast<double>((k >> 2) & 63);
-  } else if (idx < 3 * kFine) {
-    const int k = static_cast<int>(idx - 2 * kFine);
     j = 4 * (k >> 8) + 2 * ((k >> 7) & 1) + (k & 1);
     pos = static_cast<double>((k >> 1) & 63);
   } else {
-    j = static_cast<int>((idx - 3 * kFine) % kPairs);
-    pos = 64.0 * static_cast<double>((idx - 3 * kFine) / kPairs);
+    j = static_cast<int>((idx - 2 * kFine) % kPairs);
+    pos = 64.0 * static_cast<double>((idx - 2 * kFine) / kPairs);
   }
   const double theta = pow(base, -2.0 * j / static_cast<double>(kHeadDim));
   double s, c;
   sincos(pos * theta, &s, &c);
-  if (idx < kFine) {
-    out[idx] = make_float2(static_cast<float>(c), static_cast<float>(s));
-  } else if (idx < 2 * kFine) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    reinterpret_cast<h2*>(out + kRopeFine16Offset)[idx - kFine] = (h2){static_cast<f16>(c), static_cast<f16>(s)};
-  } else if (idx < 3 * kFine) {
-    out[kRopeFine32gOffset + (idx - 2 * kFine)] = make_float2(static_cast<float>(c), static_cast<float>(s));
-  } else {
-    out[kRopeCoarseOffset + (idx - 3 * kFine)] = make_float2(static_cast<float>(c), static_cast<float>(s));
-  }
+  // the sections are contiguous: fine at 0, fine group-major at kRopeFine32gOffset = kFine, coarse after it
+  out[idx] = make_float2(static_cast<float>(c), static_cast<float>(s));
 }
 
 hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hipStream_t s) {
   const int64_t n_coarse = rope_coarse_rows(n_positions);
-  const int64_t n = 3LL * kFineRows * kPairs + n_coarse * kPairs;
+  const int64_t n = 2LL * kFineRows * kPairs + n_coarse * kPairs;
   rope_table_kernel<<<dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s>>>(base, n_coarse, table);
   return hipGetLastError();
 }
