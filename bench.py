@@ -229,8 +229,10 @@ def profile_run(names, launches: int):
         per_layer = algorithmic_bytes(cfg, int(base["total_tokens"]))["total"]
         layers = max(4, int(math.ceil((1 << 30) / per_layer)))
         rope = vq.rope_table(d, int(base["max_len"]))
-        Ls = [vq.Layer(d, base if i == 0 else workloads.make_inputs(cfg, seed=cfg.seed + 1000 * i), rope=rope,
-                       rope_positions=int(base["max_len"])) for i in range(layers)]
+        same_lengths = dataclasses.replace(cfg, lengths=tuple(int(x) for x in base["seq_len"]), ragged_range=None)
+        Ls = [vq.Layer(d, base if i == 0 else workloads.make_inputs(same_lengths, seed=cfg.seed + 1000 * i),
+                       rope=rope, rope_positions=int(base["max_len"])) for i in range(layers)]
+        share_descriptors(Ls)
         for ly in Ls:  # every layer copy once (setup; also the first touch of its buffers)
             ly.attn_decode()
         torch.cuda.synchronize()
@@ -260,6 +262,15 @@ def profile_run(names, launches: int):
     print("profile: probes (read stream and LDS gathers: 0.5 s of launches, then 1 + 3 more each)", flush=True)
 
 
+def share_descriptors(Ls):
+    """The layer copies of one decode step serve the same batch: like the RoPE table, the sequence descriptors
+    (seq_start, seq_len; equal in every copy) are one pair of device arrays shared by all of them, as in a
+    model, where every layer reads the same ones."""
+    for ly in Ls[1:]:
+        assert bool((ly.seq_start == Ls[0].seq_start).all()) and bool((ly.seq_len == Ls[0].seq_len).all())
+        ly.seq_start, ly.seq_len = Ls[0].seq_start, Ls[0].seq_len
+
+
 def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check: bool, gather_tbps: float):
     import torch
     import vector_quantized_kv_amd as vq
@@ -278,6 +289,7 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
     for i in range(layers):
         inp = base if i == 0 else workloads.make_inputs(same_lengths, seed=cfg.seed + 1000 * i)
         Ls.append(vq.Layer(d, inp, rope=rope, rope_positions=int(base["max_len"])))
+    share_descriptors(Ls)
     torch.cuda.synchronize()
     check_err = None
     if check:

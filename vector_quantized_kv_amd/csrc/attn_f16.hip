@@ -225,15 +225,17 @@ __device__ __forceinline__ uint4 lds_row(const unsigned char* lds, int hi, uint3
 }
 
 // Direct global->LDS copy of groups g0 .. g0 + kN - 1 of residual r's codebook [G][R][N][8] into LDS at dst
-// (4 KiB per group); every wave moves its share.
+// (4 KiB per group); the copy is cut into kW16 parts and each wave moves part `part` (a permutation of the
+// waves, so that the workgroups of one XCD, which all copy the same KV head's codebook at the same moment,
+// start on different parts of it and spread their requests over the L2 channels).
 template <int R, int kN>
-__device__ __forceinline__ void load_groups(const f16* cb_kv, int r, int g0, unsigned char* dst, int wave, int lane) {
+__device__ __forceinline__ void load_groups(const f16* cb_kv, int r, int g0, unsigned char* dst, int part, int lane) {
   constexpr int kPerWave = kN * kCodes / kW16;
 #pragma unroll
   for (int i = 0; i < kPerWave / 64; ++i) {
-    const int c = wave * kPerWave + i * 64 + lane, g = g0 + (c >> 8), l = c & (kCodes - 1);
+    const int c = part * kPerWave + i * 64 + lane, g = g0 + (c >> 8), l = c & (kCodes - 1);
     const f16* src = cb_kv + ((static_cast<int64_t>(g) * R + r) * kCodes + l) * kGroupDim;
-    __builtin_amdgcn_global_load_lds(src, dst + (wave * kPerWave + i * 64) * 16, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, dst + (part * kPerWave + i * 64) * 16, 16, 0, 0);
   }
 }
 
@@ -250,6 +252,8 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   const int kv = blockIdx.x % a.n_kv_heads, split = blockIdx.x / a.n_kv_heads, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the part of each codebook copy this wave moves: rotated by the split (see load_groups)
+  const int part = __builtin_amdgcn_readfirstlane((wave + split) & (kW16 - 1));
   const int64_t cb_stride = static_cast<int64_t>(kGroups) * R * kCodes * kGroupDim;
   const f16* cb_k = static_cast<const f16*>(a.k_cb) + kv * cb_stride;
   const f16* cb_v = static_cast<const f16*>(a.v_cb) + kv * cb_stride;
@@ -262,14 +266,14 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   // (1) The key codebook rows of groups 0-7 and the fp32 fine phases, straight into LDS; they depend only on the
   // KV head, so they go out first. Groups 8-15 (and the R = 1 value codebook) follow the first records and land
   // while the first key unit works on groups 0-7.
-  load_groups<R, 8>(cb_k, 0, 0, lds + key_row_off<R>(0, 0), wave, lane);
-  if constexpr (R == 2) load_groups<R, 8>(cb_k, 1, 0, lds + key_row_off<R>(1, 0), wave, lane);
+  load_groups<R, 8>(cb_k, 0, 0, lds + key_row_off<R>(0, 0), part, lane);
+  if constexpr (R == 2) load_groups<R, 8>(cb_k, 1, 0, lds + key_row_off<R>(1, 0), part, lane);
   {
     constexpr int kChunks = kPhaseBytes / 16;
     const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine32gOffset);
 #pragma unroll
     for (int i = 0; i < kChunks / kThreads16; ++i) {
-      const int c = (wave * (kChunks / kThreads16) + i) * 64;
+      const int c = (part * (kChunks / kThreads16) + i) * 64;
       __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, lds + kPhaseOff + c * 16, 16, 0, 0);
     }
   }
@@ -330,11 +334,11 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   __builtin_amdgcn_sched_barrier(0);
   // (4) Key rows of groups 8-15 (and the R = 1 value codebook): published by the barrier before any wave reads
   // group 8 (publish_hi below).
-  load_groups<R, 8>(cb_k, 0, 8, lds + key_row_off<R>(0, 8), wave, lane);
+  load_groups<R, 8>(cb_k, 0, 8, lds + key_row_off<R>(0, 8), part, lane);
   if constexpr (R == 2) {
-    load_groups<R, 8>(cb_k, 1, 8, lds + key_row_off<R>(1, 8), wave, lane);
+    load_groups<R, 8>(cb_k, 1, 8, lds + key_row_off<R>(1, 8), part, lane);
   } else {
-    load_groups<R, 16>(cb_v, 0, 0, lds + value_row_off<R>(0, 0), wave, lane);
+    load_groups<R, 16>(cb_v, 0, 0, lds + value_row_off<R>(0, 0), part, lane);
   }
   constexpr int kHiLoads = kStagedTables<R> ? (R == 2 ? 2 * 8 : 8 + 16) * kCodes / kThreads16 : 0;
   __builtin_amdgcn_sched_barrier(0);
@@ -353,8 +357,8 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   auto refill_lo = [&]() {
     if constexpr (R == 2) {
       slot_barrier();
-      load_groups<R, 8>(cb_v, 0, 0, lds + value_row_off<R>(0, 0), wave, lane);
-      load_groups<R, 8>(cb_v, 1, 0, lds + value_row_off<R>(1, 0), wave, lane);
+      load_groups<R, 8>(cb_v, 0, 0, lds + value_row_off<R>(0, 0), part, lane);
+      load_groups<R, 8>(cb_v, 1, 0, lds + value_row_off<R>(1, 0), part, lane);
     }
   };
 
@@ -534,8 +538,8 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   if constexpr (R == 2) {
     __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
     slot_barrier();
-    load_groups<R, 8>(cb_v, 0, 8, lds + value_row_off<R>(0, 8), wave, lane);
-    load_groups<R, 8>(cb_v, 1, 8, lds + value_row_off<R>(1, 8), wave, lane);
+    load_groups<R, 8>(cb_v, 0, 8, lds + value_row_off<R>(0, 8), part, lane);
+    load_groups<R, 8>(cb_v, 1, 8, lds + value_row_off<R>(1, 8), part, lane);
   }
 
   // ------------------------------------------------------------------------------ wave softmax
