@@ -263,9 +263,21 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   const int64_t seq_start = sb.start;
 
   // ---------------------------------------------------------------------------------- prologue
-  // (1) The key codebook rows of groups 0-7 and the fp32 fine phases, straight into LDS; they depend only on the
-  // KV head, so they go out first. Groups 8-15 (and the R = 1 value codebook) follow the first records and land
-  // while the first key unit works on groups 0-7.
+  // A split past the end of its sequence (a ragged batch launches the longest sequence's split count for every
+  // sequence) leaves at once, before any LDS copy: only the record loads, which need the sequence bounds
+  // anyway, are on the critical path of the prologue, so testing first costs the other workgroups nothing.
+  const int S = a.split_tokens;
+  const int t0 = split * S;
+  const int h0 = kv * kGqa;
+  const int64_t bh0 = static_cast<int64_t>(b) * a.n_q_heads + h0;
+  float* out_bh = a.out + bh0 * kHeadDim;
+  if (t0 >= L) {
+    if (split == 0)  // empty sequence: the output is zero
+      for (int i = tid; i < kGqa * kHeadDim; i += kThreads16) out_bh[i] = 0.f;
+    return;
+  }
+  // (1) The key codebook rows of groups 0-7 and the fp32 fine phases, straight into LDS. Groups 8-15 (and the
+  // R = 1 value codebook) follow the first records and land while the first key unit works on groups 0-7.
   load_groups<R, 8>(cb_k, 0, 0, lds + key_row_off<R>(0, 0), part, lane);
   if constexpr (R == 2) load_groups<R, 8>(cb_k, 1, 0, lds + key_row_off<R>(1, 0), part, lane);
   {
@@ -279,17 +291,6 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const int S = a.split_tokens;
-  const int t0 = split * S;
-  const int h0 = kv * kGqa;
-  const int64_t bh0 = static_cast<int64_t>(b) * a.n_q_heads + h0;
-  float* out_bh = a.out + bh0 * kHeadDim;
-  if (t0 >= L) {
-    if (split == 0)  // empty sequence: the output is zero
-      for (int i = tid; i < kGqa * kHeadDim; i += kThreads16) out_bh[i] = 0.f;
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // the direct-to-LDS loads land before the workgroup ends
-    return;
-  }
   const int nvalid = min(S, L - t0);
   const int nblocks = (nvalid + 63) >> 6;
   const int my_blocks = (nblocks - wave + kW - 1) / kW;  // this wave owns blocks wave, wave + kW, ...

@@ -145,6 +145,18 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   const int64_t seq_start = sb.start;
 
   // ---------------------------------------------------------------------------------- prologue
+  // A split past the end of its sequence (a ragged batch launches the longest sequence's split count for every
+  // sequence) leaves at once, before any LDS copy.
+  const int S = a.split_tokens;
+  const int t0 = split * S;
+  const int h0 = kv * kGqa;
+  const int64_t bh0 = static_cast<int64_t>(b) * a.n_q_heads + h0;
+  float* out_bh = a.out + bh0 * kHeadDim;
+  if (t0 >= L) {
+    if (split == 0)
+      for (int i = tid; i < kGqa * kHeadDim; i += kThreads) out_bh[i] = 0.f;
+    return;
+  }
   // (1) fp32 fine phases (group-major, the byte layout's groups) and the codebook chunk of pass 0 (key
   // residuals 0 .. kRes-1), straight into LDS.
   {
@@ -163,17 +175,6 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const int S = a.split_tokens;
-  const int t0 = split * S;
-  const int h0 = kv * kGqa;
-  const int64_t bh0 = static_cast<int64_t>(b) * a.n_q_heads + h0;
-  float* out_bh = a.out + bh0 * kHeadDim;
-  if (t0 >= L) {
-    if (split == 0)
-      for (int i = tid; i < kGqa * kHeadDim; i += kThreads) out_bh[i] = 0.f;
-    __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));
-    return;
-  }
   const int nvalid = min(S, L - t0);
   const int nblocks = (nvalid + 63) >> 6;
   const int my_blocks = (nblocks - wave + kW - 1) / kW;
