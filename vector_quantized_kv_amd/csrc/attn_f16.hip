@@ -120,22 +120,10 @@ __device__ __forceinline__ void contract_key(const float (&w)[NB][8], const floa
   });
 }
 
-template <int G>
-__device__ __forceinline__ uint4 gather_row(const unsigned char* tab, const uint4& code) {
-  return *reinterpret_cast<const uint4*>(tab + G * kCodes * 16 + code_index(code, G) * 16);
-}
-
-// Value path, R = 2: each group's two residual rows are gathered whole and summed in fp16; an identity MFMA
-// transposes each 4-dim half within its lane quad (lane 4b + j receives dim j of the quad's 4 tokens, exactly,
-// in fp32), which converted back is the B operand of p^T x v for MFMA block b = the quad.
-template <int P>
-__device__ __forceinline__ void gather_pair2(const unsigned char* tab0, const unsigned char* tab1, const uint4& c0,
-                                             const uint4& c1, uint4 (&buf)[2][2]) {
-  buf[0][0] = gather_row<2 * P>(tab0, c0);
-  buf[0][1] = gather_row<2 * P>(tab1, c1);
-  buf[1][0] = gather_row<2 * P + 1>(tab0, c0);
-  buf[1][1] = gather_row<2 * P + 1>(tab1, c1);
-}
+// Value path, R = 2: each group's two residual rows are gathered whole (by the value pass, from the LDS map
+// below) and summed in fp16; an identity MFMA transposes each 4-dim half within its lane quad (lane 4b + j
+// receives dim j of the quad's 4 tokens, exactly, in fp32), which converted back is the B operand of p^T x v for
+// MFMA block b = the quad.
 template <int G>
 __device__ __forceinline__ void value_step_quad(const uint4& row, const h4& ident, const h4& pt,
                                                 f4 (&O)[2 * kGroups]) {

@@ -134,6 +134,9 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   const int kv = blockIdx.x % a.n_kv_heads, split = blockIdx.x / a.n_kv_heads, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the part of the prologue's copies this wave moves, rotated by the split: the workgroups of an XCD copy the
+  // same KV head's data at the same moment and so start on different parts of it (spread over the L2 channels)
+  const int part = __builtin_amdgcn_readfirstlane((wave + split) & (kW - 1));
   const int R = a.n_residuals, Wd = a.record_words;
   const int nch = (R + kRes - 1) / kRes;  // passes per kind
   const int64_t cb_stride = static_cast<int64_t>(kWG) * R * kWN * (kWRow / 2);
@@ -164,12 +167,12 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine32gOffset);
 #pragma unroll
     for (int i = 0; i < kFineChunks / kThreads; ++i) {
-      const int c = (wave * (kFineChunks / kThreads) + i) * 64;
+      const int c = (part * (kFineChunks / kThreads) + i) * 64;
       __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, lds + kPhase + c * 16, 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < kMaxBlocks; ++i) {
-      const int u0 = wave * (kSlot / 16 / kW) + i * 64;
+      const int u0 = part * (kSlot / 16 / kW) + i * 64;
       __builtin_amdgcn_global_load_lds(slot_unit_src(cb_k, R, 0, u0 + lane), lds + u0 * 16, 16, 0, 0);
     }
   }
