@@ -35,9 +35,11 @@
  * referee report's minor comments; the CommVQ summary page, Limitations, names R = 11 and 21).
  * Selected by n_groups = 2, n_codes = 64:
  *   k_codebook, v_codebook [Hkv][2][R][64][64]   as above with W = 64 (group g holds pairs 32g .. 32g+31)
- *   k_codes, v_codes       [Hkv][T][ceil(12 R / 32)] little-endian uint32 words, passed through the
+ *   k_codes, v_codes       [Hkv][ceil(12 R / 32)][T] little-endian uint32 words, passed through the
  *                          uint8_t pointer: token t's R x 2 six-bit indices as one bitstream, index
- *                          (r, g) at bit 6 (2 r + g) (bit k of the stream = bit k % 32 of word k / 32)
+ *                          (r, g) at bit 6 (2 r + g) (bit k of the stream = bit k % 32 of word k / 32),
+ *                          word w of token t at [kv][w][t] (one word plane per w, like the byte
+ *                          layout's residual planes)
  *
  * Conventions for every call:
  *   - Pointers are device pointers unless marked (host). Buffers are owned by the caller; the library
@@ -143,7 +145,7 @@ int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const
  * the last workgroup of each (b, kv) resets, so every completed call leaves it zero-filled again; the
  * rest is scratch. Calls that share one workspace must not overlap in time.
  * Codes, codebooks and rope_table must be 16-byte aligned.
- * Both layouts: the bit-packed one reads its token records [Hkv][T][words] instead of the planes.
+ * Both layouts: the bit-packed one reads its word planes [Hkv][words][T] instead of the byte planes.
  * ------------------------------------------------------------------------------------------- */
 size_t commvq_attn_decode_workspace_size(const commvq_dims* d /* host */, int32_t max_len);
 int commvq_attn_decode(const commvq_dims* d /* host */, const void* q, const uint8_t* k_codes, const uint8_t* v_codes,
@@ -176,7 +178,7 @@ int commvq_attn_decode_noalloc(const commvq_dims* d /* host */, const void* q, c
  * forward_implications: the softmax weights multiply the value codes before the codebook product):
  *   bins[g][r][l] = sum_{t < L_b} p[b][h][t] * [index (r, g) of token row seq_start[b]+t == l]
  *   out[b][h][W g + w] = sum_r sum_l bins[g][r][l] * v_codebook[kv][g][r][l][w]
- * v_codes: the byte planes [Hkv][R][T][G], or (bit-packed layout) the token records [Hkv][T][words].
+ * v_codes: the byte planes [Hkv][R][T][G], or (bit-packed layout) the word planes [Hkv][words][T].
  * p: [B][Hq][max_len] fp32, any finite real values, used as given (no renormalisation); entries at
  * t >= L_b are ignored. workspace: commvq_value_reduce_workspace_size(d, max_len) bytes.
  * Resolution: the bins are integer fixed point per (b, h, 1024-token split of t): each weight is rounded to
@@ -201,10 +203,10 @@ int commvq_value_reduce(const commvq_dims* d /* host */, const float* p, const u
  * order) and subtracts that codeword from res (res starts as the group's W values of x).
  *   x         [Hkv][n_tokens][D] in dims->dtype, in the codebook's own frame (keys before RoPE)
  *   codebook  [Hkv][G][R][N][W] in dims->dtype
- *   codes     a [Hkv][R][total_rows][G] uint8 code array, or (bit-packed layout) token records
- *             [Hkv][total_rows][ceil(12 R / 32)] uint32, 16-byte aligned; token t is written to row
- *             first_row + t (its whole record), other rows are untouched (so new tokens can be appended to
- *             a cache in place)
+ *   codes     a [Hkv][R][total_rows][G] uint8 code array, or (bit-packed layout) word planes
+ *             [Hkv][ceil(12 R / 32)][total_rows] uint32, 16-byte aligned; token t is written to row
+ *             first_row + t (its whole record: one word in each plane), other rows are untouched (so new
+ *             tokens can be appended to a cache in place)
  * Returns COMMVQ_EINVAL unless 0 <= first_row and first_row + n_tokens <= total_rows; n_tokens = 0 is a
  * no-op.
  * ------------------------------------------------------------------------------------------- */
@@ -223,7 +225,7 @@ int commvq_encode_greedy(const commvq_dims* d /* host */, const void* x, const v
  * codebook_out = codebook_in for a codeword no token selects.
  *   x             [Hkv][n_tokens][D] in dims->dtype, in the codebook's own frame (keys before RoPE)
  *   codes         [Hkv][R][n_tokens][G] uint8 (commvq_encode_greedy with first_row 0, total_rows n_tokens),
- *                 or (bit-packed layout) the token records [Hkv][n_tokens][ceil(12 R / 32)] uint32, 16-byte
+ *                 or (bit-packed layout) the word planes [Hkv][ceil(12 R / 32)][n_tokens] uint32, 16-byte
  *                 aligned
  *   codebook_in   [Hkv][G][R][N][W] in dims->dtype
  *   codebook_out  same shape and type; must not overlap codebook_in (COMMVQ_EINVAL)
@@ -237,8 +239,8 @@ int commvq_codebook_update(const commvq_dims* d /* host */, const void* x, const
 
 /* ---------------------------------------------------------------------------------------------
  * Code unpack exactly as the attention kernels read codes: out[kv][r][t][g] = index (int32).
- * codes [Hkv][R][total_tokens][G] uint8, or (bit-packed layout) the token records
- * [Hkv][total_tokens][ceil(12 R / 32)] uint32, read in the attention kernel's windows of 4 residuals.
+ * codes [Hkv][R][total_tokens][G] uint8, or (bit-packed layout) the word planes
+ * [Hkv][ceil(12 R / 32)][total_tokens] uint32, read in the attention kernel's windows of 4 residuals.
  * Used to test the unpack bit-exactly.
  * ------------------------------------------------------------------------------------------- */
 int commvq_debug_unpack(const commvq_dims* d /* host */, const uint8_t* codes, int64_t total_tokens /* host */,

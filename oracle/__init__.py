@@ -115,7 +115,7 @@ def unpack(d: Dims, codes: np.ndarray, total_tokens: int) -> np.ndarray:
 
 
 def unpack_bits(d: Dims, words, total_tokens: int) -> np.ndarray:
-    """Bit-packed index records [Hkv][T][ceil(bits*R*G/32)] uint32 -> indices [Hkv][R][T][G] uint8."""
+    """Bit-packed word planes [Hkv][ceil(bits*R*G/32)][T] uint32 -> indices [Hkv][R][T][G] uint8."""
     ww = np.ascontiguousarray(words, dtype=np.uint32)
     out = np.empty((d.n_kv_heads, d.n_residuals, int(total_tokens), d.n_groups), dtype=np.uint8)
     lib().oracle_unpack_bits(ctypes.byref(d), ww.ctypes.data_as(ctypes.c_void_p), int(total_tokens), _ptr(out))

@@ -450,22 +450,23 @@ void oracle_codebook_update(const oracle_dims* d, const double* x, const double*
  * formula R*log2(N')/g: the pages' own setting shares one index across 64 dims (g = 64) with N' = 64
  * codewords, 6 bits per index, and R = 11 or 21 rounds). Reading of the layout: a token's R*G indices
  * of b = log2(N) bits form one little-endian bitstream of 32-bit words, index (round r, group g) at bit
- * offset b*(r*G + g); a token record is ceil(b*R*G/32) words and records are [Hkv][T][words]. They are
- * unpacked into the byte layout the rest of this oracle uses, [Hkv][R][T][G]. */
+ * offset b*(r*G + g); a token record is ceil(b*R*G/32) words, and word w of token t is stored at
+ * [Hkv][w][T] (word planes). They are unpacked into the byte layout the rest of this oracle uses,
+ * [Hkv][R][T][G]. */
 void oracle_unpack_bits(const oracle_dims* d, const uint32_t* words, int64_t total_tokens, uint8_t* out) {
   int G = d->n_groups, R = d->n_residuals, bits = 0;
   while ((1 << bits) < d->n_codes) ++bits;
   int64_t rec = ((int64_t)bits * R * G + 31) / 32;
   for (int kv = 0; kv < d->n_kv_heads; ++kv)
     for (int64_t t = 0; t < total_tokens; ++t) {
-      const uint32_t* w = words + ((int64_t)kv * total_tokens + t) * rec;
+      const uint32_t* w = words + (int64_t)kv * rec * total_tokens + t; /* word i at w[i * total_tokens] */
       for (int r = 0; r < R; ++r)
         for (int g = 0; g < G; ++g) {
           int64_t pos = (int64_t)bits * (r * G + g);
           uint32_t v = 0;
           for (int k = 0; k < bits; ++k) {
             int64_t p = pos + k;
-            v |= ((w[p / 32] >> (p % 32)) & 1u) << k;
+            v |= ((w[(p / 32) * total_tokens] >> (p % 32)) & 1u) << k;
           }
           out[code_off(d, total_tokens, kv, t, r, g)] = (uint8_t)v;
         }

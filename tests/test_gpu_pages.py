@@ -192,13 +192,13 @@ def test_pages_encode_greedy_recovers_codewords_and_appends_in_place(vq):
     od = oracle.dims(1, 4 * Hkv, Hkv, R, n_groups=2, n_codes=64)
     x = oracle.decode(od, cb, idx, n).astype(np.float16)  # exact: one fp16 codeword per group
     d = vq.make_dims(1, 4 * Hkv, Hkv, R, "float16", n_groups=2, n_codes=64)
-    big = torch.full((Hkv, n + 9, 1), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    big = torch.full((Hkv, 1, n + 9), 0x5A5A5A5A, dtype=torch.int32, device="cuda")  # one word plane at R = 1
     vq.encode_greedy(d, torch.from_numpy(x).cuda(), torch.from_numpy(cb).cuda(), codes=big, first_row=5)
     torch.cuda.synchronize()
     out = big.cpu().numpy()
-    got = oracle.unpack_bits(od, np.ascontiguousarray(out[:, 5:5 + n]).view(np.uint32), n)
+    got = oracle.unpack_bits(od, np.ascontiguousarray(out[:, :, 5:5 + n]).view(np.uint32), n)
     np.testing.assert_array_equal(got, idx)
-    assert np.all(out[:, :5] == 0x5A5A5A5A) and np.all(out[:, 5 + n:] == 0x5A5A5A5A)
+    assert np.all(out[:, :, :5] == 0x5A5A5A5A) and np.all(out[:, :, 5 + n:] == 0x5A5A5A5A)
 
 
 def test_pages_attn_sixteen_kv_heads(vq):

@@ -466,10 +466,10 @@ def test_encode_eval_brute_force_and_greedy_consistency(oracle_lib):
 # ------------------------------------------------------------------------- bit-packed indices (g = 64)
 def _pack_bits_bigint(idx, bits):
     """Reference packing from the definition of a little-endian bitstream: one Python integer per token,
-    index k (k = r*G + g) at bit offset bits*k, cut into 32-bit words."""
+    index k (k = r*G + g) at bit offset bits*k, cut into 32-bit words; word w of token t goes to [kv][w][t]."""
     Hkv, R, T, G = idx.shape
     nwords = (bits * R * G + 31) // 32
-    out = np.zeros((Hkv, T, nwords), dtype=np.uint32)
+    out = np.zeros((Hkv, nwords, T), dtype=np.uint32)
     for kv in range(Hkv):
         for t in range(T):
             v = 0
@@ -477,7 +477,7 @@ def _pack_bits_bigint(idx, bits):
                 for g in range(G):
                     v |= int(idx[kv, r, t, g]) << (bits * (r * G + g))
             for k in range(nwords):
-                out[kv, t, k] = (v >> (32 * k)) & 0xFFFFFFFF
+                out[kv, k, t] = (v >> (32 * k)) & 0xFFFFFFFF
     return out
 
 
@@ -492,35 +492,45 @@ def test_unpack_bits_matches_bigint_stream(oracle_lib, R, G, N):
 
 def test_unpack_bits_hand_worked_words(oracle_lib):
     d = oracle.dims(1, 4, 1, 11, head_dim=128, n_groups=2, n_codes=64)  # 132 bits -> 5 words per token
-    ones = np.zeros((1, 1, 5), dtype=np.uint32)
-    ones[0, 0, :4] = 0xFFFFFFFF
-    ones[0, 0, 4] = 0xF
+    ones = np.zeros((1, 5, 1), dtype=np.uint32)  # [Hkv][words][T]
+    ones[0, :4, 0] = 0xFFFFFFFF
+    ones[0, 4, 0] = 0xF
     assert np.all(oracle.unpack_bits(d, ones, 1) == 63)
-    one = np.zeros((1, 1, 5), dtype=np.uint32)
-    one[0, 0, 1] = 0x10000000  # bit 60 = index k = 10 = (round 5, group 0), value 1
+    one = np.zeros((1, 5, 1), dtype=np.uint32)
+    one[0, 1, 0] = 0x10000000  # bit 60 = index k = 10 = (round 5, group 0), value 1
     got = oracle.unpack_bits(d, one, 1)
     assert got[0, 5, 0, 0] == 1 and got.sum() == 1
-    straddle = np.zeros((1, 1, 5), dtype=np.uint32)
+    straddle = np.zeros((1, 5, 1), dtype=np.uint32)
     straddle[0, 0, 0] = 1 << 30  # index k = 5 (round 2, group 1) occupies bits 30..35: value 0b110101 = 53
-    straddle[0, 0, 1] = 0b1101
+    straddle[0, 1, 0] = 0b1101
     got = oracle.unpack_bits(d, straddle, 1)
     assert got[0, 2, 0, 1] == 53 and got.sum() == 53
 
 
+def test_unpack_bits_word_planes(oracle_lib):
+    """Word w of token t sits at [kv][w][t]: a field set in word 1 of token 2 of KV head 1 belongs to that
+    token and head only."""
+    d = oracle.dims(1, 4, 2, 11, head_dim=128, n_groups=2, n_codes=64)
+    w = np.zeros((2, 5, 3), dtype=np.uint32)
+    w[1, 1, 2] = 0x10000000  # bit 60 of token 2's stream: index (round 5, group 0) = 1
+    got = oracle.unpack_bits(d, w, 3)
+    assert got[1, 5, 2, 0] == 1 and got.sum() == 1
+
+
 def test_unpack_bits_at_8_bits_one_round_is_the_byte_layout(oracle_lib):
-    """With N = 256 and R = 1 a token's bitstream is its 16 code bytes, so the byte layout read as words
-    unpacks to itself."""
+    """With N = 256 and R = 1 a token's bitstream is its 16 code bytes, so the byte layout read as
+    little-endian words (and laid out in word planes) unpacks to itself."""
     rng = np.random.default_rng(44)
     d = oracle.dims(1, 4, 3, 1)
     codes = rng.integers(0, 256, size=(3, 1, 11, 16)).astype(np.uint8)
-    words = codes.reshape(3, 11, 16).view(np.uint32)
+    words = np.ascontiguousarray(codes.reshape(3, 11, 16).view(np.uint32).transpose(0, 2, 1))
     np.testing.assert_array_equal(oracle.unpack_bits(d, words, 11), codes)
     np.testing.assert_array_equal(oracle.unpack(d, codes, 11), codes.astype(np.int32))
 
 
 def test_pages_setting_attention_matches_torch_sdpa(oracle_lib):
     """The pages' g = 64 / N' = 64 / R = 11 setting end to end: indices drawn here, laid out as bit-packed
-    records by the workloads generator, unpacked and attended by the oracle, against torch's SDPA over
+    word planes by the workloads generator, unpacked and attended by the oracle, against torch's SDPA over
     keys and values built here by plain indexing."""
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(45)
@@ -532,7 +542,7 @@ def test_pages_setting_attention_matches_torch_sdpa(oracle_lib):
     ki = rng.integers(0, N, size=(Hkv, R, L, G)).astype(np.uint8)
     vi = rng.integers(0, N, size=(Hkv, R, L, G)).astype(np.uint8)
     kw, vw = workloads.pack_bits(ki, 6), workloads.pack_bits(vi, 6)
-    assert kw.shape == (Hkv, L, 5)
+    assert kw.shape == (Hkv, 5, L)  # word planes
     out = oracle.attn_decode(d, q, oracle.unpack_bits(d, kw, L), oracle.unpack_bits(d, vw, L), kcb, vcb,
                              np.zeros(1, np.int64), np.array([L], np.int32), L)
     theta = 500000.0 ** (-np.arange(64) * 2.0 / 128)

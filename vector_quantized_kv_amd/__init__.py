@@ -219,7 +219,7 @@ def value_reduce(d: Dims, p, v_codes, v_codebook, seq_start, seq_len, max_len: i
 
 def encode_greedy(d: Dims, x, codebook, codes=None, first_row: int = 0, stream=None):
     """Greedy residual codes of x [Hkv][n][D] (see commvq_encode_greedy). With codes=None a new array is
-    returned: [Hkv][R][n][G] uint8, or for the bit-packed layout the token records [Hkv][n][words] (int32
+    returned: [Hkv][R][n][G] uint8, or for the bit-packed layout the word planes [Hkv][words][n] (int32
     tensor holding the uint32 words); otherwise the tokens are written to rows first_row.. of codes."""
     import torch
     n = int(x.shape[1])
@@ -228,11 +228,11 @@ def encode_greedy(d: Dims, x, codebook, codes=None, first_row: int = 0, stream=N
         with _on(stream):
             if packed:
                 words = (6 * d.n_residuals * d.n_groups + 31) // 32
-                codes = torch.zeros((d.n_kv_heads, n, words), dtype=torch.int32, device=x.device)
+                codes = torch.zeros((d.n_kv_heads, words, n), dtype=torch.int32, device=x.device)
             else:
                 codes = torch.zeros((d.n_kv_heads, d.n_residuals, n, d.n_groups), dtype=torch.uint8,
                                     device=x.device)
-    rows = int(codes.shape[1] if packed else codes.shape[2])
+    rows = int(codes.shape[2])
     _check(lib().commvq_encode_greedy(ctypes.byref(d), _ptr(x), _ptr(codebook), n, _ptr(codes), rows,
                                       int(first_row), _stream(stream)), "encode_greedy")
     return codes
@@ -240,7 +240,7 @@ def encode_greedy(d: Dims, x, codebook, codes=None, first_row: int = 0, stream=N
 
 def codebook_update(d: Dims, x, codes, codebook_in, codebook_out=None, stream=None):
     """One M-step of the residual codebook fit (see commvq_codebook_update): x [Hkv][n][D], codes
-    [Hkv][R][n][G] uint8, codebook_in [Hkv][G][R][N][W]. Returns codebook_out (a new tensor if None)."""
+    [Hkv][R][n][G] uint8 (bit-packed layout: word planes [Hkv][words][n]), codebook_in [Hkv][G][R][N][W]. Returns codebook_out (a new tensor if None)."""
     import torch
     n = int(x.shape[1])
     if codebook_out is None:
@@ -289,7 +289,7 @@ class Layer:
         self.q = torch.from_numpy(inputs["q"]).to(device=device, dtype=dt)
         self.k_cb = torch.from_numpy(inputs["k_cb"]).to(device=device, dtype=dt)
         self.v_cb = torch.from_numpy(inputs["v_cb"]).to(device=device, dtype=dt)
-        # bit-packed records (uint32 words) travel as int32 tensors of the same bits
+        # bit-packed word planes (uint32 words) travel as int32 tensors of the same bits
         self.k_codes = torch.from_numpy(_code_array(inputs["k_codes"])).to(device)
         self.v_codes = torch.from_numpy(_code_array(inputs["v_codes"])).to(device)
         self.seq_start = torch.from_numpy(inputs["seq_start"]).to(device)

@@ -7,7 +7,8 @@
 // indices), and many residual rounds. The average is R log2(N) / g bits per scalar (pith.science verdict
 // for arXiv 2506.18879, key_machinery; its referee report's minor comments give g = 64, N' = 64), so
 // R = 11 gives about 1 bit and R = 21 about 2 (the CommVQ summary page, Limitations, names these two).
-// A token's R x G indices are one little-endian bitstream of 32-bit words, index (r, g) at bit 6 (r G + g).
+// A token's R x G indices are one little-endian bitstream of 32-bit words, index (r, g) at bit 6 (r G + g);
+// word w of every token of a KV head lies in word plane w ([Hkv][words][T]).
 //
 // The codebooks (R x 16 KiB per KV head for keys, as much for values) do not fit in LDS, so the kernel
 // runs in passes of kRes residuals: key passes c = 0 .. nch-1, then the wave softmax, then value passes.
@@ -208,18 +209,20 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   // (3) index words of pass 0 for every block. Pass p reads the two words of its window (chunk c of the
-  // record); requests past the last pass read the last pass's words, so every pass issues the same loads
-  // (clamped rows and words, always in bounds).
-  const uint32_t* kw = reinterpret_cast<const uint32_t*>(a.k_codes);
-  const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.v_codes);
+  // record) from their word planes: a wave's 64 tokens are 256 contiguous bytes of each plane, and the word
+  // that two consecutive passes share is read again while it still sits in L2. Requests past the last pass
+  // read the last pass's words, so every pass issues the same loads (clamped rows and words, always in bounds).
+  const int64_t T = a.total_tokens;
+  const uint32_t* kw = reinterpret_cast<const uint32_t*>(a.k_codes) + static_cast<int64_t>(kv) * Wd * T;
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.v_codes) + static_cast<int64_t>(kv) * Wd * T;
   uint2 code[kMaxBlocks];
   auto request_words = [&](int pn, int i) {
     const int pc = min(pn, 2 * nch - 1);
     const int c = pc < nch ? pc : pc - nch;
     const int w0 = packed_window_word(c);
     const int w1 = min(w0 + 1, Wd - 1);
-    const uint32_t* rec = (pc < nch ? kw : vw) + (static_cast<int64_t>(kv) * a.total_tokens + token_row(i)) * Wd;
-    code[i] = make_uint2(rec[w0], rec[w1]);
+    const uint32_t* rec = (pc < nch ? kw : vw) + token_row(i);
+    code[i] = make_uint2(rec[w0 * T], rec[w1 * T]);
   };
 #pragma unroll
   for (int i = 0; i < kMaxBlocks; ++i) request_words(0, i);

@@ -38,7 +38,8 @@ __device__ __forceinline__ uint4 load_code_record(const uint8_t* codes, int64_t 
 }
 
 // Bit-packed records (one index per 64 dims, N = 64): a token's R x 2 six-bit indices form one
-// little-endian bitstream of 32-bit words, index (r, g) at bit 6 (2 r + g). Kernels read it in windows
+// little-endian bitstream of 32-bit words, index (r, g) at bit 6 (2 r + g). Word w of every token of a KV head
+// sits in plane w ([Hkv][words][T]), so a token's words are T apart. Kernels read the stream in windows
 // of kWideResPerPass residuals: window c starts at bit 6 * 2 * kWideResPerPass * c, inside words
 // packed_window_word(c) and the one after it (48 bits from a 0- or 16-bit offset: always two words).
 __device__ __forceinline__ int packed_window_word(int c) { return (kWideBits * kWideGroups * kWideResPerPass * c) >> 5; }
@@ -64,13 +65,13 @@ __device__ __forceinline__ uint32_t packed_index(uint32_t x0, uint32_t x1) {
   }
 }
 static_assert(kWideBits * kWideGroups * kWideResPerPass <= 48, "a window fits two words from a 16-bit offset");
-// Index (r, g) of one token record, read field by field (the codebook tools; the attention kernel reads
-// whole windows). A field that crosses a word boundary takes its high bits from the next word, which is
-// then still inside the record (the field ends at or before bit 12 R).
-__device__ __forceinline__ uint32_t packed_field(const uint32_t* rec, int r, int g) {
+// Index (r, g) of one token record whose words are `plane` apart, read field by field (the codebook tools;
+// the attention kernel reads whole windows). A field that crosses a word boundary takes its high bits from
+// the next word, which is then still inside the record (the field ends at or before bit 12 R).
+__device__ __forceinline__ uint32_t packed_field(const uint32_t* rec, int64_t plane, int r, int g) {
   const int bit = kWideBits * (kWideGroups * r + g), w = bit >> 5, sh = bit & 31;
-  uint32_t v = rec[w] >> sh;
-  if (sh > 32 - kWideBits) v |= rec[w + 1] << (32 - sh);
+  uint32_t v = rec[w * plane] >> sh;
+  if (sh > 32 - kWideBits) v |= rec[(w + 1) * plane] << (32 - sh);
   return v & ((1u << kWideBits) - 1);
 }
 

@@ -279,11 +279,11 @@ __global__ void __launch_bounds__(256) value_reduce_bits_kernel(const ValueReduc
     int32_t fx[kGqa];
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) fx[h] = fixed_point(w[k][h], fx_scale[h], 0);
-    const uint32_t* rec = words + (static_cast<int64_t>(kv) * a.total_tokens + row0 + tid + 256 * k) * Wd;
+    const uint32_t* rec = words + static_cast<int64_t>(kv) * Wd * a.total_tokens + row0 + tid + 256 * k;
     for (int r = 0; r < R; ++r)
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const uint32_t l = packed_field(rec, r, g);
+        const uint32_t l = packed_field(rec, a.total_tokens, r, g);
 #pragma unroll
         for (int h = 0; h < kGqa; ++h) atomicAdd(&bins[((h * G + g) * R + r) * N + l], fx[h]);
       }
@@ -353,10 +353,10 @@ __global__ void debug_unpack_bits_kernel(const uint32_t* words, int64_t total_to
   const int c = static_cast<int>(item % n_windows);
   const int64_t kt = item / n_windows;  // kv * T + t
   const int64_t kv = kt / total_tokens, t = kt % total_tokens;
-  const uint32_t* rec = words + kt * Wd;
+  const uint32_t* rec = words + kv * Wd * total_tokens + t;  // word w at rec[w * total_tokens]
   const int w0 = packed_window_word(c);
   uint32_t x0, x1;
-  packed_window(rec[w0], rec[min(w0 + 1, Wd - 1)], packed_window_shift(c), x0, x1);
+  packed_window(rec[w0 * total_tokens], rec[min(w0 + 1, Wd - 1) * total_tokens], packed_window_shift(c), x0, x1);
   uint32_t idx[2 * kWideResPerPass];
   idx[0] = packed_index<0>(x0, x1);
   idx[1] = packed_index<1>(x0, x1);
@@ -531,7 +531,8 @@ hipError_t launch_codebook_update(int dtype, int R, int Hkv, const void* x, cons
 // tokens take the rounds together: round r's codebook of the group (64 codewords x 64 dims, 16 KiB) sits in
 // LDS as fp32, and all lanes read the same codeword (a broadcast). The first minimum of the fp32 squared
 // distance is chosen and subtracted. Index (r, g) goes to bit 12 r + 6 g of the token's record: group 0's
-// pass stores every word, group 1's pass ORs its fields into them (ceil(12 R / 32) words per token).
+// pass stores every word, group 1's pass ORs its fields into them (ceil(12 R / 32) words per token, one in
+// each word plane, so consecutive tokens store consecutive words).
 __global__ void __launch_bounds__(256) encode_greedy_bits_kernel(const f16* x, const f16* cb, int R, int64_t n,
                                                                  uint32_t* words, int64_t total_rows,
                                                                  int64_t first_row) {
@@ -543,7 +544,7 @@ __global__ void __launch_bounds__(256) encode_greedy_bits_kernel(const f16* x, c
   const bool live = t < n;
   const int64_t tt = live ? t : n - 1;  // clamped: every thread takes part in the rounds (and their barriers)
   const int Wd = wide_record_words(R);
-  uint32_t* rec = words + (static_cast<int64_t>(kv) * total_rows + first_row + tt) * Wd;
+  uint32_t* rec = words + static_cast<int64_t>(kv) * Wd * total_rows + first_row + tt;  // word w at rec[w * total_rows]
   for (int g = 0; g < kWideGroups; ++g) {
     float res[W];
     const f16* xv = x + (static_cast<int64_t>(kv) * n + tt) * kHeadDim + g * W;
@@ -554,8 +555,8 @@ __global__ void __launch_bounds__(256) encode_greedy_bits_kernel(const f16* x, c
     auto flush = [&]() {
       uint32_t v = static_cast<uint32_t>(acc);
       if (live) {
-        if (g > 0) v |= rec[word];
-        rec[word] = v;
+        if (g > 0) v |= rec[word * total_rows];
+        rec[word * total_rows] = v;
       }
       acc >>= 32;
       ++word;
@@ -656,13 +657,13 @@ __global__ void __launch_bounds__(256) codebook_update_bits_kernel(const f16* x,
                                             : 1.0;
   const int Wd = wide_record_words(R);
   for (int64_t t = tid; t < n; t += blockDim.x) {
-    const uint32_t* rec = words + (static_cast<int64_t>(kv) * n + t) * Wd;
+    const uint32_t* rec = words + static_cast<int64_t>(kv) * Wd * n + t;
     const f16* xv = x + (static_cast<int64_t>(kv) * n + t) * kHeadDim + g * W + s * kUpdSlice;
     double res[kUpdSlice];
 #pragma unroll
     for (int w = 0; w < kUpdSlice; ++w) res[w] = static_cast<double>(static_cast<float>(xv[w]));
     for (int r = 0; r < R; ++r) {
-      const int l = static_cast<int>(packed_field(rec, r, g));
+      const int l = static_cast<int>(packed_field(rec, n, r, g));
       // the codeword read goes out before the atomics: LDS operations complete in order, so waiting for it
       // afterwards would also wait for every atomic of the round
       const float4 c = cws[r * N + l];

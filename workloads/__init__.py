@@ -9,9 +9,9 @@ Layouts (shared by every consumer):
   v_cb     [Hkv][G][R][N][W]       value codebook
   k_codes  [Hkv][R][T][G] uint8    one byte per code index (N = 256); one plane per residual
   v_codes  [Hkv][R][T][G] uint8
-           N < 256 (the pages' g = 64 setting, N = 64): bit-packed records [Hkv][T][words] uint32 instead,
-           each token's R*G indices of log2(N) bits as one little-endian bitstream, index (r, g) at bit
-           log2(N) * (r*G + g), words = ceil(log2(N) * R * G / 32)
+           N < 256 (the pages' g = 64 setting, N = 64): bit-packed word planes [Hkv][words][T] uint32
+           instead: each token's R*G indices of log2(N) bits as one little-endian bitstream, index (r, g) at
+           bit log2(N) * (r*G + g), words = ceil(log2(N) * R * G / 32), word w of token t at [kv][w][t]
   seq_start[B] int64, seq_len[B] int32: sequence b owns token rows seq_start[b] .. +seq_len[b]-1
 with D = head_dim, G = n_groups, W = D / G, R = n_residuals, N = n_codes, T = total tokens.
 
@@ -142,18 +142,18 @@ def make_inputs(cfg: Config, seed: Optional[int] = None) -> Dict[str, np.ndarray
 
 
 def pack_bits(idx: np.ndarray, bits: int) -> np.ndarray:
-    """Lay out indices [Hkv][R][T][G] (each < 2**bits) as bit-packed token records [Hkv][T][words] uint32."""
+    """Lay out indices [Hkv][R][T][G] (each < 2**bits) as bit-packed word planes [Hkv][words][T] uint32."""
     Hkv, R, T, G = idx.shape
     words = (bits * R * G + 31) // 32
-    out = np.zeros((Hkv, T, words), dtype=np.uint64)
+    out = np.zeros((Hkv, words, T), dtype=np.uint64)
     for r in range(R):
         for g in range(G):
             pos = bits * (r * G + g)
             w, sh = pos // 32, pos % 32
             v = idx[:, r, :, g].astype(np.uint64)
-            out[:, :, w] |= (v << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+            out[:, w, :] |= (v << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
             if sh + bits > 32:
-                out[:, :, w + 1] |= v >> np.uint64(32 - sh)
+                out[:, w + 1, :] |= v >> np.uint64(32 - sh)
     return out.astype(np.uint32)
 
 
