@@ -151,6 +151,7 @@ def probes_lib():
     L.commvq_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p]
     L.commvq_probe_lds_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.commvq_probe_lds_bin_add.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return L
 
 
@@ -217,6 +218,29 @@ def lds_gather_probe(iters: int = 256, blocks: int = 1024, reps: int = 5) -> dic
             "kernel": "lds_gather_kernel", "gathers": gathers}
 
 
+def lds_bin_add_probe(iters: int = 64, blocks: int = 1024, reps: int = 5) -> dict:
+    """Random 64-bit LDS atomic adds (commvq_probe_lds_bin_add: one workgroup of 8 waves per CU, bins of 42 units
+    x 2 head pairs x 64 codewords, a random codeword per lane): the ceiling of the bit-packed kernel's value
+    bins. The bins' total is checked against the number of adds."""
+    import torch
+    L = probes_lib()
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        assert L.commvq_probe_lds_bin_add(iters, blocks, sink.data_ptr(), s) == 0
+    sink.zero_()
+    run()
+    torch.cuda.synchronize()
+    adds = blocks * 8 * iters * 42 * 2  # wave instructions, 64 lanes each
+    assert int(sink.item()) == adds * 64, "LDS bin-add probe: the bins do not hold every add"
+    settle(lambda i: run(), 0.5)
+    ms = _timed_ms(run, reps)
+    return {"G_wave_adds_per_s": adds / (ms * 1e-3) * 1e-9,
+            "clk_per_wave_add_per_cu_at_2.4GHz": 256 * CLOCK_GHZ * 1e9 * (ms * 1e-3) / adds,
+            "kernel": "lds_bin_add_kernel", "wave_adds": adds}
+
+
 def profile_run(names, launches: int):
     """Few launches per workload (for rocprofv3), after one setup launch per layer copy, plus a 1 GiB device copy
     whose FETCH_SIZE / WRITE_SIZE calibrate the counters (it reads and writes exactly 1 GiB), plus the probes."""
@@ -259,7 +283,9 @@ def profile_run(names, launches: int):
     torch.cuda.empty_cache()
     read_stream_probe(reps=3)
     lds_gather_probe(reps=3)
-    print("profile: probes (read stream and LDS gathers: 0.5 s of launches, then 1 + 3 more each)", flush=True)
+    lds_bin_add_probe(reps=3)
+    print("profile: probes (read stream, LDS gathers, LDS bin adds: 0.5 s of launches, then 1 + 3 more each)",
+          flush=True)
 
 
 def share_descriptors(Ls):
@@ -271,7 +297,7 @@ def share_descriptors(Ls):
         ly.seq_start, ly.seq_len = Ls[0].seq_start, Ls[0].seq_len
 
 
-def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check: bool, gather_tbps: float):
+def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check: bool, probes: dict):
     import torch
     import vector_quantized_kv_amd as vq
 
@@ -371,16 +397,30 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
         "pct_hbm_peak_code_stream": 100.0 * per_layer["codes"] / (per_step_ms * 1e-3) * 1e-9 / HBM_PEAK_GBPS,
         "bytes": per_layer, "max_row_rel_err_vs_oracle": check_err,
     }
-    # Every token gathers, per residual and group, its codeword row from LDS for keys and again for values
-    # (16 bytes in the byte layout, 128 in the bit-packed one, at fp16): that LDS stream is what bounds both
-    # kernels. The whole launch, fixed costs included, is counted against it.
-    gathered = 2 * cfg.n_kv_heads * L * cfg.n_residuals * cfg.n_groups * cfg.group_dim * \
-        (2 if cfg.dtype == "float16" else 4)
-    tbps = gathered / (per_step_ms * 1e-3) * 1e-12
-    res["lds_roofline"] = {"bound": "lds", "gathered_bytes_per_launch": gathered, "achieved": tbps,
-                           "unit": "TB/s", "peak": LDS_PEAK_TBPS, "frac": tbps / LDS_PEAK_TBPS,
-                           "random_gather_ceiling": gather_tbps,
-                           "frac_of_random_gather_ceiling": tbps / gather_tbps}
+    # Byte layout: every token gathers, per residual and group, its 16-byte codeword row from LDS for keys and
+    # again for values; that LDS stream is what bounds the kernel. Bit-packed layout: the keys gather 128-byte
+    # rows the same way, and the values make two random 64-bit LDS adds per (token, residual, group) into the
+    # bins; its LDS floor is the key gathers at the measured gather ceiling plus the adds at the measured add
+    # ceiling. The whole launch, fixed costs included, is counted against them.
+    gather_tbps = probes["lds_random_gather"]["TBps"]
+    row_bytes = cfg.group_dim * (2 if cfg.dtype == "float16" else 4)
+    units = cfg.n_kv_heads * L * cfg.n_residuals * cfg.n_groups  # (token, KV head, residual, group)
+    if cfg.packed:
+        key_bytes = units * row_bytes
+        wave_adds = 2 * units / 64
+        clk_add = probes["lds_bin_add"]["clk_per_wave_add_per_cu_at_2.4GHz"]
+        floor_s = key_bytes / (gather_tbps * 1e12) + wave_adds * clk_add / (256 * CLOCK_GHZ * 1e9)
+        res["lds_roofline"] = {"bound": "lds", "key_gathered_bytes_per_launch": key_bytes,
+                               "value_bin_adds_per_launch": 2 * units, "random_gather_ceiling_TBps": gather_tbps,
+                               "bin_add_clk_per_wave_instruction": clk_add, "floor_us": floor_s * 1e6,
+                               "frac_of_lds_floor": floor_s / (per_step_ms * 1e-3)}
+    else:
+        gathered = 2 * units * row_bytes
+        tbps = gathered / (per_step_ms * 1e-3) * 1e-12
+        res["lds_roofline"] = {"bound": "lds", "gathered_bytes_per_launch": gathered, "achieved": tbps,
+                               "unit": "TB/s", "peak": LDS_PEAK_TBPS, "frac": tbps / LDS_PEAK_TBPS,
+                               "random_gather_ceiling": gather_tbps,
+                               "frac_of_random_gather_ceiling": tbps / gather_tbps}
     res["kernel"] = kernel_label(cfg)
     res["hbm_traffic_bytes_per_launch"] = read_traffic(cfg)
     del Ls
@@ -565,8 +605,10 @@ def write_profiles(bench_kt_dir: str, kt_dir: str, fetch_dir: str, write_dir: st
     fetch = _dispatches(_csv_rows(fetch_dir, "counter_collection.csv"), "Counter_Value")
     write = _dispatches(_csv_rows(write_dir, "counter_collection.csv"), "Counter_Value")
 
-    def copies(seq):
-        return [x for x in seq if "copyBuffer" in x[0]][-3:]
+    def copies(seq):  # the three 1 GiB calibration copies (the probes' small read-backs follow them)
+        cp = [x for x in seq if "copyBuffer" in x[0]]
+        big = max(v for _, v in cp)
+        return [x for x in cp if x[1] > 0.5 * big][-3:]
 
     tokens = {c.name: sum(c.lengths) for c in cfgs}  # (the profiled workloads have fixed lengths)
 
@@ -589,11 +631,14 @@ def write_profiles(bench_kt_dir: str, kt_dir: str, fetch_dir: str, write_dir: st
         d = np.array([v for _, v in kt[c.name]]) * 1e-3
         lines.append(f"| {c.name} | {kernel_label(c)} | {kernel_source_hash(kernel_kind(c))} | {len(d)} | "
                      f"{d.mean():.2f} | {d.min():.2f} | {d.max():.2f} |")
-    probes = [(n, v) for n, v in trace if "read_stream_kernel" in n or "lds_gather_kernel" in n]
+    probe_kernels = ("read_stream_kernel", "lds_gather_kernel", "lds_bin_add_kernel")
+    probes = [(n, v) for n, v in trace if any(k in n for k in probe_kernels)]
     lines += ["", "| probe | dispatches | average us | what it measures |", "|---|---|---|---|"]
     for key, what in (("read_stream_kernel", "1 GiB streaming read: HBM read rate = 1 GiB / duration"),
                       ("lds_gather_kernel", "1024 WGs x 8 waves x 256 x 16 random 16-byte LDS gathers (1 KiB per "
-                                            "wave instruction): gather ceiling = bytes / duration")):
+                                            "wave instruction): gather ceiling = bytes / duration"),
+                      ("lds_bin_add_kernel", "1024 WGs x 8 waves x 64 x 84 random 64-bit LDS adds (wave "
+                                             "instructions): add ceiling = instructions / duration")):
         d = np.array([v for n, v in probes if key in n]) * 1e-3
         if d.size:
             lines.append(f"| {key} | {len(d)} | {d.mean():.2f} | {what} |")
@@ -603,7 +648,8 @@ def write_profiles(bench_kt_dir: str, kt_dir: str, fetch_dir: str, write_dir: st
     stats = [r for r in _csv_rows(bench_kt_dir, "kernel_stats.csv") if f"attn_f16_kernel<{prim.n_residuals}>" in r["Name"]]
     btrace = [v for n, v in _dispatches(_csv_rows(bench_kt_dir, "kernel_trace.csv"))
               if f"attn_f16_kernel<{prim.n_residuals}>" in n]
-    timed = np.array(btrace[-bench_steps:]) * 1e-3
+    region = np.array(btrace[-2 * bench_steps:-bench_steps]) * 1e-3
+    alone = np.array(btrace[-bench_steps:]) * 1e-3
     cmd_b = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d <out>/bench -o bench --output-format csv -- "
              f"python3 /root/repo/bench.py --also '' --no-graph --no-cpu-baseline --steps {bench_steps}")
     head = ["# rocprofv3 kernel statistics: decode attention kernels and measurement probes", "",
@@ -614,8 +660,11 @@ def write_profiles(bench_kt_dir: str, kt_dir: str, fetch_dir: str, write_dir: st
                  f"{bench_steps} back-to-back steps and the {bench_steps} event-timed launches): "
                  f"{r['Calls']} calls, average {float(r['AverageNs']) * 1e-3:.2f} us, "
                  f"min {float(r['MinNs']) * 1e-3:.2f} us, max {float(r['MaxNs']) * 1e-3:.2f} us.", ""]
-    head += [f"The last {len(timed)} dispatches (the launches bench.py times one by one for the roofline): "
-             f"average {timed.mean():.2f} us, min {timed.min():.2f} us, max {timed.max():.2f} us.", "",
+    head += [f"The {len(region)} dispatches of the timed region (back-to-back steps; their average is the "
+             f"kernel duration behind the roofline): average {region.mean():.2f} us, min {region.min():.2f} us, "
+             f"max {region.max():.2f} us.", "",
+             f"The last {len(alone)} dispatches (each launch alone between two HIP events, us_per_launch_isolated): "
+             f"average {alone.mean():.2f} us, min {alone.min():.2f} us, max {alone.max():.2f} us.", "",
              "## Per workload (bench.py --profile)", ""]
     lines = head + lines[2:]
     with open(os.path.join(PROFILES, "attn_kernels_128k.md"), "w") as f:
@@ -690,14 +739,13 @@ def main():
         profile_run(names, max(args.steps, 1))
         return
     cfg = workloads.CONFIGS[args.config]
-    stream_probe = read_stream_probe()
-    gather_probe = lds_gather_probe()
-    prim, base = run_config(cfg, args.steps, args.warmup, args.layers, not args.no_graph, args.check,
-                            gather_probe["TBps"])
+    probes = {"hbm_read_stream": read_stream_probe(), "lds_random_gather": lds_gather_probe(),
+              "lds_bin_add": lds_bin_add_probe()}
+    prim, base = run_config(cfg, args.steps, args.warmup, args.layers, not args.no_graph, args.check, probes)
     variants = {cfg.name: prim}
     for name in [s for s in args.also.split(",") if s and s != cfg.name]:
         variants[name], _ = run_config(workload(name), args.steps, args.warmup, args.layers, not args.no_graph,
-                                       args.check, gather_probe["TBps"])
+                                       args.check, probes)
         if name in PAGES_CONTEXT:
             variants[name]["pages_context"] = PAGES_CONTEXT[name]
 
@@ -720,7 +768,7 @@ def main():
                      "kernel": f"{kernel_label(cfg)} (fused decode attention, one launch per layer)",
                      "algorithmic_bytes_per_launch": prim["bytes"]["codes"]},
         "variants": variants,
-        "probes": {"hbm_read_stream": stream_probe, "lds_random_gather": gather_probe},
+        "probes": probes,
         "kernel_source_sha256_16": {kind: kernel_source_hash(kind) for kind in KERNELS},
     }
     line["codebook_tools"] = codebook_tools_timing()

@@ -12,7 +12,13 @@
  *     64 KiB table of 16 groups x 256 rows, the access pattern of the attention kernels' codebook gathers
  *     (each lane a random row of the same group). Per call: blocks x 8 x iters x 16 x 1 KiB are gathered,
  *     so bytes / time is the random-gather throughput of LDS. `sink` as above.
- * Both return 0 or the hipError_t of the launch; pointers are device pointers; work is enqueued on `stream`
+ *   commvq_probe_lds_bin_add: `blocks` workgroups of 8 waves, one per CU (160 KiB of LDS each); every wave
+ *     performs iters x 42 x 2 random 64-bit LDS atomic adds (ds_add_u64) into bins of 42 units x 2 head
+ *     pairs x 64 codewords, the access pattern of the bit-packed attention kernel's value bins (each lane a
+ *     random codeword of the same unit, both head pairs). `sink` (8 bytes of device memory, zeroed by the
+ *     caller) receives the bins' total, blocks x 8 x iters x 42 x 2 x 64 when every add landed; wave
+ *     instructions / time is the throughput of random 64-bit LDS adds.
+ * All return 0 or the hipError_t of the launch; pointers are device pointers; work is enqueued on `stream`
  * (a hipStream_t; NULL is the default stream).
  */
 #ifndef COMMVQ_PROBES_H
@@ -26,6 +32,7 @@ extern "C" {
 
 int commvq_probe_read_stream(const void* buf, size_t bytes, int blocks, void* sink, void* stream);
 int commvq_probe_lds_gather(int iters, int blocks, void* sink, void* stream);
+int commvq_probe_lds_bin_add(int iters, int blocks, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

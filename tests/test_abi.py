@@ -34,7 +34,7 @@ def test_probe_library_exports_its_header():
         pytest.skip("libcommvq_probes.so not built")
     L = ctypes.CDLL(vbuild.PROBES_LIB)
     names = declared_symbols("commvq_probes.h")
-    assert names == ["commvq_probe_lds_gather", "commvq_probe_read_stream"]
+    assert names == ["commvq_probe_lds_bin_add", "commvq_probe_lds_gather", "commvq_probe_read_stream"]
     for n in names:
         assert hasattr(L, n), n
         assert not hasattr(vq.lib(), n), n
@@ -42,9 +42,12 @@ def test_probe_library_exports_its_header():
     L.commvq_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p]
     L.commvq_probe_lds_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.commvq_probe_lds_bin_add.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert L.commvq_probe_read_stream(None, 16, 1, 0x1000, None) != 0
     assert L.commvq_probe_read_stream(0x1000, 15, 1, 0x1000, None) != 0
     assert L.commvq_probe_lds_gather(0, 1, 0x1000, None) != 0
+    assert L.commvq_probe_lds_bin_add(1, 0, 0x1000, None) != 0
+    assert L.commvq_probe_lds_bin_add(1, 1, None, None) != 0
 
 
 def test_dims_struct_layout_matches_header():

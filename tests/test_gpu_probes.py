@@ -1,6 +1,7 @@
 """The benchmark's measurement probes (libcommvq_probes.so) run through their C ABI and keep their contract:
-every launch succeeds and the sink, written only if the folded value equals a fixed constant, stays untouched
-for these inputs (a zero-filled buffer folds to zero; the LDS probe never writes it)."""
+every launch succeeds; the read and gather probes' sink, written only if the folded value equals a fixed
+constant, stays untouched for these inputs (a zero-filled buffer folds to zero; the gather probe never writes
+it); the bin-add probe's bins hold exactly one count per add."""
 import ctypes
 import sys
 
@@ -19,6 +20,7 @@ def probes():
     L.commvq_probe_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p,
                                            ctypes.c_void_p]
     L.commvq_probe_lds_gather.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.commvq_probe_lds_bin_add.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     return L
 
 
@@ -42,3 +44,15 @@ def test_lds_gather_probe(probes):
     assert probes.commvq_probe_lds_gather(4, 256, sink.data_ptr(), s) == 0
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
+
+
+def test_lds_bin_add_probe_counts_every_add(probes):
+    print("\n[case] probe LDS bin add", flush=True)
+    sys.stdout.flush()
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for iters, blocks in ((1, 1), (3, 300)):
+        sink.zero_()
+        assert probes.commvq_probe_lds_bin_add(iters, blocks, sink.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        assert int(sink.item()) == blocks * 8 * iters * 42 * 2 * 64

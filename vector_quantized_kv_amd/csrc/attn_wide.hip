@@ -10,27 +10,31 @@
 // A token's R x G indices are one little-endian bitstream of 32-bit words, index (r, g) at bit 6 (r G + g);
 // word w of every token of a KV head lies in word plane w ([Hkv][words][T]).
 //
-// The codebooks (R x 16 KiB per KV head for keys, as much for values) do not fit in LDS, so the kernel
-// runs in passes of kRes residuals: key passes c = 0 .. nch-1, then the wave softmax, then value passes.
-// Pass p's codebook chunk (kRes residuals x 2 groups x 8 KiB) sits in LDS slot p % 2 while the chunk of
-// pass p + 1 is staged through registers into the other slot. Scores and the value accumulators are
-// linear in the residuals, so each pass adds its chunk's share to the MFMA accumulators.
+// The key codebooks (R x 16 KiB per KV head) do not fit in LDS, so the key side runs in passes of kRes
+// residuals, c = 0 .. nch-1: pass c's codebook chunk (kRes residuals x 2 groups x 8 KiB) sits in LDS slot
+// c % 2 while the chunk of pass c + 1 is staged through registers into the other slot. Scores are linear in
+// the residuals, so each pass adds its chunk's share to the MFMA accumulators.
+//
+// Values take the pages' own form (pith.science verdict for arXiv 2506.18879, key_machinery and
+// forward_implications: the softmax weights multiply the value codes before the codebook product): every
+// token adds its softmax weights to bin (g, r, l) of each of its value indices, and the bins are contracted
+// with the value codebook once per workgroup. A row gather moves 128 bytes per (token, residual, group); a
+// bin update moves the 4 heads' weights in two 64-bit LDS atomics, about a third of the LDS time. The weights
+// are e^{s - M} with M the workgroup's maximum per head, in fixed point (multiples of 2^-19, two heads per
+// 64-bit bin whose 32-bit halves never carry into each other), so the bins are exact and independent of the
+// order of the adds.
 //
 // Work item, lanes and MFMA layouts are those of the fp16 byte-layout kernel (attn_f16.hip): lane = token of a
 // 64-token block, 4 GQA heads per KV head, the per-64-token RoPE phase on the query and the per-lane phase on
 // the keys. A 16-byte chunk cc of the 128-byte row of group g holds RoPE pairs 32 g + 4 cc .. + 3, exactly
-// the pairs of the byte layout's group 8 g + cc, so the key contraction's query operand, the p^T operands,
-// the softmax and the epilogue are the byte layout's. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual rows,
-// sums them in fp32 on the matrix core (an MFMA with the identity as A adds a lane's four fp16 values to
-// its fp32 accumulator), and then
-//   keys:   rotates the fp32 sum by the lane's fine phases in fp32 (phases read from a 32 KiB LDS table) and
-//           contracts it with the fp32 block query on the fp32 matrix core (v_mfma_f32_4x4x1_16b_f32, query
-//           broadcast from one 4-lane block per dim): no fp16 rounding on the key side, so wide logit ranges
-//           keep the attention within tolerance;
-//   values: sums with the identity as B instead, which transposes each 4x4 (token x dim) quad tile as it
-//           accumulates, rounds once to fp16 and multiplies by p^T.
-// Residuals past R in the last pass of each kind use a zero matrix in place of the identity (their gathers
-// read a real row and add nothing).
+// the pairs of the byte layout's group 8 g + cc, so the key contraction's query operand and the epilogue are
+// the byte layout's. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual
+// rows, sums them in fp32 on the matrix core (an MFMA with the identity as A adds a lane's four fp16 values to
+// its fp32 accumulator), rotates the sum by the lane's fine phases in fp32 (phases read from a 32 KiB LDS
+// table) and contracts it with the fp32 block query on the fp32 matrix core (v_mfma_f32_4x4x1_16b_f32, query
+// broadcast from one 4-lane block per dim): no fp16 rounding on the key side, so wide logit ranges keep the
+// attention within tolerance. Residuals past R in the last pass use a zero matrix in place of the identity
+// (their gathers read a real row and add nothing).
 // Rows are stored with their 16-byte chunks permuted by the codeword (physical chunk = cc xor
 // ((l >> 1) & 7)), so the 16 lanes that share an LDS cycle land on random ones of the 16 bank groups
 // instead of the two that a 128-byte row stride would give them.
@@ -54,8 +58,12 @@ constexpr int kPhase = 2 * kSlot;                // LDS offset of the fp32 fine 
 constexpr int kPhaseBytes = kGroups * 2 * 64 * 16;
 constexpr int kWAhead = 1;                       // units whose gathers are in flight ahead of the current one
 constexpr int kWBufs = kWAhead + 1;
+constexpr int kFxBits = 19;                      // value bins: softmax weights in multiples of 2^-19
 static_assert(kSlot / 16 == kMaxBlocks * kThreads, "one staged 16-byte unit per thread per block");
 static_assert(kPhase + kPhaseBytes <= 160 * 1024, "codebook slots and phases fit the CU's LDS");
+static_assert(kWG * kWideMaxResiduals * 2 * kWN * 8 <= kSlot, "the value bins fit one codebook slot");
+static_assert((static_cast<int64_t>(kW) * kMaxBlocks * 64 << kFxBits) <= (static_cast<int64_t>(1) << 32),
+              "a bin's 32-bit halves (each at most 2^19 per token) never carry into each other");
 
 // Global source of 16-byte unit u of the slot holding residuals r0 .. r0 + kRes - 1 (unit u = table
 // f = 2 rho + g, codeword l, physical chunk pc). Residuals past R read residual R - 1 (never used).
@@ -108,22 +116,21 @@ __device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[kRes], const h
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Value unit: with B = identity, lane 4b + j of D receives value j of each lane of its quad (dim j of the
-// quad's 4 tokens), so the residual sum accumulates already transposed; rounded to fp16 it is the B
-// operand of p^T x v for byte-layout group G.
+// One residual's share of the bins x value codebook product for RoPE-pair chunk cc of group g: lane 4 q + j
+// loads codeword row l = lane (dims 8 cc .. 8 cc + 7, fp16), an identity MFMA turns each 4x4 (codeword x dim)
+// tile into the B operand (lane 4 q + j: dim j of codewords 4 q .. 4 q + 3), and the bins' hi and lo parts
+// (A operand: lane 4 q + h, head h, codewords 4 q .. 4 q + 3) accumulate into the byte layout's O pair 2 G,
+// 2 G + 1 of group G = 8 g + cc.
 template <int G>
-__device__ __forceinline__ void wide_value_unit(const uint4 (&rows)[kRes], const h4 (&idr)[kRes], const h4& pt,
-                                                f4 (&O)[2 * kGroups]) {
+__device__ __forceinline__ void wide_bin_unit(const uint4& row, const h4& ident, const h4& ahi, const h4& alo,
+                                              f4 (&O)[2 * kGroups]) {
   const f4 z = {0.f, 0.f, 0.f, 0.f};
-  f4 x0 = mfma(cat(as_h2(rows[0].x), as_h2(rows[0].y)), idr[0], z);
-  f4 x1 = mfma(cat(as_h2(rows[0].z), as_h2(rows[0].w)), idr[0], z);
-#pragma unroll
-  for (int rho = 1; rho < kRes; ++rho) {
-    x0 = mfma(cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), idr[rho], x0);
-    x1 = mfma(cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), idr[rho], x1);
-  }
-  O[2 * G] = mfma(pt, to_h4(x0), O[2 * G]);
-  O[2 * G + 1] = mfma(pt, to_h4(x1), O[2 * G + 1]);
+  const h4 v0 = to_h4(mfma(cat(as_h2(row.x), as_h2(row.y)), ident, z));  // exact: fp16 values
+  const h4 v1 = to_h4(mfma(cat(as_h2(row.z), as_h2(row.w)), ident, z));
+  O[2 * G] = mfma(ahi, v0, O[2 * G]);
+  O[2 * G] = mfma(alo, v0, O[2 * G]);
+  O[2 * G + 1] = mfma(ahi, v1, O[2 * G + 1]);
+  O[2 * G + 1] = mfma(alo, v1, O[2 * G + 1]);
 }
 
 __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
@@ -248,17 +255,17 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   const h4 ident = identity_b(lane);
   const h4 zero4 = {(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
 
-  // ------------------------------------------------------------------------- pass machinery
-  // Staging: during pass p, each thread fetches one 16-byte unit per block of pass p + 1's codebook chunk
-  // and writes it into slot (p + 1) % 2 one block later (that slot's last reader, pass p - 1, finished at
-  // the barrier that ended it).
+  // ------------------------------------------------------------------------- key passes
+  // Staging: during pass c, each thread fetches one 16-byte unit per block of pass c + 1's codebook chunk
+  // and writes it into slot (c + 1) % 2 one block later (that slot's last reader, pass c - 1, finished at
+  // the barrier that ended it). The last pass writes zeros there instead: that slot then holds the value bins.
   uint4 stage;
-  auto stage_src = [&](int pn, int i) {
-    const int pc = min(pn, 2 * nch - 1);
-    const bool key = pc < nch;
-    return slot_unit_src(key ? cb_k : cb_v, R, kRes * (key ? pc : pc - nch), i * kThreads + tid);
+  auto stage_load = [&](int pn, int i) {
+    if (pn < nch)
+      stage = *reinterpret_cast<const uint4*>(slot_unit_src(cb_k, R, kRes * pn, i * kThreads + tid));
+    else
+      stage = make_uint4(0u, 0u, 0u, 0u);
   };
-  auto stage_load = [&](int pn, int i) { stage = *reinterpret_cast<const uint4*>(stage_src(pn, i)); };
   auto stage_store = [&](int pn, int i) {
     *reinterpret_cast<uint4*>(lds + (pn & 1) * kSlot + (i * kThreads + tid) * 16) = stage;
   };
@@ -276,17 +283,12 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   f4 sc[kMaxBlocks];
 #pragma unroll
   for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
-  f4 O[2 * kGroups];  // value accumulators (zeroed after the key passes)
-  h4 pth[kMaxBlocks];
 
-  // One pass: kind 0 = keys (chunk c, pass p = c), kind 1 = values (pass p = nch + c). Units (g, cc) of
-  // the wave's blocks form one software pipeline: the gathers of unit n + kWAhead go out before the
-  // arithmetic of unit n; block i + 1's row offsets are computed (and its next-pass words requested) at
-  // the start of block i.
-  auto pass = [&](auto kind_c, const int c) {
-    constexpr bool kKey = decltype(kind_c)::value == 0;
-    const int p = kKey ? c : nch + c;
-    const int slot_off = (p & 1) * kSlot;
+  // One key pass (chunk c). Units (g, cc) of the wave's blocks form one software pipeline: the gathers of
+  // unit n + kWAhead go out before the arithmetic of unit n; block i + 1's row offsets are computed (and its
+  // next-pass words requested) at the start of block i.
+  auto key_pass = [&](const int c) {
+    const int slot_off = (c & 1) * kSlot;
     const int nres = min(kRes, R - kRes * c);
     h4 idr[kRes];  // the identity for the pass's residuals, the zero matrix past R
 #pragma unroll
@@ -300,7 +302,7 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i < kMaxBlocks) {
         addresses(c, slot_off, code[i], adr[i & 1]);
-        request_words(p + 1, i);
+        request_words(c + 1, i);
       }
     };
     auto issue = [&](auto mc) {
@@ -319,59 +321,145 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
       constexpr int i = decltype(ic)::value;
       __builtin_amdgcn_s_setprio(block_prio(i));
       block_addresses(std::integral_constant<int, i + 1>{});
-      if (i > 0) stage_store(p + 1, i - 1);
-      stage_load(p + 1, i);
+      if (i > 0) stage_store(c + 1, i - 1);
+      stage_load(c + 1, i);
       if (i < my_blocks) {
-        if constexpr (kKey) {
-          f4 acc[2] = {sc[i], (f4){0.f, 0.f, 0.f, 0.f}};  // real-part and imaginary-part chains
-          float4 ph[2];
-          auto unit = [&](auto uc) {
-            constexpr int u = decltype(uc)::value, n = kUnits * i + u;
-            constexpr int G = (u / kChunks) * 8 + u % kChunks;  // byte-layout group of (g, cc)
-            ph[0] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G) * 64 + lane) * 16);
-            ph[1] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G + 1) * 64 + lane) * 16);
-            __builtin_amdgcn_sched_barrier(0);
-            issue(std::integral_constant<int, n + kWAhead>{});
-            __builtin_amdgcn_sched_barrier(0);
-            wide_key_unit<G>(rows[n % kWBufs], idr, ph[0], ph[1], cur[G / 4], acc);
-          };
-          static_for<kUnits>(unit);
-          sc[i] = acc[0] + acc[1];
+        f4 acc[2] = {sc[i], (f4){0.f, 0.f, 0.f, 0.f}};  // real-part and imaginary-part chains
+        float4 ph[2];
+        auto unit = [&](auto uc) {
+          constexpr int u = decltype(uc)::value, n = kUnits * i + u;
+          constexpr int G = (u / kChunks) * 8 + u % kChunks;  // byte-layout group of (g, cc)
+          ph[0] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G) * 64 + lane) * 16);
+          ph[1] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G + 1) * 64 + lane) * 16);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(std::integral_constant<int, n + kWAhead>{});
+          __builtin_amdgcn_sched_barrier(0);
+          wide_key_unit<G>(rows[n % kWBufs], idr, ph[0], ph[1], cur[G / 4], acc);
+        };
+        static_for<kUnits>(unit);
+        sc[i] = acc[0] + acc[1];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
-        } else {
-          auto unit = [&](auto uc) {
-            constexpr int u = decltype(uc)::value, n = kUnits * i + u;
-            constexpr int G = (u / kChunks) * 8 + u % kChunks;
-            __builtin_amdgcn_sched_barrier(0);
-            issue(std::integral_constant<int, n + kWAhead>{});
-            __builtin_amdgcn_sched_barrier(0);
-            wide_value_unit<G>(rows[n % kWBufs], idr, pth[i], O);
-          };
-          static_for<kUnits>(unit);
-        }
+        for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
       }
     };
     static_for<kMaxBlocks>(block);
     __builtin_amdgcn_s_setprio(0);
-    stage_store(p + 1, kMaxBlocks - 1);
-    lds_barrier();  // pass p + 1's chunk is complete; every wave is done with slot p % 2
+    stage_store(c + 1, kMaxBlocks - 1);
+    lds_barrier();  // slot (c + 1) % 2 is complete; every wave is done with slot c % 2
   };
 
-  for (int c = 0; c < nch; ++c) pass(std::integral_constant<int, 0>{}, c);
+  for (int c = 0; c < nch; ++c) key_pass(c);
 
-  float m_w[kGqa], l_w[kGqa];
-  wave_softmax_regs<kW>(sc, my_blocks, wave, lane, nvalid, a.scale, m_w, l_w);
+  // ------------------------------------------------------------------------- softmax weights
+  // M = the workgroup's maximum scaled score per head (finite: the split holds a valid token); each wave's
+  // weights p = e^{s - M} in fixed point, two heads per 64-bit word; l_w = the wave's sum of them.
+  float M[kGqa], l_w[kGqa];
+  uint64_t fx[kMaxBlocks][2];
   {
-    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    float* wg_m = reinterpret_cast<float*>(lds + kPhase);  // [kW][kGqa] (the phases are no longer read)
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i) pth[i] = to_h4(mfma(to_h4(sc[i]), ident, z));  // quad transpose of p
+    for (int h = 0; h < kGqa; ++h) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kMaxBlocks; ++i) {
+        const bool ok = i < my_blocks && (wave + kW * i) * 64 + lane < nvalid;
+        sc[i][h] = ok ? sc[i][h] * a.scale : -INFINITY;
+        mx = fmaxf(mx, sc[i][h]);
+      }
+      mx = wave_max(mx);
+      if (lane == 0) wg_m[wave * kGqa + h] = mx;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      M[h] = wg_m[h];
+#pragma unroll
+      for (int w = 1; w < kW; ++w) M[h] = fmaxf(M[h], wg_m[w * kGqa + h]);
+    }
+    float lsum[kGqa] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMaxBlocks; ++i) {
+      uint32_t qv[kGqa];
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h) {
+        // masked tokens: e^{-inf} = 0
+        qv[h] = __float2uint_rn(__expf(sc[i][h] - M[h]) * static_cast<float>(1 << kFxBits));
+        lsum[h] += static_cast<float>(qv[h]);
+      }
+      fx[i][0] = qv[0] | (static_cast<uint64_t>(qv[1]) << 32);
+      fx[i][1] = qv[2] | (static_cast<uint64_t>(qv[3]) << 32);
+    }
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) l_w[h] = wave_sum(lsum[h]) * (1.f / static_cast<float>(1 << kFxBits));
   }
 
+  // ------------------------------------------------------------------------- value bins
+  // bins[g][r][hp][l] (64-bit words, heads 2 hp and 2 hp + 1) in the slot the last key pass zeroed. Window c
+  // of every block: its 8 indices select the bins its weights go to; the words of window c + 1 are requested
+  // in their place (one window ahead, as in the key passes).
+  unsigned long long* bins = reinterpret_cast<unsigned long long*>(lds + (nch & 1) * kSlot);
+  for (int c = 0; c < nch; ++c) {
+    const int nres = min(kRes, R - kRes * c);
+    auto block = [&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      // (every block requests its words, as in the key passes, so that the loads stay in flight)
+      uint32_t x0, x1;
+      packed_window(code[i].x, code[i].y, packed_window_shift(c), x0, x1);
+      request_words(nch + c + 1, i);
+      if (i < my_blocks) {
+        static_for<kIdx>([&](auto fc) {
+          constexpr int f = decltype(fc)::value, rho = f >> 1, g = f & 1;
+          if (rho < nres) {
+            unsigned long long* bp = bins + ((g * R + kRes * c + rho) * 2) * kWN + packed_index<f>(x0, x1);
+            __hip_atomic_fetch_add(bp, fx[i][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(bp + kWN, fx[i][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        });
+      }
+    };
+    static_for<kMaxBlocks>(block);
+  }
+  lds_barrier();  // every token's weights are in the bins
+
+  // ------------------------------------------------------------------------- bins x value codebook
+  // The wave takes the (g, r) of its share (every kW-th of the 2 R), each one MFMA column sweep over the 8
+  // chunks of group g. A operand: bins of head h = lane & 3, codewords 4 (lane >> 2) .. + 3, as fp16 hi + lo of
+  // their value in units of 1 (exact to 2^-22 relative).
+  f4 O[2 * kGroups];
 #pragma unroll
   for (int c = 0; c < 2 * kGroups; ++c) O[c] = (f4){0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nch; ++c) pass(std::integral_constant<int, 1>{}, c);
+  {
+    const int hh = lane & 3, l4 = (lane >> 2) * 4;
+    static_for<kWG>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      for (int r = ((wave - g * R) % kW + kW) % kW; r < R; r += kW) {
+        const f16* vrow = cb_v + ((static_cast<int64_t>(g) * R + r) * kWN + lane) * (kWRow / 2);
+        uint4 row[kChunks];
+#pragma unroll
+        for (int cc = 0; cc < kChunks; ++cc) row[cc] = *reinterpret_cast<const uint4*>(vrow + 8 * cc);
+        const uint4* bq = reinterpret_cast<const uint4*>(bins + ((g * R + r) * 2 + (hh >> 1)) * kWN + l4);
+        const uint4 u0 = bq[0], u1 = bq[1];  // codewords l4, l4 + 1 | l4 + 2, l4 + 3: (heads 2 hp, 2 hp + 1)
+        const bool odd = hh & 1;
+        const uint32_t cnt[4] = {odd ? u0.y : u0.x, odd ? u0.w : u0.z, odd ? u1.y : u1.x, odd ? u1.w : u1.z};
+        h4 ahi, alo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const Split2 sp = split2(static_cast<float>(cnt[k]) * (1.f / static_cast<float>(1 << kFxBits)));
+          ahi[k] = sp.hi;
+          alo[k] = sp.lo;
+        }
+        static_for<kChunks>([&](auto ccc) {
+          constexpr int cc = decltype(ccc)::value;
+          wide_bin_unit<8 * g + cc>(row[cc], ident, ahi, alo, O);
+        });
+      }
+    });
+  }
 
+  // every wave's weights are relative to the same M
+  float m_w[kGqa];
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h) m_w[h] = M[h];
   attn_epilogue<kW>(a, lds, wave_ml, is_last, lane_id(), wave * 64 + lane_id(), wave, O, b, kv, split, L, S, bh0,
                     out_bh, m_w, l_w);
 }

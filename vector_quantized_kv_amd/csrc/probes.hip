@@ -1,5 +1,6 @@
-// Measurement probes for the benchmark (declared in commvq_probes.h): a streaming HBM read and the LDS
-// random-gather throughput. Not part of the attention path; built into libcommvq_probes.so.
+// Measurement probes for the benchmark (declared in commvq_probes.h): a streaming HBM read, the LDS
+// random-gather throughput and the throughput of random 64-bit LDS atomic adds. Not part of the attention
+// path; built into libcommvq_probes.so.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -59,6 +60,35 @@ __global__ void __launch_bounds__(kProbeWaves * 64) lds_gather_kernel(int iters,
   if (iters == -1) sink[0] = kNever;  // (never: iters >= 1) keeps sink an argument of the kernel
 }
 
+// Random 64-bit LDS adds into bins laid out as the bit-packed attention kernel's value bins: 42 units
+// (R = 21 residuals x 2 groups) of [2 head pairs][64 codewords] 64-bit words, 43 KiB; per unit every lane adds
+// to the same random codeword of both head pairs (two wave instructions). The bins' total is written to sink
+// (so the adds are kept), and it equals 2 x 42 x iters x 512 per workgroup.
+constexpr int kBinUnits = 42;
+
+__global__ void __launch_bounds__(kProbeWaves * 64) lds_bin_add_kernel(int iters, unsigned long long* sink) {
+  // 160 KiB, of which the bins use the first 43 KiB: one workgroup per CU, as in the attention kernel
+  __shared__ unsigned long long bins[kLdsBytes / 8];
+  static_assert(kBinUnits * 2 * 64 * 8 <= kLdsBytes, "the bins fit the array");
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBinUnits * 2 * 64; i += kProbeWaves * 64) bins[i] = 0;
+  __syncthreads();
+  uint32_t x = 0x2545f491u ^ (static_cast<uint32_t>(tid) * 0x9e3779b1u) ^ (blockIdx.x * 0x85ebca6bu);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll 6
+    for (int u = 0; u < kBinUnits; ++u) {
+      x = x * 1664525u + 1013904223u;
+      unsigned long long* b = bins + u * 128 + (x >> 26);
+      __hip_atomic_fetch_add(b, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_add(b + 64, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  __syncthreads();
+  unsigned long long t = 0;
+  for (int i = tid; i < kBinUnits * 2 * 64; i += kProbeWaves * 64) t += bins[i];
+  atomicAdd(sink, t);
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,6 +98,13 @@ int commvq_probe_read_stream(const void* buf, size_t bytes, int blocks, void* si
     return static_cast<int>(hipErrorInvalidValue);
   read_stream_kernel<<<blocks, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const u32x4*>(buf), bytes / 16,
                                                                           static_cast<uint32_t*>(sink));
+  return static_cast<int>(hipGetLastError());
+}
+
+int commvq_probe_lds_bin_add(int iters, int blocks, void* sink, void* stream) {
+  if (!sink || blocks < 1 || iters < 1) return static_cast<int>(hipErrorInvalidValue);
+  lds_bin_add_kernel<<<blocks, kProbeWaves * 64, 0, static_cast<hipStream_t>(stream)>>>(
+      iters, static_cast<unsigned long long*>(sink));
   return static_cast<int>(hipGetLastError());
 }
 
