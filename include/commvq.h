@@ -240,7 +240,7 @@ int commvq_codebook_update(const commvq_dims* d /* host */, const void* x, const
 /* ---------------------------------------------------------------------------------------------
  * Code unpack exactly as the attention kernels read codes: out[kv][r][t][g] = index (int32).
  * codes [Hkv][R][total_tokens][G] uint8, or (bit-packed layout) the word planes
- * [Hkv][ceil(12 R / 32)][total_tokens] uint32, read in the attention kernel's windows of 4 residuals.
+ * [Hkv][ceil(12 R / 32)][total_tokens] uint32, read in the attention kernel's windows of 8 residuals (3 words).
  * Used to test the unpack bit-exactly.
  * ------------------------------------------------------------------------------------------- */
 int commvq_debug_unpack(const commvq_dims* d /* host */, const uint8_t* codes, int64_t total_tokens /* host */,

@@ -10,10 +10,15 @@
 // A token's R x G indices are one little-endian bitstream of 32-bit words, index (r, g) at bit 6 (r G + g);
 // word w of every token of a KV head lies in word plane w ([Hkv][words][T]).
 //
-// The key codebooks (R x 16 KiB per KV head) do not fit in LDS, so the key side runs in passes of kRes
-// residuals, c = 0 .. nch-1: pass c's codebook chunk (kRes residuals x 2 groups x 8 KiB) sits in LDS slot
-// c % 2 while the chunk of pass c + 1 is staged through registers into the other slot. Scores are linear in
-// the residuals, so each pass adds its chunk's share to the MFMA accumulators.
+// The key codebooks (R x 16 KiB per KV head) do not fit in LDS, so the key side runs in passes. A pass holds
+// 8 tables of 8 KiB (64 KiB) in one of two LDS slots while the next pass's tables are staged through registers
+// into the other slot. Index window c of the bitstream (residuals kRes c .. kRes c + kRes - 1) takes two passes,
+// one per group g, of kRes residuals each; a last window of at most kRes / 2 residuals takes one pass of
+// kRes / 2 residuals of both groups. Scores are linear in the residuals, so each pass adds its share to the MFMA
+// accumulators. The rotation and the contraction run once per pass and unit, so a pass over more residuals of
+// one group costs half the arithmetic per gathered row; the short last pass keeps a window of a few residuals
+// from gathering rows that add nothing. The tables of residuals past R in the last pass hold zero rows, so
+// every pass sums all of its tables and no pass branches inside its units.
 //
 // Values take the pages' own form (pith.science verdict for arXiv 2506.18879, key_machinery and
 // forward_implications: the softmax weights multiply the value codes before the codebook product): every
@@ -28,13 +33,12 @@
 // 64-token block, 4 GQA heads per KV head, the per-64-token RoPE phase on the query and the per-lane phase on
 // the keys. A 16-byte chunk cc of the 128-byte row of group g holds RoPE pairs 32 g + 4 cc .. + 3, exactly
 // the pairs of the byte layout's group 8 g + cc, so the key contraction's query operand and the epilogue are
-// the byte layout's. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's kRes residual
-// rows, sums them in fp32 on the matrix core (an MFMA with the identity as A adds a lane's four fp16 values to
-// its fp32 accumulator), rotates the sum by the lane's fine phases in fp32 (phases read from a 32 KiB LDS
-// table) and contracts it with the fp32 block query on the fp32 matrix core (v_mfma_f32_4x4x1_16b_f32, query
-// broadcast from one 4-lane block per dim): no fp16 rounding on the key side, so wide logit ranges keep the
-// attention within tolerance. Residuals past R in the last pass use a zero matrix in place of the identity
-// (their gathers read a real row and add nothing).
+// the byte layout's. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's residual rows
+// (residuals past R, in the last window, are skipped), sums them in fp32 on the matrix core (an MFMA with the
+// identity as A adds a lane's four fp16 values to its fp32 accumulator), rotates the sum by the lane's fine
+// phases in fp32 (phases read from a 32 KiB LDS table) and contracts it with the fp32 block query on the fp32
+// matrix core (v_mfma_f32_4x4x1_16b_f32, query broadcast from one 4-lane block per dim): no fp16 rounding on
+// the key side, so wide logit ranges keep the attention within tolerance.
 // Rows are stored with their 16-byte chunks permuted by the codeword (physical chunk = cc xor
 // ((l >> 1) & 7)), so the 16 lanes that share an LDS cycle land on random ones of the 16 bank groups
 // instead of the two that a 128-byte row stride would give them.
@@ -47,11 +51,11 @@ constexpr int kWG = kWideGroups;                 // index groups per head (2)
 constexpr int kWN = kWideCodes;                  // codewords per residual codebook (64)
 constexpr int kWRow = kHeadDim / kWG * 2;        // bytes per fp16 codeword row (128)
 constexpr int kWTab = kWN * kWRow;               // bytes per (residual, group) table (8 KiB)
-constexpr int kRes = kWideResPerPass;            // residuals per pass (4)
-constexpr int kIdx = kRes * kWG;                 // indices per pass (8)
-constexpr int kSlot = kIdx * kWTab;              // bytes per codebook slot (64 KiB)
+constexpr int kRes = kWideResPerPass;            // residuals per index window (8)
+constexpr int kIdx = kRes * kWG;                 // indices per window (16)
+constexpr int kTables = 8;                       // (residual, group) tables per codebook slot
+constexpr int kSlot = kTables * kWTab;           // bytes per codebook slot (64 KiB)
 constexpr int kChunks = kWRow / 16;              // 16-byte chunks per row (8)
-constexpr int kUnits = kWG * kChunks;            // units (g, cc) per block (16)
 constexpr int kW = 8;                            // waves per workgroup
 constexpr int kThreads = kW * 64;
 constexpr int kPhase = 2 * kSlot;                // LDS offset of the fp32 fine phases [G][h][lane][2 pairs]
@@ -65,12 +69,10 @@ static_assert(kWG * kWideMaxResiduals * 2 * kWN * 8 <= kSlot, "the value bins fi
 static_assert((static_cast<int64_t>(kW) * kMaxBlocks * 64 << kFxBits) <= (static_cast<int64_t>(1) << 32),
               "a bin's 32-bit halves (each at most 2^19 per token) never carry into each other");
 
-// Global source of 16-byte unit u of the slot holding residuals r0 .. r0 + kRes - 1 (unit u = table
-// f = 2 rho + g, codeword l, physical chunk pc). Residuals past R read residual R - 1 (never used).
-__device__ __forceinline__ const unsigned char* slot_unit_src(const f16* cb_kv, int R, int r0, int u) {
-  const int f = u >> 9, l = (u >> 3) & (kWN - 1), pc = u & 7;
-  const int rho = f >> 1, g = f & 1;
-  const int r = min(r0 + rho, R - 1);
+// Global source of 16-byte unit u (0 .. 511) of the LDS table of residual r, group g: codeword l = u / 8, physical
+// chunk pc = u % 8.
+__device__ __forceinline__ const unsigned char* table_unit_src(const f16* cb_kv, int R, int g, int r, int u) {
+  const int l = (u >> 3) & (kWN - 1), pc = u & 7;
   const int cc = pc ^ ((l >> 1) & 7);
   return reinterpret_cast<const unsigned char*>(cb_kv + ((static_cast<int64_t>(g) * R + r) * kWN + l) * (kWRow / 2)) +
          cc * 16;
@@ -82,21 +84,21 @@ __device__ __forceinline__ f4 mfma32_bcast(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 4, ABID, 0);
 }
 
-// Key unit of byte-layout group G (RoPE pairs 4G .. 4G+3): the sum of the unit's kRes residual chunks, in fp32 on
-// the matrix core (with A = identity, lane 4b + j of D receives its own B values plus C; idr[rho] is the zero
-// matrix for residuals past R), rotated by the lane's fine phases (p0: pairs 4G, 4G+1; p1: 4G+2, 4G+3, each
-// (cos, sin)) in fp32, then contracted with the block query q'' (pair j = 4G + u broadcast from block j mod 16):
-// q''_re x w_re into acc[0], q''_im x w_im into acc[1].
-template <int G>
-__device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[kRes], const h4 (&idr)[kRes], const float4& p0,
+// Key unit of byte-layout group G = 8 g + CC (RoPE pairs 4G .. 4G+3): the sum of the unit's NR residual chunks
+// (zero rows past R), in fp32 on the matrix core (with A = identity, lane 4b + j of D receives its own B values
+// plus C), rotated by the lane's fine phases (p0: pairs 4G, 4G+1; p1: 4G+2, 4G+3, each (cos, sin)) in fp32,
+// then contracted with the block query q'' (pair j = 4G + u broadcast from block j mod 16, which does not
+// depend on g): q''_re x w_re into acc[0], q''_im x w_im into acc[1].
+template <int NR, int CC>
+__device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[NR], const h4& ident, const float4& p0,
                                               const float4& p1, const float2& A, f4 (&acc)[2]) {
   const f4 z = {0.f, 0.f, 0.f, 0.f};
-  f4 k0 = mfma(idr[0], cat(as_h2(rows[0].x), as_h2(rows[0].y)), z);
-  f4 k1 = mfma(idr[0], cat(as_h2(rows[0].z), as_h2(rows[0].w)), z);
+  f4 k0 = mfma(ident, cat(as_h2(rows[0].x), as_h2(rows[0].y)), z);
+  f4 k1 = mfma(ident, cat(as_h2(rows[0].z), as_h2(rows[0].w)), z);
 #pragma unroll
-  for (int rho = 1; rho < kRes; ++rho) {
-    k0 = mfma(idr[rho], cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), k0);
-    k1 = mfma(idr[rho], cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), k1);
+  for (int rho = 1; rho < NR; ++rho) {
+    k0 = mfma(ident, cat(as_h2(rows[rho].x), as_h2(rows[rho].y)), k0);
+    k1 = mfma(ident, cat(as_h2(rows[rho].z), as_h2(rows[rho].w)), k1);
   }
   const float cs[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
   float w[8];
@@ -110,7 +112,7 @@ __device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[kRes], const h
   __builtin_amdgcn_sched_barrier(0);  // the fp32 MFMAs run as one burst (they do not overlap VALU work)
   static_for<8>([&](auto dc) {
     constexpr int d = decltype(dc)::value;
-    constexpr int abid = (4 * G + d / 2) & 15;
+    constexpr int abid = (4 * CC + d / 2) & 15;
     acc[d & 1] = mfma32_bcast<abid>((d & 1) ? A.y : A.x, w[d], acc[d & 1]);
   });
   __builtin_amdgcn_sched_barrier(0);
@@ -146,7 +148,17 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   // same KV head's data at the same moment and so start on different parts of it (spread over the L2 channels)
   const int part = __builtin_amdgcn_readfirstlane((wave + split) & (kW - 1));
   const int R = a.n_residuals, Wd = a.record_words;
-  const int nch = (R + kRes - 1) / kRes;  // passes per kind
+  const int nch = (R + kRes - 1) / kRes;         // index windows
+  const int tail = R - kRes * (nch - 1);          // residuals in the last window (1 .. kRes)
+  const bool tail_both = 2 * tail <= kRes;        // the last window in one pass over both groups
+  const int npass = 2 * (nch - 1) + (tail_both ? 1 : 2);
+  // (group, residual) of table t of pass p's slot (r >= R: a table of zero rows)
+  auto pass_table = [&](int p, int t, int& g, int& r) {
+    const int c = min(p >> 1, nch - 1);
+    const bool both = tail_both && p == npass - 1;
+    g = both ? (t & 1) : (p & 1);
+    r = kRes * c + (both ? t >> 1 : t);
+  };
   const int64_t cb_stride = static_cast<int64_t>(kWG) * R * kWN * (kWRow / 2);
   const f16* cb_k = static_cast<const f16*>(a.k_cb) + kv * cb_stride;
   const f16* cb_v = static_cast<const f16*>(a.v_cb) + kv * cb_stride;
@@ -168,8 +180,8 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
       for (int i = tid; i < kGqa * kHeadDim; i += kThreads) out_bh[i] = 0.f;
     return;
   }
-  // (1) fp32 fine phases (group-major, the byte layout's groups) and the codebook chunk of pass 0 (key
-  // residuals 0 .. kRes-1), straight into LDS.
+  // (1) fp32 fine phases (group-major, the byte layout's groups) and the tables of pass 0 (wave part moves
+  // table part), straight into LDS.
   {
     constexpr int kFineChunks = kPhaseBytes / 16;
     const unsigned char* src = reinterpret_cast<const unsigned char*>(a.rope + kRopeFine32gOffset);
@@ -178,10 +190,20 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
       const int c = (part * (kFineChunks / kThreads) + i) * 64;
       __builtin_amdgcn_global_load_lds(src + (c + lane) * 16, lds + kPhase + c * 16, 16, 0, 0);
     }
+    static_assert(kTables == kW && kWTab / 16 == kMaxBlocks * 64, "one table per wave, 64 units per load");
+    int g0, r0;
+    pass_table(0, part, g0, r0);
+    if (r0 < R) {
 #pragma unroll
-    for (int i = 0; i < kMaxBlocks; ++i) {
-      const int u0 = part * (kSlot / 16 / kW) + i * 64;
-      __builtin_amdgcn_global_load_lds(slot_unit_src(cb_k, R, 0, u0 + lane), lds + u0 * 16, 16, 0, 0);
+      for (int i = 0; i < kMaxBlocks; ++i) {
+        const int u = i * 64 + lane;
+        __builtin_amdgcn_global_load_lds(table_unit_src(cb_k, R, g0, r0, u), lds + part * kWTab + (i * 64) * 16, 16,
+                                         0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kMaxBlocks; ++i)
+        *reinterpret_cast<uint4*>(lds + part * kWTab + (i * 64 + lane) * 16) = make_uint4(0u, 0u, 0u, 0u);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -215,25 +237,25 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // (3) index words of pass 0 for every block. Pass p reads the two words of its window (chunk c of the
-  // record) from their word planes: a wave's 64 tokens are 256 contiguous bytes of each plane, and the word
-  // that two consecutive passes share is read again while it still sits in L2. Requests past the last pass
-  // read the last pass's words, so every pass issues the same loads (clamped rows and words, always in bounds).
+  // (3) index words of pass 0 for every block. Step p (key passes p < npass, then value windows p - npass)
+  // reads the three words of its window from their word planes: a wave's 64 tokens are 256 contiguous bytes
+  // of each plane. The two key passes of a window read the same words (the second time from L2). Requests past
+  // the last step read the last step's words, so every step issues the same loads (clamped rows and words,
+  // always in bounds).
   const int64_t T = a.total_tokens;
   const uint32_t* kw = reinterpret_cast<const uint32_t*>(a.k_codes) + static_cast<int64_t>(kv) * Wd * T;
   const uint32_t* vw = reinterpret_cast<const uint32_t*>(a.v_codes) + static_cast<int64_t>(kv) * Wd * T;
-  uint2 code[kMaxBlocks];
+  uint3 code[kMaxBlocks];
   auto request_words = [&](int pn, int i) {
-    const int pc = min(pn, 2 * nch - 1);
-    const int c = pc < nch ? pc : pc - nch;
+    const int pc = min(pn, npass + nch - 1);
+    const int c = pc < npass ? min(pc >> 1, nch - 1) : pc - npass;
     const int w0 = packed_window_word(c);
-    const int w1 = min(w0 + 1, Wd - 1);
-    const uint32_t* rec = (pc < nch ? kw : vw) + token_row(i);
-    code[i] = make_uint2(rec[w0 * T], rec[w1 * T]);
+    const uint32_t* rec = (pc < npass ? kw : vw) + token_row(i);
+    code[i] = make_uint3(rec[min(w0, Wd - 1) * T], rec[min(w0 + 1, Wd - 1) * T], rec[min(w0 + 2, Wd - 1) * T]);
   };
 #pragma unroll
   for (int i = 0; i < kMaxBlocks; ++i) request_words(0, i);
-  constexpr int kPrologueRecords = 2 * kMaxBlocks;
+  constexpr int kPrologueRecords = 3 * kMaxBlocks;
 
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kPrologueRecords));
@@ -253,66 +275,66 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     stepE[k] = e;
   }
   const h4 ident = identity_b(lane);
-  const h4 zero4 = {(f16)0.f, (f16)0.f, (f16)0.f, (f16)0.f};
 
   // ------------------------------------------------------------------------- key passes
-  // Staging: during pass c, each thread fetches one 16-byte unit per block of pass c + 1's codebook chunk
-  // and writes it into slot (c + 1) % 2 one block later (that slot's last reader, pass c - 1, finished at
-  // the barrier that ended it). The last pass writes zeros there instead: that slot then holds the value bins.
+  // Staging: during pass p, each thread fetches one 16-byte unit per block of pass p + 1's tables (block i:
+  // table i) and writes it into slot (p + 1) % 2 one block later (that slot's last reader, pass p - 1, finished
+  // at the barrier that ended it). The last pass writes zeros there instead: that slot then holds the value bins.
   uint4 stage;
   auto stage_load = [&](int pn, int i) {
-    if (pn < nch)
-      stage = *reinterpret_cast<const uint4*>(slot_unit_src(cb_k, R, kRes * pn, i * kThreads + tid));
+    int g = 0, r = R;
+    if (pn < npass) pass_table(pn, i, g, r);
+    if (r < R)
+      stage = *reinterpret_cast<const uint4*>(table_unit_src(cb_k, R, g, r, tid));
     else
       stage = make_uint4(0u, 0u, 0u, 0u);
   };
   auto stage_store = [&](int pn, int i) {
     *reinterpret_cast<uint4*>(lds + (pn & 1) * kSlot + (i * kThreads + tid) * 16) = stage;
   };
-  // LDS offsets (without the table offset f * kWTab) of the rows of a block's kIdx indices in pass p.
-  auto addresses = [&](int c, int slot_off, const uint2 w, uint32_t (&adr)[kIdx]) {
-    uint32_t x0, x1;
-    packed_window(w.x, w.y, packed_window_shift(c), x0, x1);
-    static_for<kIdx>([&](auto fc) {
-      constexpr int f = decltype(fc)::value;
-      const uint32_t idx = packed_index<f>(x0, x1);
-      adr[f] = slot_off + idx * kWRow + ((idx >> 1) & 7) * 16;  // (residuals past R: a real row, added with 0)
-    });
-  };
 
   f4 sc[kMaxBlocks];
 #pragma unroll
   for (int i = 0; i < kMaxBlocks; ++i) sc[i] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  // One key pass (chunk c). Units (g, cc) of the wave's blocks form one software pipeline: the gathers of
-  // unit n + kWAhead go out before the arithmetic of unit n; block i + 1's row offsets are computed (and its
-  // next-pass words requested) at the start of block i.
-  auto key_pass = [&](const int c) {
-    const int slot_off = (c & 1) * kSlot;
-    const int nres = min(kRes, R - kRes * c);
-    h4 idr[kRes];  // the identity for the pass's residuals, the zero matrix past R
-#pragma unroll
-    for (int rho = 0; rho < kRes; ++rho) idr[rho] = rho < nres ? ident : zero4;
-    uint32_t adr[2][kIdx];
-    uint4 rows[kWBufs][kRes];
+  // One key pass over NR residuals of NG = kRes / NR groups of window c (NG = 1: group g, pass 2 c + g; NG = 2:
+  // the last pass). Its slot holds table t = rho (NG = 1) or 2 rho + g (NG = 2) for residual kRes c + rho.
+  // Units (g, cc) of the wave's blocks form one software pipeline: the gathers of unit n + kWAhead go out before
+  // the arithmetic of unit n; block i + 1's row offsets are computed (and its next-pass words requested) at the
+  // start of block i.
+  auto key_pass = [&](auto nrc, const int g, const int c) {
+    constexpr int NR = decltype(nrc)::value, NG = kRes / NR, NU = kChunks * NG;
+    const int p = NG == 1 ? 2 * c + g : npass - 1;
+    const int slot_off = (p & 1) * kSlot;
+    // group g's indices 2 rho + g of the window are indices 2 rho of the window shifted by 6 g
+    const int sh = NG == 1 ? kWideBits * g : 0;
+    const unsigned char* phases = lds + kPhase + (NG == 1 ? g * (kChunks * 2 * 64 * 16) : 0);
+    uint32_t adr[2][kTables];
+    uint4 rows[kWBufs][NR];
     float2 cur[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) cur[k] = qc0[k];
     auto block_addresses = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i < kMaxBlocks) {
-        addresses(c, slot_off, code[i], adr[i & 1]);
-        request_words(c + 1, i);
+        const uint32_t x0 = __builtin_amdgcn_alignbit(code[i].y, code[i].x, sh);
+        const uint32_t x1 = __builtin_amdgcn_alignbit(code[i].z, code[i].y, sh);
+        const uint32_t x2 = code[i].z >> sh;
+        static_for<kTables>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          const uint32_t idx = packed_index<NG == 1 ? 2 * t : t>(x0, x1, x2);
+          adr[i & 1][t] = slot_off + t * kWTab + idx * kWRow + ((idx >> 1) & 7) * 16;
+        });
+        request_words(p + 1, i);
       }
     };
     auto issue = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      if constexpr (m < kUnits * kMaxBlocks) {
-        constexpr int i = m / kUnits, u = m % kUnits, g = u / kChunks, cc = u % kChunks;
+      if constexpr (m < NU * kMaxBlocks) {
+        constexpr int i = m / NU, gu = (m % NU) / kChunks, cc = m % kChunks;
 #pragma unroll
-        for (int rho = 0; rho < kRes; ++rho)
-          rows[m % kWBufs][rho] =
-              *reinterpret_cast<const uint4*>(lds + (adr[i & 1][2 * rho + g] ^ (16 * cc)) + (2 * rho + g) * kWTab);
+        for (int rho = 0; rho < NR; ++rho)
+          rows[m % kWBufs][rho] = *reinterpret_cast<const uint4*>(lds + (adr[i & 1][NG * rho + gu] ^ (16 * cc)));
       }
     };
     block_addresses(std::integral_constant<int, 0>{});
@@ -321,22 +343,24 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
       constexpr int i = decltype(ic)::value;
       __builtin_amdgcn_s_setprio(block_prio(i));
       block_addresses(std::integral_constant<int, i + 1>{});
-      if (i > 0) stage_store(c + 1, i - 1);
-      stage_load(c + 1, i);
+      if (i > 0) stage_store(p + 1, i - 1);
+      stage_load(p + 1, i);
       if (i < my_blocks) {
         f4 acc[2] = {sc[i], (f4){0.f, 0.f, 0.f, 0.f}};  // real-part and imaginary-part chains
         float4 ph[2];
+        // query operand pairs: byte-layout groups 8 g .. 8 g + 7 (NG = 1), all groups (NG = 2)
+        const float2 cq[2] = {g ? cur[2] : cur[0], g ? cur[3] : cur[1]};
         auto unit = [&](auto uc) {
-          constexpr int u = decltype(uc)::value, n = kUnits * i + u;
-          constexpr int G = (u / kChunks) * 8 + u % kChunks;  // byte-layout group of (g, cc)
-          ph[0] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G) * 64 + lane) * 16);
-          ph[1] = *reinterpret_cast<const float4*>(lds + kPhase + ((2 * G + 1) * 64 + lane) * 16);
+          constexpr int u = decltype(uc)::value, n = NU * i + u, cc = u % kChunks;
+          constexpr int Gp = u;  // byte-layout group relative to the phase base (8 g + cc, or cc for NG = 1)
+          ph[0] = *reinterpret_cast<const float4*>(phases + ((2 * Gp) * 64 + lane) * 16);
+          ph[1] = *reinterpret_cast<const float4*>(phases + ((2 * Gp + 1) * 64 + lane) * 16);
           __builtin_amdgcn_sched_barrier(0);
           issue(std::integral_constant<int, n + kWAhead>{});
           __builtin_amdgcn_sched_barrier(0);
-          wide_key_unit<G>(rows[n % kWBufs], idr, ph[0], ph[1], cur[G / 4], acc);
+          wide_key_unit<NR, cc>(rows[n % kWBufs], ident, ph[0], ph[1], NG == 1 ? cq[cc / 4] : cur[Gp / 4], acc);
         };
-        static_for<kUnits>(unit);
+        static_for<NU>(unit);
         sc[i] = acc[0] + acc[1];
 #pragma unroll
         for (int k = 0; k < 4; ++k) cur[k] = cmul_conj(cur[k], stepE[k]);
@@ -344,11 +368,12 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     };
     static_for<kMaxBlocks>(block);
     __builtin_amdgcn_s_setprio(0);
-    stage_store(c + 1, kMaxBlocks - 1);
-    lds_barrier();  // slot (c + 1) % 2 is complete; every wave is done with slot c % 2
+    stage_store(p + 1, kMaxBlocks - 1);
+    lds_barrier();  // slot (p + 1) % 2 is complete; every wave is done with slot p % 2
   };
 
-  for (int c = 0; c < nch; ++c) key_pass(c);
+  for (int p = 0; p < npass - (tail_both ? 1 : 0); ++p) key_pass(std::integral_constant<int, kRes>{}, p & 1, p >> 1);
+  if (tail_both) key_pass(std::integral_constant<int, kRes / 2>{}, 0, nch - 1);
 
   // ------------------------------------------------------------------------- softmax weights
   // M = the workgroup's maximum scaled score per head (finite: the split holds a valid token); each wave's
@@ -395,22 +420,21 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
 
   // ------------------------------------------------------------------------- value bins
   // bins[g][r][hp][l] (64-bit words, heads 2 hp and 2 hp + 1) in the slot the last key pass zeroed. Window c
-  // of every block: its 8 indices select the bins its weights go to; the words of window c + 1 are requested
+  // of every block: its 16 indices select the bins its weights go to; the words of window c + 1 are requested
   // in their place (one window ahead, as in the key passes).
-  unsigned long long* bins = reinterpret_cast<unsigned long long*>(lds + (nch & 1) * kSlot);
+  unsigned long long* bins = reinterpret_cast<unsigned long long*>(lds + (npass & 1) * kSlot);
   for (int c = 0; c < nch; ++c) {
     const int nres = min(kRes, R - kRes * c);
     auto block = [&](auto ic) {
       constexpr int i = decltype(ic)::value;
       // (every block requests its words, as in the key passes, so that the loads stay in flight)
-      uint32_t x0, x1;
-      packed_window(code[i].x, code[i].y, packed_window_shift(c), x0, x1);
-      request_words(nch + c + 1, i);
+      const uint3 w = code[i];
+      request_words(npass + c + 1, i);
       if (i < my_blocks) {
         static_for<kIdx>([&](auto fc) {
           constexpr int f = decltype(fc)::value, rho = f >> 1, g = f & 1;
           if (rho < nres) {
-            unsigned long long* bp = bins + ((g * R + kRes * c + rho) * 2) * kWN + packed_index<f>(x0, x1);
+            unsigned long long* bp = bins + ((g * R + kRes * c + rho) * 2) * kWN + packed_index<f>(w.x, w.y, w.z);
             __hip_atomic_fetch_add(bp, fx[i][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_fetch_add(bp + kWN, fx[i][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
           }

@@ -36,7 +36,7 @@ constexpr int kWideGroups = 2;
 constexpr int kWideCodes = 64;
 constexpr int kWideBits = 6;
 constexpr int kWideMaxResiduals = 32;
-constexpr int kWideResPerPass = 4;  // residual codebooks per attention pass (one 64 KiB LDS slot)
+constexpr int kWideResPerPass = 8;  // residuals per index window (16 indices, 3 words) and per key pass (8 x 8 KiB)
 __host__ __device__ inline int wide_record_words(int R) { return (kWideBits * R * kWideGroups + 31) / 32; }
 
 // Attention workgroup: fp16 storage runs 8 waves (two per SIMD) over two 64 KiB codebook slots; fp32

@@ -39,32 +39,26 @@ __device__ __forceinline__ uint4 load_code_record(const uint8_t* codes, int64_t 
 
 // Bit-packed records (one index per 64 dims, N = 64): a token's R x 2 six-bit indices form one
 // little-endian bitstream of 32-bit words, index (r, g) at bit 6 (2 r + g). Word w of every token of a KV head
-// sits in plane w ([Hkv][words][T]), so a token's words are T apart. Kernels read the stream in windows
-// of kWideResPerPass residuals: window c starts at bit 6 * 2 * kWideResPerPass * c, inside words
-// packed_window_word(c) and the one after it (48 bits from a 0- or 16-bit offset: always two words).
+// sits in plane w ([Hkv][words][T]), so a token's words are T apart. Kernels read the stream in windows of
+// kWideResPerPass residuals: window c is the 96 bits of words 3 c .. 3 c + 2 (words past the record are
+// read as its last word; the fields they would hold lie past bit 12 R and are never used).
 __device__ __forceinline__ int packed_window_word(int c) { return (kWideBits * kWideGroups * kWideResPerPass * c) >> 5; }
-__device__ __forceinline__ int packed_window_shift(int c) {
-  return (kWideBits * kWideGroups * kWideResPerPass * c) & 31;
-}
-// (x0, x1) = bits sh .. sh + 31 and sh + 32 .. of the word pair (lo, hi).
-__device__ __forceinline__ void packed_window(uint32_t lo, uint32_t hi, int sh, uint32_t& x0, uint32_t& x1) {
-  x0 = __builtin_amdgcn_alignbit(hi, lo, sh);
-  x1 = hi >> sh;
-}
-// Index F of a window (F = 2 rho + g for residual kWideResPerPass * c + rho, group g).
+static_assert(kWideBits * kWideGroups * kWideResPerPass == 96, "a window is three whole words");
+// Index F of a window from its words (x0, x1, x2); F = 2 rho + g for residual kWideResPerPass * c + rho,
+// group g.
 template <int F>
-__device__ __forceinline__ uint32_t packed_index(uint32_t x0, uint32_t x1) {
-  constexpr int bit = kWideBits * F;
+__device__ __forceinline__ uint32_t packed_index(uint32_t x0, uint32_t x1, uint32_t x2) {
+  constexpr int bit = kWideBits * F, wi = bit >> 5, sh = bit & 31;
   constexpr uint32_t mask = (1u << kWideBits) - 1;
-  if constexpr (bit + kWideBits <= 32) {
-    return (x0 >> bit) & mask;
-  } else if constexpr (bit >= 32) {
-    return (x1 >> (bit - 32)) & mask;
+  static_assert(wi < 3, "inside the window");
+  const uint32_t lo = wi == 0 ? x0 : (wi == 1 ? x1 : x2);
+  if constexpr (sh + kWideBits <= 32) {
+    return (lo >> sh) & mask;
   } else {
-    return ((x0 >> bit) | (x1 << (32 - bit))) & mask;
+    const uint32_t hi = wi == 0 ? x1 : x2;
+    return __builtin_amdgcn_alignbit(hi, lo, sh) & mask;
   }
 }
-static_assert(kWideBits * kWideGroups * kWideResPerPass <= 48, "a window fits two words from a 16-bit offset");
 // Index (r, g) of one token record whose words are `plane` apart, read field by field (the codebook tools;
 // the attention kernel reads whole windows). A field that crosses a word boundary takes its high bits from
 // the next word, which is then still inside the record (the field ends at or before bit 12 R).

@@ -344,7 +344,7 @@ hipError_t launch_debug_unpack(int R, int Hkv, int64_t total_tokens, const uint8
   return hipGetLastError();
 }
 
-// Bit-packed records: one thread per (kv, token, window c); it reads the window's two words and unpacks
+// Bit-packed records: one thread per (kv, token, window c); it reads the window's three words and unpacks
 // them with the same window functions the attention kernel uses. out is [Hkv][R][T][2] int32.
 __global__ void debug_unpack_bits_kernel(const uint32_t* words, int64_t total_tokens, int R, int Wd, int n_windows,
                                          int64_t n_items, int32_t* out) {
@@ -355,18 +355,16 @@ __global__ void debug_unpack_bits_kernel(const uint32_t* words, int64_t total_to
   const int64_t kv = kt / total_tokens, t = kt % total_tokens;
   const uint32_t* rec = words + kv * Wd * total_tokens + t;  // word w at rec[w * total_tokens]
   const int w0 = packed_window_word(c);
-  uint32_t x0, x1;
-  packed_window(rec[w0 * total_tokens], rec[min(w0 + 1, Wd - 1) * total_tokens], packed_window_shift(c), x0, x1);
-  uint32_t idx[2 * kWideResPerPass];
-  idx[0] = packed_index<0>(x0, x1);
-  idx[1] = packed_index<1>(x0, x1);
-  idx[2] = packed_index<2>(x0, x1);
-  idx[3] = packed_index<3>(x0, x1);
-  idx[4] = packed_index<4>(x0, x1);
-  idx[5] = packed_index<5>(x0, x1);
-  idx[6] = packed_index<6>(x0, x1);
-  idx[7] = packed_index<7>(x0, x1);
-  static_assert(kWideResPerPass == 4, "eight indices per window");
+  const uint32_t x0 = rec[min(w0, Wd - 1) * total_tokens], x1 = rec[min(w0 + 1, Wd - 1) * total_tokens];
+  const uint32_t x2 = rec[min(w0 + 2, Wd - 1) * total_tokens];
+  static_assert(kWideResPerPass == 8 && kWideGroups == 2, "sixteen indices per window");
+  const uint32_t idx[2 * kWideResPerPass] = {
+      packed_index<0>(x0, x1, x2),  packed_index<1>(x0, x1, x2),  packed_index<2>(x0, x1, x2),
+      packed_index<3>(x0, x1, x2),  packed_index<4>(x0, x1, x2),  packed_index<5>(x0, x1, x2),
+      packed_index<6>(x0, x1, x2),  packed_index<7>(x0, x1, x2),  packed_index<8>(x0, x1, x2),
+      packed_index<9>(x0, x1, x2),  packed_index<10>(x0, x1, x2), packed_index<11>(x0, x1, x2),
+      packed_index<12>(x0, x1, x2), packed_index<13>(x0, x1, x2), packed_index<14>(x0, x1, x2),
+      packed_index<15>(x0, x1, x2)};
 #pragma unroll
   for (int rho = 0; rho < kWideResPerPass; ++rho) {
     const int r = kWideResPerPass * c + rho;
