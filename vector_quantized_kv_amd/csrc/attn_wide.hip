@@ -118,17 +118,20 @@ __device__ __forceinline__ void wide_key_unit(const uint4 (&rows)[NR], const h4&
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One residual's share of the bins x value codebook product for RoPE-pair chunk cc of group g: lane 4 q + j
-// loads codeword row l = lane (dims 8 cc .. 8 cc + 7, fp16), an identity MFMA turns each 4x4 (codeword x dim)
-// tile into the B operand (lane 4 q + j: dim j of codewords 4 q .. 4 q + 3), and the bins' hi and lo parts
-// (A operand: lane 4 q + h, head h, codewords 4 q .. 4 q + 3) accumulate into the byte layout's O pair 2 G,
-// 2 G + 1 of group G = 8 g + cc.
-template <int G>
-__device__ __forceinline__ void wide_bin_unit(const uint4& row, const h4& ident, const h4& ahi, const h4& alo,
+// One residual's share of the bins x value codebook product for RoPE-pair chunk CC of its group: the B operands
+// (lane 4 q + j: dim 8 CC + 4 x + j of codewords 4 q .. 4 q + 3) come from the residual's table in LDS through
+// the transposing read, where the table holds codeword l's chunk cc at 16-byte unit 8 l + (cc ^ (l & 7)); the
+// bins' hi and lo parts (A operand: lane 4 q + h, head h, codewords 4 q .. 4 q + 3) accumulate into the byte
+// layout's O pair 2 G, 2 G + 1 of group G.
+template <int G, int CC>
+__device__ __forceinline__ void wide_bin_unit(const unsigned char* vt, const int lane, const h4& ahi, const h4& alo,
                                               f4 (&O)[2 * kGroups]) {
-  const f4 z = {0.f, 0.f, 0.f, 0.f};
-  const h4 v0 = to_h4(mfma(cat(as_h2(row.x), as_h2(row.y)), ident, z));  // exact: fp16 values
-  const h4 v1 = to_h4(mfma(cat(as_h2(row.z), as_h2(row.w)), ident, z));
+  // the transposing read hands lane 16 q' + 4 a + e value e of the loads named by lanes 16 q' + 4 k + a: lane
+  // 16 q' + 4 k + a names codeword 16 q' + 4 a + k
+  const int l = (lane & 48) + 4 * (lane & 3) + ((lane >> 2) & 3);
+  const unsigned char* src = vt + (8 * l + (CC ^ (l & 7))) * 16;
+  const h4 v0 = lds_read_tr(src);
+  const h4 v1 = lds_read_tr(src + 8);
   O[2 * G] = mfma(ahi, v0, O[2 * G]);
   O[2 * G] = mfma(alo, v0, O[2 * G]);
   O[2 * G + 1] = mfma(ahi, v1, O[2 * G + 1]);
@@ -375,6 +378,24 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   for (int p = 0; p < npass - (tail_both ? 1 : 0); ++p) key_pass(std::integral_constant<int, kRes>{}, p & 1, p >> 1);
   if (tail_both) key_pass(std::integral_constant<int, kRes / 2>{}, 0, nch - 1);
 
+  // The value tables for the bins x value codebook product below go through this wave's 8 KiB of the last key
+  // pass's slot (free since that pass's closing barrier); the first one is copied now.
+  constexpr int kSteps = (kWideMaxResiduals + kW - 1) / kW;
+  auto step_r = [&](int g, int n) { return ((wave - g * R) % kW + kW) % kW + kW * n; };
+  unsigned char* vtab = lds + ((npass - 1) & 1) * kSlot + wave * kWTab;
+  auto load_vtab = [&](int g, int r) {
+    const f16* tab = cb_v + (static_cast<int64_t>(g) * R + r) * kWN * (kWRow / 2);
+#pragma unroll
+    for (int k = 0; k < kWTab / 1024; ++k) {
+      const int l = 8 * k + (lane >> 3), cc = (lane & 7) ^ (l & 7);
+      __builtin_amdgcn_global_load_lds(tab + l * (kWRow / 2) + cc * 8, vtab + k * 1024, 16, 0, 0);
+    }
+  };
+  if (step_r(0, 0) < R)
+    load_vtab(0, step_r(0, 0));
+  else if (step_r(1, 0) < R)
+    load_vtab(1, step_r(1, 0));
+
   // ------------------------------------------------------------------------- softmax weights
   // M = the workgroup's maximum scaled score per head (finite: the split holds a valid token); each wave's
   // weights p = e^{s - M} in fixed point, two heads per 64-bit word; l_w = the wave's sum of them.
@@ -446,21 +467,21 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   lds_barrier();  // every token's weights are in the bins
 
   // ------------------------------------------------------------------------- bins x value codebook
-  // The wave takes the (g, r) of its share (every kW-th of the 2 R), each one MFMA column sweep over the 8
-  // chunks of group g. A operand: bins of head h = lane & 3, codewords 4 (lane >> 2) .. + 3, as fp16 hi + lo of
-  // their value in units of 1 (exact to 2^-22 relative).
+  // The wave takes the (g, r) of its share (every kW-th of the 2 R), in steps m = g kSteps + n with
+  // r = r0(g) + kW n. Each step's value table is copied into the wave's 8 KiB of the last key pass's slot by
+  // coalesced direct-to-LDS loads (codeword l's chunk cc to unit 8 l + (cc ^ (l & 7))), the next step's copy
+  // going out once the current table has been read. A operand: bins of head h = lane & 3, codewords
+  // 4 (lane >> 2) .. + 3, as fp16 hi + lo of their value in units of 1 (exact to 2^-22 relative).
   f4 O[2 * kGroups];
 #pragma unroll
   for (int c = 0; c < 2 * kGroups; ++c) O[c] = (f4){0.f, 0.f, 0.f, 0.f};
   {
     const int hh = lane & 3, l4 = (lane >> 2) * 4;
-    static_for<kWG>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      for (int r = ((wave - g * R) % kW + kW) % kW; r < R; r += kW) {
-        const f16* vrow = cb_v + ((static_cast<int64_t>(g) * R + r) * kWN + lane) * (kWRow / 2);
-        uint4 row[kChunks];
-#pragma unroll
-        for (int cc = 0; cc < kChunks; ++cc) row[cc] = *reinterpret_cast<const uint4*>(vrow + 8 * cc);
+    static_for<kWG * kSteps>([&](auto mc) {
+      constexpr int m = decltype(mc)::value, g = m / kSteps, n = m % kSteps;
+      const int r = step_r(g, n);
+      if (r < R) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(0));  // this wave's copy of the table has landed
         const uint4* bq = reinterpret_cast<const uint4*>(bins + ((g * R + r) * 2 + (hh >> 1)) * kWN + l4);
         const uint4 u0 = bq[0], u1 = bq[1];  // codewords l4, l4 + 1 | l4 + 2, l4 + 3: (heads 2 hp, 2 hp + 1)
         const bool odd = hh & 1;
@@ -474,8 +495,16 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
         }
         static_for<kChunks>([&](auto ccc) {
           constexpr int cc = decltype(ccc)::value;
-          wide_bin_unit<8 * g + cc>(row[cc], ident, ahi, alo, O);
+          wide_bin_unit<8 * g + cc, cc>(vtab, lane, ahi, alo, O);
         });
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);  // the table has been read: the next copy may overwrite it
+        __builtin_amdgcn_sched_barrier(0);
+        int gn = g, nn = n + 1;
+        if (nn >= kSteps || step_r(gn, nn) >= R) {
+          gn = g + 1;
+          nn = 0;
+        }
+        if (gn < kWG && step_r(gn, nn) < R) load_vtab(gn, step_r(gn, nn));
       }
     });
   }
