@@ -59,8 +59,11 @@ def kernel_kind(cfg) -> str:
 
 
 def kernel_label(cfg) -> str:
+    """The kernel's name as rocprofv3 reports it: byte layout templated on R, bit-packed layout on the number of
+    residuals in the last 8-residual index window."""
     name = KERNELS[kernel_kind(cfg)][0]
-    return name if cfg.packed else f"{name}<{cfg.n_residuals}>"
+    R = cfg.n_residuals
+    return f"{name}<{R - 8 * ((R + 7) // 8 - 1)}>" if cfg.packed else f"{name}<{R}>"
 
 
 def kernel_source_hash(kind: str) -> str:

@@ -138,6 +138,9 @@ __device__ __forceinline__ void wide_bin_unit(const unsigned char* vt, const int
   O[2 * G + 1] = mfma(alo, v1, O[2 * G + 1]);
 }
 
+// TAIL: residuals in the last index window, R - kRes (ceil(R / kRes) - 1), 1 .. kRes (a kernel per value, so that the
+// last window's passes gather exactly its residuals).
+template <int TAIL>
 __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kSlot + kPhaseBytes];
   // epilogue-only LDS (placed in the codebook slots, past the reduction buffer, once the passes are done)
@@ -152,8 +155,7 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   const int part = __builtin_amdgcn_readfirstlane((wave + split) & (kW - 1));
   const int R = a.n_residuals, Wd = a.record_words;
   const int nch = (R + kRes - 1) / kRes;         // index windows
-  const int tail = R - kRes * (nch - 1);          // residuals in the last window (1 .. kRes)
-  const bool tail_both = 2 * tail <= kRes;        // the last window in one pass over both groups
+  constexpr bool tail_both = 2 * TAIL <= kRes;    // the last window in one pass over both groups
   const int npass = 2 * (nch - 1) + (tail_both ? 1 : 2);
   // (group, residual) of table t of pass p's slot (r >= R: a table of zero rows)
   auto pass_table = [&](int p, int t, int& g, int& r) {
@@ -305,8 +307,9 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
   // Units (g, cc) of the wave's blocks form one software pipeline: the gathers of unit n + kWAhead go out before
   // the arithmetic of unit n; block i + 1's row offsets are computed (and its next-pass words requested) at the
   // start of block i.
-  auto key_pass = [&](auto nrc, const int g, const int c) {
-    constexpr int NR = decltype(nrc)::value, NG = kRes / NR, NU = kChunks * NG;
+  auto key_pass = [&](auto nrc, auto ngc, const int g, const int c) {
+    constexpr int NR = decltype(nrc)::value, NG = decltype(ngc)::value, NU = kChunks * NG;
+    static_assert(NR * NG <= kTables, "the pass's tables fit its slot");
     const int p = NG == 1 ? 2 * c + g : npass - 1;
     const int slot_off = (p & 1) * kSlot;
     // group g's indices 2 rho + g of the window are indices 2 rho of the window shifted by 6 g
@@ -375,8 +378,18 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
     lds_barrier();  // slot (p + 1) % 2 is complete; every wave is done with slot p % 2
   };
 
-  for (int p = 0; p < npass - (tail_both ? 1 : 0); ++p) key_pass(std::integral_constant<int, kRes>{}, p & 1, p >> 1);
-  if (tail_both) key_pass(std::integral_constant<int, kRes / 2>{}, 0, nch - 1);
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using Full = std::integral_constant<int, kRes>;
+  using Tail = std::integral_constant<int, TAIL>;
+  const int nfull = 2 * (nch - 1) + (TAIL == kRes ? 2 : 0);  // passes over full windows
+  for (int p = 0; p < nfull; ++p) key_pass(Full{}, I1{}, p & 1, p >> 1);
+  if constexpr (tail_both) {
+    key_pass(Tail{}, I2{}, 0, nch - 1);
+  } else if constexpr (TAIL < kRes) {
+    key_pass(Tail{}, I1{}, 0, nch - 1);
+    key_pass(Tail{}, I1{}, 1, nch - 1);
+  }
 
   // The value tables for the bins x value codebook product below go through this wave's 8 KiB of the last key
   // pass's slot (free since that pass's closing barrier); the first one is copied now.
@@ -520,7 +533,17 @@ __global__ void __launch_bounds__(kThreads) attn_wide_kernel(const AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_wide(int B, const AttnArgs& a, hipStream_t s) {
-  attn_wide_kernel<<<dim3(a.n_splits * a.n_kv_heads, B), kThreads, 0, s>>>(a);
+  const dim3 grid(a.n_splits * a.n_kv_heads, B);
+  switch (a.n_residuals - kRes * ((a.n_residuals + kRes - 1) / kRes - 1)) {
+    case 1: attn_wide_kernel<1><<<grid, kThreads, 0, s>>>(a); break;
+    case 2: attn_wide_kernel<2><<<grid, kThreads, 0, s>>>(a); break;
+    case 3: attn_wide_kernel<3><<<grid, kThreads, 0, s>>>(a); break;
+    case 4: attn_wide_kernel<4><<<grid, kThreads, 0, s>>>(a); break;
+    case 5: attn_wide_kernel<5><<<grid, kThreads, 0, s>>>(a); break;
+    case 6: attn_wide_kernel<6><<<grid, kThreads, 0, s>>>(a); break;
+    case 7: attn_wide_kernel<7><<<grid, kThreads, 0, s>>>(a); break;
+    default: attn_wide_kernel<8><<<grid, kThreads, 0, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 
