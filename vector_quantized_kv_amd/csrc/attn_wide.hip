@@ -13,12 +13,12 @@
 // The key codebooks (R x 16 KiB per KV head) do not fit in LDS, so the key side runs in passes. A pass holds
 // 8 tables of 8 KiB (64 KiB) in one of two LDS slots while the next pass's tables are staged through registers
 // into the other slot. Index window c of the bitstream (residuals kRes c .. kRes c + kRes - 1) takes two passes,
-// one per group g, of kRes residuals each; a last window of at most kRes / 2 residuals takes one pass of
-// kRes / 2 residuals of both groups. Scores are linear in the residuals, so each pass adds its share to the MFMA
-// accumulators. The rotation and the contraction run once per pass and unit, so a pass over more residuals of
-// one group costs half the arithmetic per gathered row; the short last pass keeps a window of a few residuals
-// from gathering rows that add nothing. The tables of residuals past R in the last pass hold zero rows, so
-// every pass sums all of its tables and no pass branches inside its units.
+// one per group g, of kRes residuals each. The last window holds TAIL residuals (the kernel's template argument):
+// one pass over both groups if TAIL <= kRes / 2, else two passes of TAIL residuals, so every pass gathers only
+// rows of residuals that exist and no pass branches inside its units (a slot's unused tables hold zero rows).
+// Scores are linear in the residuals, so each pass adds its share to the MFMA accumulators. The rotation and the
+// contraction run once per pass and unit, so a pass over more residuals of one group costs less arithmetic per
+// gathered row.
 //
 // Values take the pages' own form (pith.science verdict for arXiv 2506.18879, key_machinery and
 // forward_implications: the softmax weights multiply the value codes before the codebook product): every
@@ -33,12 +33,12 @@
 // 64-token block, 4 GQA heads per KV head, the per-64-token RoPE phase on the query and the per-lane phase on
 // the keys. A 16-byte chunk cc of the 128-byte row of group g holds RoPE pairs 32 g + 4 cc .. + 3, exactly
 // the pairs of the byte layout's group 8 g + cc, so the key contraction's query operand and the epilogue are
-// the byte layout's. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's residual rows
-// (residuals past R, in the last window, are skipped), sums them in fp32 on the matrix core (an MFMA with the
-// identity as A adds a lane's four fp16 values to its fp32 accumulator), rotates the sum by the lane's fine
-// phases in fp32 (phases read from a 32 KiB LDS table) and contracts it with the fp32 block query on the fp32
-// matrix core (v_mfma_f32_4x4x1_16b_f32, query broadcast from one 4-lane block per dim): no fp16 rounding on
-// the key side, so wide logit ranges keep the attention within tolerance.
+// the byte layout's. Per unit (g, cc) a lane gathers its token's chunk from each of the pass's residual rows,
+// sums them in fp32 on the matrix core (an MFMA with the identity as A adds a lane's four fp16 values to its
+// fp32 accumulator), rotates the sum by the lane's fine phases in fp32 (phases read from a 32 KiB LDS table) and
+// contracts it with the fp32 block query on the fp32 matrix core (v_mfma_f32_4x4x1_16b_f32, query broadcast
+// from one 4-lane block per dim): no fp16 rounding on the key side, so wide logit ranges keep the attention
+// within tolerance.
 // Rows are stored with their 16-byte chunks permuted by the codeword (physical chunk = cc xor
 // ((l >> 1) & 7)), so the 16 lanes that share an LDS cycle land on random ones of the 16 bank groups
 // instead of the two that a 128-byte row stride would give them.
