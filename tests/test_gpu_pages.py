@@ -45,7 +45,7 @@ def pages_cfg(name, B, lengths, R, seed, n_kv=2):
     return workloads.custom(name, B, 4 * n_kv, n_kv, lengths, R, "float16", seed, n_groups=2, n_codes=64)
 
 
-@pytest.mark.parametrize("R", [1, 3, 4, 5, 11, 21, 32])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 21, 32])
 def test_pages_unpack_bit_exact(vq, R):
     cfg = pages_cfg(f"unpack_r{R}", 2, (777, 1), R, 300 + R)
     announce(f"debug_unpack bit-packed R={R}")
@@ -87,13 +87,18 @@ def test_pages_attn_matches_oracle_configs(vq, name):
 
 
 PAGES_EDGE = [
-    # name, B, lengths, R
-    ("pages_r1_ragged", 4, (1, 64, 65, 3000), 1),        # one pass per kind, three zero-row residuals
-    ("pages_r4_whole_pass", 2, (513, 4096), 4),          # exactly one full pass per kind
-    ("pages_r5_empty_seq", 3, (700, 0, 2049), 5),        # a one-residual last pass; an empty sequence
+    # name, B, lengths, R. The kernel is instantiated per last-window size T = R - 8 (ceil(R / 8) - 1): T <= 4 takes
+    # one pass over both groups, T > 4 two one-group passes; every T from 1 to 8 appears below.
+    ("pages_r1_ragged", 4, (1, 64, 65, 3000), 1),        # T = 1: a single pass over both groups
+    ("pages_r2_tail", 2, (1500, 64), 2),                 # T = 2
+    ("pages_r4_whole_pass", 2, (513, 4096), 4),          # T = 4: the largest both-group pass
+    ("pages_r5_empty_seq", 3, (700, 0, 2049), 5),        # T = 5: the smallest one-group tail; an empty sequence
+    ("pages_r14_tail6", 2, (3000, 777), 14),             # a full window, then T = 6
+    ("pages_r15_tail7", 1, (2500,), 15),                 # a full window, then T = 7
+    ("pages_r8_one_window", 2, (129, 2048), 8),          # T = 8: one full window, no tail pass
     ("pages_r13_ragged", 2, (4097, 123), 13),
     ("pages_r11_split_boundary", 2, (2048, 4096), 11),
-    ("pages_r32_max", 1, (5000,), 32),                   # the largest R: twelve-word records
+    ("pages_r32_max", 1, (5000,), 32),                   # the largest R: twelve-word records, four full windows
     ("pages_r21_long_merge", 1, (300000,), 21),          # more than 32 splits per (sequence, KV head)
 ]
 
