@@ -30,10 +30,9 @@
 // codebooks, replaced by the two value codebooks in two halves (groups 0-7, then 8-15) as the passes move on.
 //
 // Value pass (fp16 operands, fp32 accumulation; the softmax weights and value codewords are rounded
-// to fp16 once): R = 2 gathers both residual rows whole, sums them in fp16 and transposes each 4x4
-// (token x dim) tile of a lane quad with an identity MFMA; R = 1 reads each row with two transposing
-// 8-byte LDS reads, issued for the token of the transposed lane so that the delivered tile is the same
-// quad tile. Both then accumulate p^T x v with the 4x4x4 MFMA.
+// to fp16 once): each group's rows are gathered whole (R = 2: both residuals, summed in fp16), each 4x4
+// (token x dim) tile of a lane quad is transposed with an identity MFMA, and p^T x v accumulates with the
+// 4x4x4 MFMA.
 // The workgroup combines its waves, writes (M, L, o[128]) per q head, and the last workgroup of each
 // (b, kv) merges the splits (attn_common.h).
 #include <hip/hip_runtime.h>
@@ -120,10 +119,10 @@ __device__ __forceinline__ void contract_key(const float (&w)[NB][8], const floa
   });
 }
 
-// Value path, R = 2: each group's two residual rows are gathered whole (by the value pass, from the LDS map
-// below) and summed in fp16; an identity MFMA transposes each 4-dim half within its lane quad (lane 4b + j
-// receives dim j of the quad's 4 tokens, exactly, in fp32), which converted back is the B operand of p^T x v for
-// MFMA block b = the quad.
+// Value path: each group's row (R = 2: the fp16 sum of its two residual rows) is gathered whole by the value pass
+// from the LDS map below; an identity MFMA transposes each 4-dim half within its lane quad (lane 4b + j receives
+// dim j of the quad's 4 tokens, exactly, in fp32), which converted back is the B operand of p^T x v for MFMA
+// block b = the quad.
 template <int G>
 __device__ __forceinline__ void value_step_quad(const uint4& row, const h4& ident, const h4& pt,
                                                 f4 (&O)[2 * kGroups]) {
@@ -138,41 +137,6 @@ __device__ __forceinline__ void value_pair2(const uint4 (&buf)[2][2], const h4& 
                                             f4 (&O)[2 * kGroups]) {
   value_step_quad<2 * P>(add_rows(buf[0][0], buf[0][1]), ident, pt, O);
   value_step_quad<2 * P + 1>(add_rows(buf[1][0], buf[1][1]), ident, pt, O);
-}
-
-// Value path, R = 1: each group's row is read as two transposing 8-byte reads. Within a 16-lane group, lane
-// a + 4k names the row of the token in lane 4a + k (its record was moved there by transpose_record), so lane
-// 4a + e receives dim e (and 4 + e) of tokens 4a .. 4a + 3: the B operand of p^T x v for the quad a.
-template <int Q>
-__device__ __forceinline__ void gather_quarter_tr(const unsigned char* tab, const uint4& code, uint4 (&buf)[4]) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const unsigned char* row = tab + (4 * Q + u) * kCodes * 16 + code_index(code, 4 * Q + u) * 16;
-    const h4 lo = lds_read_tr(row), hi = lds_read_tr(row + 8);
-    buf[u] = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
-                        __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
-  }
-}
-template <int G>
-__device__ __forceinline__ void value_step(const uint4& tv, const h4& pt, f4 (&O)[2 * kGroups]) {
-  O[2 * G] = mfma(pt, cat(as_h2(tv.x), as_h2(tv.y)), O[2 * G]);
-  O[2 * G + 1] = mfma(pt, cat(as_h2(tv.z), as_h2(tv.w)), O[2 * G + 1]);
-}
-template <int Q>
-__device__ __forceinline__ void value_quarter(const uint4 (&buf)[4], const h4& pt, f4 (&O)[2 * kGroups]) {
-  value_step<4 * Q + 0>(buf[0], pt, O);
-  value_step<4 * Q + 1>(buf[1], pt, O);
-  value_step<4 * Q + 2>(buf[2], pt, O);
-  value_step<4 * Q + 3>(buf[3], pt, O);
-}
-// Record of the token in lane 16 (L / 16) + 4 (L mod 4) + (L / 4) mod 4 (a 4x4 transpose within each 16-lane
-// group), through the LDS crossbar (no LDS memory).
-__device__ __forceinline__ uint4 transpose_record(const uint4& r, int lane) {
-  const int src = ((lane & ~15) | ((lane & 3) << 2) | ((lane >> 2) & 3)) << 2;
-  return make_uint4(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.x)),
-                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.y)),
-                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.z)),
-                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(r.w)));
 }
 
 // LDS map (bytes). Codebook rows are 16 bytes (8 fp16), 4 KiB per (residual, group).
@@ -595,13 +559,15 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
     });
   } else {
     const unsigned char* vtab = lds + hi;
-    uint4 rows[kBufs][4];  // gathered rows of quarters n .. n + kAhead
-    uint4 vrec[kMaxBlocks];  // value records moved to the transposed lanes
+    uint4 rows[kBufs][4];  // gathered rows of quarters n .. n + kAhead (4 groups each)
     auto issue = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
       if constexpr (m < 4 * kMaxBlocks) {
-        if constexpr (m % 4 == 0) vrec[m / 4] = transpose_record(code[m / 4], lane_id());
-        gather_quarter_tr<m % 4>(vtab, vrec[m / 4], rows[m % kBufs]);
+        constexpr int Q = m % 4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          rows[m % kBufs][u] = *reinterpret_cast<const uint4*>(vtab + (4 * Q + u) * kCodes * 16 +
+                                                               code_index(code[m / 4], 4 * Q + u) * 16);
       }
     };
     if (my_blocks > 0) static_for<kAhead>(issue);
@@ -615,7 +581,10 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
           __builtin_amdgcn_sched_barrier(0);
           issue(std::integral_constant<int, n + kAhead>{});
           __builtin_amdgcn_sched_barrier(0);
-          value_quarter<n % 4>(rows[n % kBufs], pt[i], O);
+          static_for<4>([&](auto uc) {
+            constexpr int u = decltype(uc)::value;
+            value_step_quad<4 * (n % 4) + u>(rows[n % kBufs][u], ident, pt[i], O);
+          });
         });
       }
     });
