@@ -131,9 +131,11 @@ int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const
  * No key or value is dequantized to memory. Sequences with L_b = 0 produce zeros.
  * Arithmetic: codewords are read in dtype; the residual sum, the key rotation, the scores, the softmax and
  * the value accumulation run in fp32 for both dtypes (fp16 storage included), so the error does not grow
- * with the logit range: results stay within 2e-3 (fp16 storage) and 1e-5 (fp32) of the exact value per
- * output row, relative to the row's largest entry, for score spreads up to a standard deviation of 12 and
- * tokens that dominate the softmax.
+ * with the logit range. The value products round the softmax weights once: to fp16 for fp16 storage in the
+ * byte layout, and, in the bit-packed layout, to the nearest multiple of 2^-19 of the split's largest weight
+ * per head, binned by value index in exact integer sums. Results stay within 2e-3 (fp16 storage) and 1e-5
+ * (fp32) of the exact value per output row, relative to the row's largest entry, for score spreads up to a
+ * standard deviation of 12 and tokens that dominate the softmax.
  * rope_table: from commvq_rope_table with rope_positions >= max_len.
  * max_len (host) should be >= every seq_len[b], and seq_start[b] + seq_len[b] <= total_tokens (host),
  * the row count of the code arrays. The kernels cannot report a descriptor that breaks these bounds (it
