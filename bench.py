@@ -485,6 +485,53 @@ def codebook_tools_timing(reps: int = 3):
     }
 
 
+def step_kernels_timing(reps: int = 20):
+    """The exported steps of the path, each on its own at the 128K layer shape (llama8b_128k_r2 inputs, fp16,
+    R = 2), against the HBM roofline of its algorithmic bytes: the RoPE phase table for 131072 positions (bytes
+    written), the query x codebook table of the 32 q heads (codebook read, table written), and the value reduction
+    (value codes and fp32 weights p read; bins in LDS, one partial per 2048-token split, then their sum)."""
+    import torch
+    import vector_quantized_kv_amd as vq
+    cfg = workloads.CONFIGS["llama8b_128k_r2"]
+    d = vq.dims_of(cfg)
+    inp = workloads.make_inputs(cfg)
+    ly = vq.Layer(d, inp)
+    T = int(inp["total_tokens"])
+    g = torch.Generator(device="cuda").manual_seed(7)
+    p = torch.rand((cfg.batch, cfg.n_q_heads, ly.max_len), generator=g, device="cuda")
+    rope = vq.rope_table(d, T)
+    table = vq.qcodebook_table(d, ly.q, ly.k_cb)
+    vout = vq.value_reduce(d, p, ly.v_codes, ly.v_cb, ly.seq_start, ly.seq_len, ly.max_len, T)
+    ws = torch.empty(max(vq.value_reduce_workspace_size(d, ly.max_len), 16), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        settle(lambda i: fn(), 0.2)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    def line(t, nbytes):
+        gbps = nbytes / t * 1e-9
+        return {"us": t * 1e6, "algorithmic_bytes": nbytes, "achieved_GBps": gbps, "bound": "hbm",
+                "peak_GBps": HBM_PEAK_GBPS, "frac": gbps / HBM_PEAK_GBPS}
+    t_rope = timed(lambda: vq.rope_table(d, T))
+    t_tab = timed(lambda: vq.qcodebook_table(d, ly.q, ly.k_cb, out=table))
+    t_val = timed(lambda: vq.value_reduce(d, p, ly.v_codes, ly.v_cb, ly.seq_start, ly.seq_len, ly.max_len, T,
+                                          workspace=ws, out=vout))
+    cb_bytes = ly.k_cb.numel() * ly.k_cb.element_size()
+    return {
+        "shape": f"{T} tokens, {cfg.n_kv_heads} KV / {cfg.n_q_heads} q heads, R={cfg.n_residuals}, fp16",
+        "rope_table": line(t_rope, rope.numel() * 4),
+        "qcodebook_table": line(t_tab, cb_bytes + table.numel() * table.element_size()),
+        "value_reduce": line(t_val, ly.v_codes.numel() * ly.v_codes.element_size() + p.numel() * 4),
+    }
+
+
 # workloads of bench.py --profile (one attention kernel per workload kind; 20 launches each)
 PROFILE_ALSO = ("llama8b_128k_r1", "pages_g64_r11_128k", "pages_g64_r21_128k")
 
@@ -774,6 +821,7 @@ def main():
         "probes": probes,
         "kernel_source_sha256_16": {kind: kernel_source_hash(kind) for kind in KERNELS},
     }
+    line["steps"] = step_kernels_timing()
     line["codebook_tools"] = codebook_tools_timing()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, base)

@@ -183,10 +183,10 @@ int commvq_attn_decode_noalloc(const commvq_dims* d /* host */, const void* q, c
  * v_codes: the byte planes [Hkv][R][T][G], or (bit-packed layout) the word planes [Hkv][words][T].
  * p: [B][Hq][max_len] fp32, any finite real values, used as given (no renormalisation); entries at
  * t >= L_b are ignored. workspace: commvq_value_reduce_workspace_size(d, max_len) bytes.
- * Resolution: the bins are integer fixed point per (b, h, 1024-token split of t): each weight is rounded to
- * a multiple of 2^-20 * 2^e, where 2^e is the power of two just above the split's max |p| (fp16 storage),
- * and its rounding residual once more at 2^-40 * 2^e (fp32 storage). A weight below half that step (about
- * 2^-21, resp. 2^-41, of the split's largest) thus contributes nothing, and every other one is represented
+ * Resolution: the bins are integer fixed point per (b, h, 2048-token split of t): each weight is rounded to
+ * a multiple of 2^-19 * 2^e, where 2^e is the power of two just above the split's max |p| (fp16 storage),
+ * and its rounding residual once more at 2^-39 * 2^e (fp32 storage). A weight below half that step (about
+ * 2^-20, resp. 2^-40, of the split's largest) thus contributes nothing, and every other one is represented
  * to that absolute step; the result does not depend on the order of the adds.
  * seq_start / seq_len are clamped as in commvq_attn_decode (length at most max_len and the rows left).
  * ------------------------------------------------------------------------------------------- */

@@ -126,7 +126,7 @@ def test_workspace_sizes():
     assert vq.attn_decode_workspace_size(d1, 131072) == attn_ws(1, 32, 32)  # 4096-token splits
     d32 = vq.make_dims(1, 4, 1, 2, dtype="float32")
     assert vq.attn_decode_workspace_size(d32, 1024) == attn_ws(1, 4, 4)     # fp32: 4 waves, 256-token splits
-    assert vq.value_reduce_workspace_size(d, 2048) == 2 * 32 * 2 * 132 * 4
+    assert vq.value_reduce_workspace_size(d, 4096) == 2 * 32 * 2 * 132 * 4  # 2048-token splits
     # RoPE table: fine fp32 pair-major (64 x 64 x 8 B), fine fp16 (64 x 64 x 4 B), fine fp32 group-major
     # (64 x 64 x 8 B), coarse (ceil(n/64) x 64 x 8 B)
     assert vq.lib().commvq_rope_table_size(ctypes.byref(d), 131072) == (4096 + 4096 + 2048 * 64) * 8

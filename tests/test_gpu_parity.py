@@ -128,14 +128,19 @@ def test_qcodebook_table_matches_oracle(vq, dtype, R, tol):
 
 
 @pytest.mark.parametrize("dtype,R,signed", [("float32", 2, False), ("float32", 1, True), ("float16", 2, False),
-                                            ("float16", 1, True)])
+                                            ("float16", 1, True), ("float16", 1, False), ("float16", 2, True),
+                                            ("float16", 2, "mixed")])
 def test_value_reduce_matches_oracle(vq, dtype, R, signed):
+    """Weights of either sign; "mixed": negative only in a few tokens of the second 2048-token split of the first
+    sequence, so that one workgroup takes the signed bins and the others the non-negative ones."""
     announce(f"value_reduce {dtype} R={R} signed={signed}")
     cfg = workloads.custom("vr", 3, 8, 2, (2500, 1, 1024), R, dtype, 22)
     inp = workloads.make_inputs(cfg)
     L = int(inp["max_len"])
     rng = np.random.default_rng(23)
-    p = rng.uniform(-1 if signed else 0, 1, size=(3, 8, L)).astype(np.float32)
+    p = rng.uniform(-1 if signed is True else 0, 1, size=(3, 8, L)).astype(np.float32)
+    if signed == "mixed":
+        p[0, 3, 2100:2110] *= -1.0
     d = vq.dims_of(cfg)
     dt = torch.float16 if dtype == "float16" else torch.float32
     got = vq.value_reduce(d, torch.from_numpy(p).cuda(), torch.from_numpy(inp["v_codes"]).cuda(),

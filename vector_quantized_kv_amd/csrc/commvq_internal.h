@@ -14,7 +14,7 @@ constexpr int kGroups = 16;     // G: code indices per residual per vector
 constexpr int kGroupDim = 8;    // W: dims per group (4 RoPE pairs)
 constexpr int kCodes = 256;     // N: one byte per index
 constexpr int kGqa = 4;         // q heads per KV head
-constexpr int kSplitTokens = 1024;  // value_reduce: tokens per (sequence, KV head) work item
+constexpr int kSplitTokens = 2048;  // value_reduce: tokens per (sequence, KV head) work item
 constexpr int kPartFloats = 132;    // per (b, q head, split): m, l, 2 pad, o[128]
 constexpr int kFineRows = 64;       // RoPE table: fine rows e^{i f theta}, f < 64
 // RoPE table sections, in float2 units: fine fp32 [j][f]; fine fp32 group-major [g][h][f][p] with

@@ -98,11 +98,12 @@ hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, 
 
 // ----------------------------------------------------------------------------------- value bins
 // Fixed-point bins: LDS float atomics are slow on this chip, integer ones are not. Per (split, head) the
-// weights are scaled by a power of two, fx_scale = 2^(20 - e) with max|w| < 2^e, so |w * fx_scale| < 2^20
-// exactly and a 1024-token split's bin sums stay inside int32. Pass 0 bins rint(w * fx_scale); the fp32
+// weights are scaled by a power of two, fx_scale = 2^(19 - e) with max|w| < 2^e, so |rint(w * fx_scale)| <= 2^19
+// and a 2048-token split's bin sums stay within 2^30 (inside int32). Pass 0 bins rint(w * fx_scale); the fp32
 // path adds pass 1, which bins rint((w * fx_scale - rint(w * fx_scale)) * 2^20), the rounding residual of
-// pass 0 at 2^20 times the resolution (every step exact, as the scale is a power of two). A weight is thus
-// represented to 2^-21 of the split's max|w| (fp16 storage) or 2^-41 (fp32). bins layout [kGqa][kGroups][R][kCodes].
+// pass 0 at 2^20 times the resolution (at most 2^19 in magnitude; every step exact, as the scale is a power of
+// two). A weight is thus represented to 2^-20 of the split's max|w| (fp16 storage) or 2^-40 (fp32). bins layout
+// [kGqa][kGroups][R][kCodes].
 __device__ __forceinline__ int32_t fixed_point(float w, float fx_scale, int pass) {
   const float x = w * fx_scale;
   const float hi = rintf(x);
@@ -113,7 +114,7 @@ __device__ __forceinline__ float fixed_point_scale(float max_abs) {
   if (!(max_abs > 0.f)) return 1.f;
   int e;
   frexpf(max_abs, &e);  // max_abs = m 2^e, m in [0.5, 1)
-  return ldexpf(1.f, 20 - e);
+  return ldexpf(1.f, 19 - e);
 }
 
 template <int R, int TPT>
@@ -136,14 +137,42 @@ __device__ __forceinline__ void bin_weights(int32_t* bins, const uint4 (&vc)[TPT
   }
 }
 
-// acc[i] += weight * sum_r sum_l bins[h][g][r][l] * CV[g][r][l][w] for output d = (tid + 256 i) & 127 of head
-// h = (tid + 256 i) >> 7 (o = 8 g + w); each thread handles 2 outputs.
-template <typename T, int R>
-__device__ __forceinline__ void contract_bins(const int32_t* bins, const T* vcb, float weight, float (&acc)[2]) {
+// Non-negative weights (a softmax's, the usual case): two heads share a 64-bit bin, layout [2 head pairs][kGroups]
+// [R][kCodes] (the same bytes as the int32 bins). A bin's sums stay within 2^30 (see fixed_point_scale), so the
+// low head never carries into the high one and one ds_add_u64 does the work of two ds_add_u32.
+template <int R, int TPT>
+__device__ __forceinline__ void bin_weights_pairs(unsigned long long* bins, const uint4 (&vc)[TPT][R],
+                                                  const float (&w)[TPT][kGqa], const bool (&valid)[TPT],
+                                                  const float (&fx_scale)[kGqa]) {
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    if (!valid[k]) continue;
+    uint32_t fx[kGqa];
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<uint32_t>(fixed_point(w[k][h], fx_scale[h], 0));
+    const unsigned long long p01 = fx[0] | (static_cast<unsigned long long>(fx[1]) << 32);
+    const unsigned long long p23 = fx[2] | (static_cast<unsigned long long>(fx[3]) << 32);
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t l = code_index(vc[k][r], g);
+        __hip_atomic_fetch_add(bins + (g * R + r) * kCodes + l, p01, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(bins + ((kGroups + g) * R + r) * kCodes + l, p23, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+  }
+}
+
+// acc[i] += weight * sum_r sum_l bins[h][g][r][l] * CV[g][r][l][w] for output d = (tid + NT i) & 127 of head
+// h = (tid + NT i) >> 7 (o = 8 g + w); each of the NT threads handles kGqa * kHeadDim / NT outputs.
+template <typename T, int R, int NT>
+__device__ __forceinline__ void contract_bins(const int32_t* bins, const T* vcb, float weight,
+                                              float (&acc)[kGqa * kHeadDim / NT]) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, h = idx >> 7, d = idx & 127, g = d >> 3, w = d & 7;
+  for (int i = 0; i < kGqa * kHeadDim / NT; ++i) {
+    const int idx = tid + NT * i, h = idx >> 7, d = idx & 127, g = d >> 3, w = d & 7;
     float sum = 0.f;
     for (int r = 0; r < R; ++r) {
       const int32_t* bb = bins + ((h * kGroups + g) * R + r) * kCodes;
@@ -154,16 +183,123 @@ __device__ __forceinline__ void contract_bins(const int32_t* bins, const T* vcb,
   }
 }
 
+// fp16 storage: the same product on the matrix core (v_mfma_f32_4x4x4_16b_f16). Wave w of the kVrWaves takes
+// groups kVrGpw w .. kVrGpw w + kVrGpw - 1 (every residual and codeword), so each output belongs to one wave. Per (group, residual,
+// 64-codeword chunk c): a coalesced 16-byte load hands lane l the row of codeword 64 c + l (a byte-layout row is
+// 16 bytes), an MFMA against the identity turns each 4x4 (codeword x dim) quad tile into the B operand (lane
+// 4 q + j: dim j of codewords 64 c + 4 q .. + 3, exact in fp32, so exact back in fp16), and the bins of head
+// h = lane & 3 and those codewords, scaled by 2^-16 (exact: |bin| < 2^31) and split into fp16 hi + lo (2^-22
+// relative), are the A operand. The 16 quads of each output are summed across lanes at the end; lane j < 4 then
+// writes dims 8 g + 4 x + j of every head: part[h][8 g + 4 x + j] = sum * 2^16 * scale[h].
+constexpr int kVrWaves = 8;                      // waves per value-reduce workgroup (one workgroup per CU: the bins)
+constexpr int kVrThreads = 64 * kVrWaves;
+constexpr int kVrGpw = kGroups / kVrWaves;         // groups per wave in the contraction
+static_assert(kGroups % kVrWaves == 0 && kSplitTokens % kVrThreads == 0, "groups and tokens split evenly");
+typedef _Float16 vr_h4 __attribute__((ext_vector_type(4)));
+typedef float vr_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ vr_f4 vr_mfma(vr_h4 a, vr_h4 b, vr_f4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ vr_h4 vr_row_half(uint32_t x, uint32_t y) {
+  const vr_h4 v = {__builtin_bit_cast(f16, static_cast<uint16_t>(x)), __builtin_bit_cast(f16, static_cast<uint16_t>(x >> 16)),
+                   __builtin_bit_cast(f16, static_cast<uint16_t>(y)), __builtin_bit_cast(f16, static_cast<uint16_t>(y >> 16))};
+  return v;
+}
+// The wave's codeword rows, rows[gi][r][c] = codeword 64 c + lane of residual r, group kVrGpw wave + gi (loaded
+// before the bins are filled, so that their latency hides behind the binning).
+template <int R>
+__device__ __forceinline__ void load_value_rows(const f16* vcb, uint4 (&rows)[kVrGpw][R][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int gi = 0; gi < kVrGpw; ++gi)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        rows[gi][r][c] = *reinterpret_cast<const uint4*>(
+            vcb + ((static_cast<int64_t>(kVrGpw * wave + gi) * R + r) * kCodes + 64 * c + lane) * kGroupDim);
+}
+template <int R, bool kPairs>
+__device__ __forceinline__ void contract_bins_mfma(const int32_t* bins, const uint4 (&rows)[kVrGpw][R][4],
+                                                   const float (&scale)[kGqa], float* part, int64_t row_stride) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hh = lane & 3, q4 = (lane >> 2) * 4;
+  const vr_h4 ident = {static_cast<f16>(hh == 0), static_cast<f16>(hh == 1), static_cast<f16>(hh == 2),
+                       static_cast<f16>(hh == 3)};
+  const vr_f4 z = {0.f, 0.f, 0.f, 0.f};
+  vr_f4 O[kVrGpw][2];
+#pragma unroll
+  for (int gi = 0; gi < kVrGpw; ++gi) O[gi][0] = O[gi][1] = z;
+#pragma unroll
+  for (int gi = 0; gi < kVrGpw; ++gi) {
+    const int g = kVrGpw * wave + gi;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint4 (&row)[4] = rows[gi][r];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        int32_t cnt[4];
+        if constexpr (kPairs) {  // 64-bit bins of head pair hh / 2: this head is the low or high half
+          const int4* bp = reinterpret_cast<const int4*>(
+              bins + 2 * (((hh >> 1) * kGroups + g) * R + r) * kCodes + 2 * (64 * c + q4));
+          const int4 b0 = bp[0], b1 = bp[1];
+          const bool hi = hh & 1;
+          cnt[0] = hi ? b0.y : b0.x;
+          cnt[1] = hi ? b0.w : b0.z;
+          cnt[2] = hi ? b1.y : b1.x;
+          cnt[3] = hi ? b1.w : b1.z;
+        } else {
+          const int4 bq = *reinterpret_cast<const int4*>(bins + ((hh * kGroups + g) * R + r) * kCodes + 64 * c + q4);
+          cnt[0] = bq.x;
+          cnt[1] = bq.y;
+          cnt[2] = bq.z;
+          cnt[3] = bq.w;
+        }
+        vr_h4 ahi, alo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = static_cast<float>(cnt[k]) * (1.f / 65536.f);
+          const f16 hi = static_cast<f16>(x);
+          ahi[k] = hi;
+          alo[k] = static_cast<f16>(x - static_cast<float>(hi));
+        }
+        const vr_f4 t0 = vr_mfma(vr_row_half(row[c].x, row[c].y), ident, z);
+        const vr_f4 t1 = vr_mfma(vr_row_half(row[c].z, row[c].w), ident, z);
+        const vr_h4 v0 = {static_cast<f16>(t0[0]), static_cast<f16>(t0[1]), static_cast<f16>(t0[2]), static_cast<f16>(t0[3])};
+        const vr_h4 v1 = {static_cast<f16>(t1[0]), static_cast<f16>(t1[1]), static_cast<f16>(t1[2]), static_cast<f16>(t1[3])};
+        O[gi][0] = vr_mfma(ahi, v0, O[gi][0]);
+        O[gi][0] = vr_mfma(alo, v0, O[gi][0]);
+        O[gi][1] = vr_mfma(ahi, v1, O[gi][1]);
+        O[gi][1] = vr_mfma(alo, v1, O[gi][1]);
+      }
+    }
+  }
+  // sum the 16 quads (lanes with the same j = lane & 3), then lane j writes dim 4 x + j of its groups
+#pragma unroll
+  for (int gi = 0; gi < kVrGpw; ++gi)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h) {
+        float v = O[gi][x][h];
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (lane < 4) part[h * row_stride + 4 + 8 * (kVrGpw * wave + gi) + 4 * x + lane] = v * 65536.f * scale[h];
+      }
+}
+
 // ----------------------------------------------------------------------------------- value reduce
 // The reordered value reduce of the pages: weights are binned by value code (bin_weights), then the
 // bins are contracted with the value codebook (contract_bins). One workgroup per (sequence, KV head,
-// 1024-token split); partial outputs are summed by combine_sum_kernel. Any finite weights bin exactly up
+// 2048-token split); partial outputs are summed by combine_sum_kernel. Any finite weights bin exactly up
 // to the fixed-point resolution above (one pass for fp16 storage, two for fp32).
 template <typename T, int R>
-__global__ void __launch_bounds__(256) value_reduce_kernel(const ValueReduceArgs a) {
-  constexpr int TPT = kSplitTokens / 256;
+__global__ void __launch_bounds__(kVrThreads) value_reduce_kernel(const ValueReduceArgs a) {
+  constexpr int TPT = kSplitTokens / kVrThreads;
   constexpr int kPasses = sizeof(T) == 4 ? 2 : 1;
-  __shared__ float red[4][kGqa];
+  __shared__ float red[kVrWaves][kGqa];
   __shared__ __attribute__((aligned(16))) int32_t work[kGqa * kGroups * R * kCodes];
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens);
@@ -178,57 +314,110 @@ __global__ void __launch_bounds__(256) value_reduce_kernel(const ValueReduceArgs
   uint4 vc[TPT][R];
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
-    const int t = t0 + tid + 256 * k;
+    const int t = t0 + tid + kVrThreads * k;
     valid[k] = t < L;
 #pragma unroll
     for (int h = 0; h < kGqa; ++h)
       w[k][h] = valid[k] ? a.p[(static_cast<int64_t>(b) * a.n_q_heads + h0 + h) * a.p_stride + t] : 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      vc[k][r] = valid[k] ? load_code_record(a.v_codes, a.total_tokens, kv, row0 + tid + 256 * k, R, r)
+      vc[k][r] = valid[k] ? load_code_record(a.v_codes, a.total_tokens, kv, row0 + tid + kVrThreads * k, R, r)
                           : make_uint4(0, 0, 0, 0);
   }
+  __shared__ int neg_w[kVrWaves];
+  bool neg = false;
 #pragma unroll
   for (int h = 0; h < kGqa; ++h) {
     float mx = 0.f;
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) mx = fmaxf(mx, fabsf(w[k][h]));
+    for (int k = 0; k < TPT; ++k) {
+      mx = fmaxf(mx, fabsf(w[k][h]));
+      neg |= w[k][h] < 0.f;
+    }
     mx = wave_max(mx);
     if (lane == 0) red[wave][h] = mx;
   }
+  const bool wave_neg = __ballot(neg) != 0;
+  if (lane == 0) neg_w[wave] = wave_neg;
   __syncthreads();
+  bool any_neg = false;
+#pragma unroll
+  for (int v = 0; v < kVrWaves; ++v) any_neg |= neg_w[v] != 0;
   float fx_scale[kGqa];
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h)
-    fx_scale[h] = fixed_point_scale(fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h])));
-  const T* vcb = static_cast<const T*>(a.v_cb) + static_cast<int64_t>(kv) * kGroups * R * kCodes * kGroupDim;
-  float acc[2] = {0.f, 0.f};
-  for (int pass = 0; pass < kPasses; ++pass) {
-    if (pass > 0) __syncthreads();  // every thread has finished reading the previous pass's bins
-    for (int i = tid; i < kGqa * kGroups * R * kCodes; i += 256) work[i] = 0;
-    __syncthreads();
-    bin_weights<R, TPT>(work, vc, w, valid, fx_scale, pass);
-    __syncthreads();
-    contract_bins<T, R>(work, vcb, pass == 0 ? 1.f : 1.f / 1048576.f, acc);
+  for (int h = 0; h < kGqa; ++h) {
+    float mx = red[0][h];
+#pragma unroll
+    for (int v = 1; v < kVrWaves; ++v) mx = fmaxf(mx, red[v][h]);
+    fx_scale[h] = fixed_point_scale(mx);
   }
+  const T* vcb = static_cast<const T*>(a.v_cb) + static_cast<int64_t>(kv) * kGroups * R * kCodes * kGroupDim;
   float* part = a.part + ((static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits + split) * kPartFloats;
   const int64_t row_stride = static_cast<int64_t>(a.n_splits) * kPartFloats;
+  if constexpr (sizeof(T) == 2) {
+    uint4 rows[kVrGpw][R][4];
+    load_value_rows<R>(reinterpret_cast<const f16*>(vcb), rows);
+    for (int i = tid; i < kGqa * kGroups * R * kCodes / 4; i += kVrThreads)
+      reinterpret_cast<int4*>(work)[i] = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    float inv[kGqa];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, h = idx >> 7, d = idx & 127;
-    part[h * row_stride + 4 + d] = acc[i] / fx_scale[h];
+    for (int h = 0; h < kGqa; ++h) inv[h] = 1.f / fx_scale[h];  // a power of two: exact
+    if (!any_neg) {
+      bin_weights_pairs<R, TPT>(reinterpret_cast<unsigned long long*>(work), vc, w, valid, fx_scale);
+      __syncthreads();
+      contract_bins_mfma<R, true>(work, rows, inv, part, row_stride);
+    } else {
+      bin_weights<R, TPT>(work, vc, w, valid, fx_scale, 0);
+      __syncthreads();
+      contract_bins_mfma<R, false>(work, rows, inv, part, row_stride);
+    }
+  } else {
+    constexpr int kOut = kGqa * kHeadDim / kVrThreads;
+    float acc[kOut] = {};
+    for (int pass = 0; pass < kPasses; ++pass) {
+      if (pass > 0) __syncthreads();  // every thread has finished reading the previous pass's bins
+      for (int i = tid; i < kGqa * kGroups * R * kCodes / 4; i += kVrThreads)
+      reinterpret_cast<int4*>(work)[i] = make_int4(0, 0, 0, 0);
+      __syncthreads();
+      bin_weights<R, TPT>(work, vc, w, valid, fx_scale, pass);
+      __syncthreads();
+      contract_bins<T, R, kVrThreads>(work, vcb, pass == 0 ? 1.f : 1.f / 1048576.f, acc);
+    }
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+      const int idx = tid + kVrThreads * i, h = idx >> 7, d = idx & 127;
+      part[h * row_stride + 4 + d] = acc[i] / fx_scale[h];
+    }
   }
 }
 
-__global__ void __launch_bounds__(128) combine_sum_kernel(const float* part, const ValueReduceArgs a, float* out) {
-  const int bh = blockIdx.x, b = bh / a.n_q_heads, d = threadIdx.x;
+// One workgroup per (b, q head): thread (d, k) sums the splits k, k + 8, ... of output d (four loads in flight),
+// and the 8 partial sums are added in a fixed order.
+constexpr int kCombineParts = 8;
+__global__ void __launch_bounds__(kCombineParts * kHeadDim) combine_sum_kernel(const float* part, const ValueReduceArgs a,
+                                                                             float* out) {
+  __shared__ float red[kCombineParts][kHeadDim];
+  const int bh = blockIdx.x, b = bh / a.n_q_heads, d = threadIdx.x & (kHeadDim - 1), k = threadIdx.x / kHeadDim;
   const int L = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens).len;  // as value_reduce_kernel
   const int n_splits = a.n_splits;
   const int ns = (L + kSplitTokens - 1) / kSplitTokens;
-  const float* p = part + static_cast<int64_t>(bh) * n_splits * kPartFloats;
-  float acc = 0.f;
-  for (int s = 0; s < ns; ++s) acc += p[s * kPartFloats + 4 + d];
-  out[static_cast<int64_t>(bh) * kHeadDim + d] = acc;
+  const float* p = part + static_cast<int64_t>(bh) * n_splits * kPartFloats + 4 + d;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = k;
+  for (; s + 3 * kCombineParts < ns; s += 4 * kCombineParts) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += p[static_cast<int64_t>(s + u * kCombineParts) * kPartFloats];
+  }
+  for (; s < ns; s += kCombineParts) acc[0] += p[static_cast<int64_t>(s) * kPartFloats];
+  red[k][d] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (k == 0) {
+    float t = red[0][d];
+#pragma unroll
+    for (int j = 1; j < kCombineParts; ++j) t += red[j][d];
+    out[static_cast<int64_t>(bh) * kHeadDim + d] = t;
+  }
 }
 
 // Bit-packed records (G = 2, N = 64, W = 64, R up to 32, fp16 storage): the same split, one-pass fixed-point
@@ -312,15 +501,15 @@ hipError_t launch_value_reduce(int dtype, bool packed, int R, int B, const Value
   if (packed) {  // fp16 only
     value_reduce_bits_kernel<<<grid, 256, 0, s>>>(a, R);
   } else if (dtype == COMMVQ_F16) {
-    if (R == 1) value_reduce_kernel<f16, 1><<<grid, 256, 0, s>>>(a);
-    else value_reduce_kernel<f16, 2><<<grid, 256, 0, s>>>(a);
+    if (R == 1) value_reduce_kernel<f16, 1><<<grid, kVrThreads, 0, s>>>(a);
+    else value_reduce_kernel<f16, 2><<<grid, kVrThreads, 0, s>>>(a);
   } else {
-    if (R == 1) value_reduce_kernel<float, 1><<<grid, 256, 0, s>>>(a);
-    else value_reduce_kernel<float, 2><<<grid, 256, 0, s>>>(a);
+    if (R == 1) value_reduce_kernel<float, 1><<<grid, kVrThreads, 0, s>>>(a);
+    else value_reduce_kernel<float, 2><<<grid, kVrThreads, 0, s>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_sum_kernel<<<dim3(B * a.n_q_heads), dim3(128), 0, s>>>(a.part, a, out);
+  combine_sum_kernel<<<dim3(B * a.n_q_heads), dim3(kCombineParts * kHeadDim), 0, s>>>(a.part, a, out);
   return hipGetLastError();
 }
 
