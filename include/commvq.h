@@ -109,13 +109,14 @@ int commvq_rope_table(const commvq_dims* d /* host */, int32_t n_positions, void
                       void* stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Query x key-codebook table ("computed once and reused across all cached positions",
- * pith.science verdict, key_machinery; summary page, Approach):
+ * Query x key-codebook table: built once per query and shared by every cached position (pith.science verdict,
+ * key_machinery; summary page, Approach):
  *   table[b][h][g][r][l][2u]   = q[b][h][2j] * a + q[b][h][2j+1] * b
  *   table[b][h][g][r][l][2u+1] = q[b][h][2j] * b - q[b][h][2j+1] * a
  * i.e. conj(q_j) * (a + i b) for pair j = (W/2) g + u and codeword (a, b) = k_codebook[kv][g][r][l][2u..2u+1]
  * (W = 8 in the byte layout, 64 in the bit-packed one).
  * Output [B][Hq][G][R][N][W] in dtype (fp16 results are rounded once from fp32).
+ * k_codebook and table must be 16-byte aligned (COMMVQ_EINVAL otherwise).
  * ------------------------------------------------------------------------------------------- */
 int commvq_qcodebook_table(const commvq_dims* d /* host */, const void* q, const void* k_codebook, void* table,
                            void* stream);

@@ -7,7 +7,7 @@
  *
  * Sources (the pages this follows; cited by title and section/field):
  *   [ABS]  "1-bit quantization" tag page (aitopics.org): the CommVQ abstract. Additive quantization
- *          of the KV cache, "decoded via simple matrix multiplication"; RoPE-commutative codebook.
+ *          of the KV cache, decoded by a plain matrix product with the codebook; RoPE-commutative codebook.
  *   [SUM]  "CommVQ: Commutative Vector Quantization for KV Cache Compression" (atlas.scime.ai
  *          summary), section "Approach": each key/value vector is quantized as a whole with
  *          additive quantization; the key codebook commutes with RoPE so query-codebook products

@@ -109,6 +109,10 @@ def test_misaligned_codes_rejected():
     p, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1001)
     st = L.commvq_attn_decode(ctypes.byref(d), p, odd, p, p, p, p, p, 10, 10, p, 10, p, 1 << 30, p, None)
     assert st == vq.EINVAL and "aligned" in vq.last_error_detail()
+    # the query x codebook table moves codeword rows in 16-byte pieces
+    assert L.commvq_qcodebook_table(ctypes.byref(d), p, odd, p, None) == vq.EINVAL
+    assert "aligned" in vq.last_error_detail()
+    assert L.commvq_qcodebook_table(ctypes.byref(d), p, p, odd, None) == vq.EINVAL
 
 
 def test_workspace_sizes():

@@ -131,14 +131,20 @@ def _torch_dtype(d: Dims):
     return torch.float16 if d.dtype == F16 else torch.float32
 
 
-def rope_table(d: Dims, n_positions: int, device="cuda", stream=None):
-    """Two-level RoPE phase table for positions 0 .. n_positions-1 (see commvq_rope_table)."""
+def rope_table(d: Dims, n_positions: int, device="cuda", stream=None, out=None):
+    """Two-level RoPE phase table for positions 0 .. n_positions-1 (see commvq_rope_table); written into `out`
+    (fp32, at least commvq_rope_table_size bytes) when given."""
     import torch
     nbytes = lib().commvq_rope_table_size(ctypes.byref(d), int(n_positions))
     if nbytes == 0:
         _check(lib().commvq_rope_table(ctypes.byref(d), int(n_positions), None, 0, None), "rope_table")
-    with _on(stream):
-        t = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+    if out is not None:
+        if out.dtype != torch.float32 or out.numel() * 4 < nbytes:
+            raise ValueError(f"rope_table: out must be fp32 with at least {nbytes // 4} elements")
+        t = out
+    else:
+        with _on(stream):
+            t = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
     _check(lib().commvq_rope_table(ctypes.byref(d), int(n_positions), ctypes.c_void_p(t.data_ptr()), nbytes,
                                    _stream(stream)), "rope_table")
     return t

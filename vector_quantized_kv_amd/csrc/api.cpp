@@ -191,6 +191,8 @@ int commvq_rope_table(const commvq_dims* d, int32_t n_positions, void* table, si
 int commvq_qcodebook_table(const commvq_dims* d, const void* q, const void* k_codebook, void* table, void* stream) {
   if (int st = check_dims(d)) return st;
   if (!q || !k_codebook || !table) return fail(COMMVQ_EINVAL, "q, k_codebook and table must be non-NULL");
+  if (!aligned16(k_codebook) || !aligned16(table))
+    return fail(COMMVQ_EINVAL, "k_codebook and table must be 16-byte aligned");
   return hip_status(launch_qtable(d->dtype, packed_family(d), d->n_residuals, d->batch, d->n_q_heads, d->n_kv_heads,
                                   q, k_codebook, table, static_cast<hipStream_t>(stream)),
                     "qcodebook_table launch");

@@ -27,7 +27,12 @@ __device__ __forceinline__ float ld(const T* p) {
 // pair-major (entry j * 64 + f = e^{i f theta_j}), fine group-major (entry ((g * 2 + h) * 64 + f) * 2 + p for
 // pair j = 4g + 2h + p: a lane's phases of two pairs in one 16-byte read), coarse position-major (entry
 // c * 64 + j = e^{i 64 c theta_j}).
-__global__ void rope_table_kernel(double base, int64_t n_coarse, float2* out) {
+__global__ void __launch_bounds__(256) rope_table_kernel(double base, int64_t n_coarse, float2* out) {
+  // theta_j = base^(-2j / head_dim) once per pair and workgroup (64 fp64 pows, not one per entry)
+  __shared__ double theta[kPairs];
+  if (threadIdx.x < kPairs)
+    theta[threadIdx.x] = pow(base, -2.0 * static_cast<int>(threadIdx.x) / static_cast<double>(kHeadDim));
+  __syncthreads();
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   constexpr int64_t kFine = static_cast<int64_t>(kFineRows) * kPairs;
   if (idx >= 2 * kFine + n_coarse * kPairs) return;
@@ -44,9 +49,8 @@ __global__ void rope_table_kernel(double base, int64_t n_coarse, float2* out) {
     j = static_cast<int>((idx - 2 * kFine) % kPairs);
     pos = 64.0 * static_cast<double>((idx - 2 * kFine) / kPairs);
   }
-  const double theta = pow(base, -2.0 * j / static_cast<double>(kHeadDim));
   double s, c;
-  sincos(pos * theta, &s, &c);
+  sincos(pos * theta[j], &s, &c);
   // the sections are contiguous: fine at 0, fine group-major at kRopeFine32gOffset = kFine, coarse after it
   out[idx] = make_float2(static_cast<float>(c), static_cast<float>(s));
 }
@@ -60,20 +64,34 @@ hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hi
 
 // ------------------------------------------------------------------------- query x codebook table
 // grid (G*R, Hq, B), block N: thread l writes the W/2 complex entries of code l. Byte layout G = 16, N = 256,
-// W = 8; bit-packed layout G = 2, N = 64, W = 64.
+// W = 8; bit-packed layout G = 2, N = 64, W = 64. Codeword and entries move in 16-byte pieces (a codeword row
+// is W * sizeof(T) >= 16 bytes and 16-byte aligned), so a wave's loads and stores cover whole contiguous rows.
 template <typename T, int G, int N>
 __global__ void __launch_bounds__(256) qtable_kernel(const T* q, const T* kcb, T* out, int Hq, int Hkv, int R) {
   constexpr int W = kHeadDim / G;
+  constexpr int kPer = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte piece
+  static_assert(W % kPer == 0, "codeword rows are whole 16-byte pieces");
   const int gr = blockIdx.x, h = blockIdx.y, b = blockIdx.z, l = threadIdx.x;
   const int g = gr / R, r = gr % R, kv = h / (Hq / Hkv);
   const T* qq = q + (static_cast<int64_t>(b) * Hq + h) * kHeadDim + W * g;
-  const T* c = kcb + (((static_cast<int64_t>(kv) * G + g) * R + r) * N + l) * W;
-  T* o = out + ((((static_cast<int64_t>(b) * Hq + h) * G + g) * R + r) * N + l) * W;
+  const uint4* c = reinterpret_cast<const uint4*>(kcb + (((static_cast<int64_t>(kv) * G + g) * R + r) * N + l) * W);
+  uint4* o = reinterpret_cast<uint4*>(out + ((((static_cast<int64_t>(b) * Hq + h) * G + g) * R + r) * N + l) * W);
 #pragma unroll
-  for (int u = 0; u < W / 2; ++u) {
-    const float q0 = ld(qq + 2 * u), q1 = ld(qq + 2 * u + 1), a = ld(c + 2 * u), bb = ld(c + 2 * u + 1);
-    o[2 * u] = static_cast<T>(q0 * a + q1 * bb);
-    o[2 * u + 1] = static_cast<T>(q0 * bb - q1 * a);
+  for (int piece = 0; piece < W / kPer; ++piece) {
+    union {
+      uint4 v;
+      T e[kPer];
+    } in, res;
+    in.v = c[piece];
+#pragma unroll
+    for (int u = 0; u < kPer / 2; ++u) {
+      const int d = piece * kPer + 2 * u;
+      const float q0 = ld(qq + d), q1 = ld(qq + d + 1);
+      const float a = static_cast<float>(in.e[2 * u]), bb = static_cast<float>(in.e[2 * u + 1]);
+      res.e[2 * u] = static_cast<T>(q0 * a + q1 * bb);
+      res.e[2 * u + 1] = static_cast<T>(q0 * bb - q1 * a);
+    }
+    o[piece] = res.v;
   }
 }
 
