@@ -60,15 +60,20 @@ def test_pages_qcodebook_table_matches_oracle(vq, R):
             assert err <= 1e-3, (b, h, err)
 
 
-@pytest.mark.parametrize("R,signed", [(1, False), (5, True), (21, False), (32, True)])
+@pytest.mark.parametrize("R,signed", [(1, False), (5, True), (8, False), (11, "mixed"), (21, False), (32, True),
+                                      (32, False)])
 def test_pages_value_reduce_matches_oracle(vq, R, signed):
+    """Weights of either sign; "mixed": negative only in a few tokens of the second 2048-token split of the first
+    sequence (one workgroup takes the signed bins, the others the non-negative ones)."""
     announce(f"value_reduce bit-packed R={R} signed={signed}")
     cfg = pages_cfg("vr", 3, (2500, 1, 1024), R, 100 + R)
     inp = workloads.make_inputs(cfg)
     L = int(inp["max_len"])
     T = int(inp["total_tokens"])
     rng = np.random.default_rng(110 + R)
-    p = rng.uniform(-1 if signed else 0, 1, size=(3, 8, L)).astype(np.float32)
+    p = rng.uniform(-1 if signed is True else 0, 1, size=(3, 8, L)).astype(np.float32)
+    if signed == "mixed":
+        p[0, 5, 2200:2203] *= -1.0
     d = vq.dims_of(cfg)
     v_words = torch.from_numpy(np.ascontiguousarray(inp["v_codes"]).view(np.int32)).cuda()
     got = vq.value_reduce(d, torch.from_numpy(p).cuda(), v_words, torch.from_numpy(inp["v_cb"]).cuda(),

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <utility>
+
 #include "device_common.h"
 
 namespace commvq {
@@ -438,13 +440,135 @@ __global__ void __launch_bounds__(kCombineParts * kHeadDim) combine_sum_kernel(c
   }
 }
 
-// Bit-packed records (G = 2, N = 64, W = 64, R up to 32, fp16 storage): the same split, one-pass fixed-point
-// bins and partials.
-// Bins [kGqa][2][R][64] (64 KiB at R = 32); each token reads its R x 2 indices field by field.
-__global__ void __launch_bounds__(256) value_reduce_bits_kernel(const ValueReduceArgs a, int R) {
-  constexpr int TPT = kSplitTokens / 256;
+// Bit-packed records (2 groups of 64 dims, 64 codewords, R <= 32): the same split, fixed point, sign test and
+// partials as value_reduce_kernel. A token's indices are read in windows of 8 residuals (3 words, 16 indices).
+// Bins [4 heads][2][R][64] int32, or for non-negative splits [2 head pairs][2][R][64] uint64 in the same bytes
+// (64 KiB at R = 32: two workgroups share a CU). The contraction runs on the VALU: the R x 64 (residual,
+// codeword) rows are dealt evenly to the waves, lane (g, w) accumulates dims 2w, 2w + 1 of group g for the 4
+// heads, and the waves' sums meet in LDS (over the bins, once every wave has read them).
+template <int F, bool kPairs>
+__device__ __forceinline__ void bin_packed_field(int32_t* bins, int R, int c, uint32_t x0, uint32_t x1, uint32_t x2,
+                                                 const uint32_t (&fx)[kGqa]) {
+  constexpr int G = kWideGroups, N = kWideCodes, g = F & 1;
+  const int r = kWideResPerPass * c + (F >> 1);
+  if (r >= R) return;  // fields of the last window past the record
+  const uint32_t l = packed_index<F>(x0, x1, x2);
+  if constexpr (kPairs) {
+    unsigned long long* b64 = reinterpret_cast<unsigned long long*>(bins);
+    const unsigned long long p01 = fx[0] | (static_cast<unsigned long long>(fx[1]) << 32);
+    const unsigned long long p23 = fx[2] | (static_cast<unsigned long long>(fx[3]) << 32);
+    __hip_atomic_fetch_add(b64 + (g * R + r) * N + l, p01, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(b64 + ((G + g) * R + r) * N + l, p23, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) atomicAdd(&bins[((h * G + g) * R + r) * N + l], static_cast<int32_t>(fx[h]));
+  }
+}
+
+template <bool kPairs, int... F>
+__device__ __forceinline__ void bin_packed_window(int32_t* bins, int R, int c, uint32_t x0, uint32_t x1, uint32_t x2,
+                                                  const uint32_t (&fx)[kGqa], std::integer_sequence<int, F...>) {
+  (bin_packed_field<F, kPairs>(bins, R, c, x0, x1, x2, fx), ...);
+}
+
+// Every record word a thread needs (TPT tokens x NWIN windows x 3 words) is requested before the first add, so
+// the HBM latency is paid once per thread.
+template <bool kPairs, int TPT, int NWIN>
+__device__ __forceinline__ void bin_packed_tokens(int32_t* bins, int R, const uint32_t* rec, int64_t plane,
+                                                  const float (&w)[TPT][kGqa], const bool (&valid)[TPT],
+                                                  const float (&fx_scale)[kGqa]) {
+  const int Wd = wide_record_words(R);
+  uint32_t x[TPT][NWIN][3];
+#pragma unroll
+  for (int k = 0; k < TPT; ++k)
+#pragma unroll
+    for (int c = 0; c < NWIN; ++c)
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        x[k][c][i] = valid[k] ? rec[kVrThreads * k + min(packed_window_word(c) + i, Wd - 1) * plane] : 0u;
+#pragma unroll
+  for (int k = 0; k < TPT; ++k) {
+    if (!valid[k]) continue;
+    uint32_t fx[kGqa];
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<uint32_t>(fixed_point(w[k][h], fx_scale[h], 0));
+#pragma unroll
+    for (int c = 0; c < NWIN; ++c)
+      bin_packed_window<kPairs>(bins, R, c, x[k][c][0], x[k][c][1], x[k][c][2], fx,
+                                std::make_integer_sequence<int, kWideGroups * kWideResPerPass>{});
+  }
+}
+
+template <bool kPairs, int TPT>
+__device__ __forceinline__ void bin_packed_split(int32_t* bins, int R, const uint32_t* rec, int64_t plane,
+                                                 const float (&w)[TPT][kGqa], const bool (&valid)[TPT],
+                                                 const float (&fx_scale)[kGqa]) {
+  static_assert(kWideMaxResiduals == 4 * kWideResPerPass, "at most 4 windows");
+  switch ((R + kWideResPerPass - 1) / kWideResPerPass) {
+    case 1: bin_packed_tokens<kPairs, TPT, 1>(bins, R, rec, plane, w, valid, fx_scale); break;
+    case 2: bin_packed_tokens<kPairs, TPT, 2>(bins, R, rec, plane, w, valid, fx_scale); break;
+    case 3: bin_packed_tokens<kPairs, TPT, 3>(bins, R, rec, plane, w, valid, fx_scale); break;
+    default: bin_packed_tokens<kPairs, TPT, 4>(bins, R, rec, plane, w, valid, fx_scale); break;
+  }
+}
+
+// Lane (g, w)'s sums over 8 consecutive (residual, codeword) rows kk .. kk + 7 of the 4 heads.
+template <bool kPairs>
+__device__ __forceinline__ void contract_packed_rows(const int32_t* bins, int K, int g, int kk,
+                                                     const uint32_t (&cv)[8], float (&acc)[kGqa][2]) {
+  const unsigned long long* b64 = reinterpret_cast<const unsigned long long*>(bins);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float cnt[kGqa];
+    if constexpr (kPairs) {
+      const unsigned long long lo = b64[g * K + kk + j], hi = b64[(kWideGroups + g) * K + kk + j];
+      cnt[0] = static_cast<float>(static_cast<uint32_t>(lo));
+      cnt[1] = static_cast<float>(static_cast<uint32_t>(lo >> 32));
+      cnt[2] = static_cast<float>(static_cast<uint32_t>(hi));
+      cnt[3] = static_cast<float>(static_cast<uint32_t>(hi >> 32));
+    } else {
+#pragma unroll
+      for (int h = 0; h < kGqa; ++h) cnt[h] = static_cast<float>(bins[(h * kWideGroups + g) * K + kk + j]);
+    }
+    union {
+      uint32_t u;
+      f16 e[2];
+    } c;
+    c.u = cv[j];
+    const float c0 = static_cast<float>(c.e[0]), c1 = static_cast<float>(c.e[1]);
+#pragma unroll
+    for (int h = 0; h < kGqa; ++h) {
+      acc[h][0] = fmaf(cnt[h], c0, acc[h][0]);
+      acc[h][1] = fmaf(cnt[h], c1, acc[h][1]);
+    }
+  }
+}
+
+// Rows [k0, k1) (multiples of 8) of the contraction; the codebook words of the next 8 rows are in flight while
+// the current 8 are summed.
+template <bool kPairs>
+__device__ __forceinline__ void contract_packed(const int32_t* bins, int K, int g, int k0, int k1, const f16* vcb,
+                                                float (&acc)[kGqa][2]) {
+  constexpr int W = kHeadDim / kWideGroups;
+  uint32_t cur[8], nxt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cur[j] = *reinterpret_cast<const uint32_t*>(vcb + static_cast<int64_t>(k0 + j) * W);
+  for (int kk = k0; kk < k1; kk += 8) {
+    const int kn = kk + 8 < k1 ? kk + 8 : kk;  // the last step reloads its own rows (in bounds, unused)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) nxt[j] = *reinterpret_cast<const uint32_t*>(vcb + static_cast<int64_t>(kn + j) * W);
+    contract_packed_rows<kPairs>(bins, K, g, kk, cur, acc);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cur[j] = nxt[j];
+  }
+}
+
+__global__ void __launch_bounds__(kVrThreads) value_reduce_bits_kernel(const ValueReduceArgs a, int R) {
+  constexpr int TPT = kSplitTokens / kVrThreads;
   constexpr int G = kWideGroups, N = kWideCodes, W = kHeadDim / G;
-  __shared__ float red[4][kGqa];
+  static_assert(G * W / 2 == 64 && kGqa * kHeadDim == kVrThreads, "lane (g, w) pairs and one output per thread");
+  __shared__ float red[kVrWaves][kGqa];
+  __shared__ int neg_w[kVrWaves];
   __shared__ __attribute__((aligned(16))) int32_t bins[kGqa * G * kWideMaxResiduals * N];
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens);
@@ -454,70 +578,81 @@ __global__ void __launch_bounds__(256) value_reduce_bits_kernel(const ValueReduc
   const int64_t row0 = sb.start + t0;
   const int h0 = kv * kGqa;
   const int wave = tid >> 6, lane = tid & 63;
-  const int Wd = wide_record_words(R);
   const uint32_t* words = reinterpret_cast<const uint32_t*>(a.v_codes);
   bool valid[TPT];
   float w[TPT][kGqa];
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
-    const int t = t0 + tid + 256 * k;
+    const int t = t0 + tid + kVrThreads * k;
     valid[k] = t < L;
 #pragma unroll
     for (int h = 0; h < kGqa; ++h)
       w[k][h] = valid[k] ? a.p[(static_cast<int64_t>(b) * a.n_q_heads + h0 + h) * a.p_stride + t] : 0.f;
   }
-  for (int i = tid; i < kGqa * G * R * N; i += 256) bins[i] = 0;
+  const int n_bins = kGqa * G * R * N;  // a multiple of 4 int32
+  for (int i = tid; i < n_bins / 4; i += kVrThreads) reinterpret_cast<int4*>(bins)[i] = make_int4(0, 0, 0, 0);
+  bool neg = false;
 #pragma unroll
   for (int h = 0; h < kGqa; ++h) {
     float mx = 0.f;
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) mx = fmaxf(mx, fabsf(w[k][h]));
+    for (int k = 0; k < TPT; ++k) {
+      mx = fmaxf(mx, fabsf(w[k][h]));
+      neg |= w[k][h] < 0.f;
+    }
     mx = wave_max(mx);
     if (lane == 0) red[wave][h] = mx;
   }
+  const bool wave_neg = __ballot(neg) != 0;
+  if (lane == 0) neg_w[wave] = wave_neg;
   __syncthreads();
+  bool any_neg = false;
+#pragma unroll
+  for (int v = 0; v < kVrWaves; ++v) any_neg |= neg_w[v] != 0;
   float fx_scale[kGqa];
 #pragma unroll
-  for (int h = 0; h < kGqa; ++h)
-    fx_scale[h] = fixed_point_scale(fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h])));
+  for (int h = 0; h < kGqa; ++h) {
+    float mx = 0.f;
 #pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    if (!valid[k]) continue;
-    int32_t fx[kGqa];
-#pragma unroll
-    for (int h = 0; h < kGqa; ++h) fx[h] = fixed_point(w[k][h], fx_scale[h], 0);
-    const uint32_t* rec = words + static_cast<int64_t>(kv) * Wd * a.total_tokens + row0 + tid + 256 * k;
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const uint32_t l = packed_field(rec, a.total_tokens, r, g);
-#pragma unroll
-        for (int h = 0; h < kGqa; ++h) atomicAdd(&bins[((h * G + g) * R + r) * N + l], fx[h]);
-      }
+    for (int v = 0; v < kVrWaves; ++v) mx = fmaxf(mx, red[v][h]);
+    fx_scale[h] = fixed_point_scale(mx);
   }
+  const uint32_t* rec = words + static_cast<int64_t>(kv) * wide_record_words(R) * a.total_tokens + row0 + tid;
+  if (!any_neg)
+    bin_packed_split<true, TPT>(bins, R, rec, a.total_tokens, w, valid, fx_scale);
+  else
+    bin_packed_split<false, TPT>(bins, R, rec, a.total_tokens, w, valid, fx_scale);
   __syncthreads();
-  // o[h][64g + w] = sum_r sum_l bins[h][g][r][l] * CV[g][r][l][w] / fx_scale[h]; each thread 2 outputs
+  // contraction: wave v takes rows [v K / 8, (v + 1) K / 8) of the K = R x 64 (residual, codeword) rows
+  const int g = lane >> 5, wp = lane & 31;
+  const f16* vcb = static_cast<const f16*>(a.v_cb) + static_cast<int64_t>(kv) * G * R * N * W + g * R * N * W + 2 * wp;
+  const int K = R * N, k0 = wave * K / kVrWaves, k1 = (wave + 1) * K / kVrWaves;
+  float acc[kGqa][2] = {};
+  static_assert(kWideCodes % (8 * kVrWaves) == 0, "each wave's rows are whole steps of 8");
+  if (!any_neg)
+    contract_packed<true>(bins, K, g, k0, k1, vcb, acc);
+  else
+    contract_packed<false>(bins, K, g, k0, k1, vcb, acc);
+  __syncthreads();  // every wave has read the bins: their LDS takes the waves' sums
+  float* sums = reinterpret_cast<float*>(bins);  // [kVrWaves][kGqa][kHeadDim], 16 KiB
+#pragma unroll
+  for (int h = 0; h < kGqa; ++h)
+    *reinterpret_cast<float2*>(sums + (wave * kGqa + h) * kHeadDim + W * g + 2 * wp) = make_float2(acc[h][0], acc[h][1]);
+  __syncthreads();
+  const int h = tid >> 7, d = tid & (kHeadDim - 1);
+  float o = 0.f;
+#pragma unroll
+  for (int v = 0; v < kVrWaves; ++v) o += sums[(v * kGqa + h) * kHeadDim + d];
   float* part = a.part + ((static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits + split) * kPartFloats;
   const int64_t row_stride = static_cast<int64_t>(a.n_splits) * kPartFloats;
-  const f16* vcb = static_cast<const f16*>(a.v_cb) + static_cast<int64_t>(kv) * G * R * N * W;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + 256 * i, h = idx >> 7, d = idx & 127, g = d / W, wd = d % W;
-    float acc = 0.f;
-    for (int r = 0; r < R; ++r) {
-      const int32_t* bb = bins + ((h * G + g) * R + r) * N;
-      const f16* cv = vcb + (static_cast<int64_t>(g) * R + r) * N * W + wd;
-      for (int l = 0; l < N; ++l) acc = fmaf(static_cast<float>(bb[l]), static_cast<float>(cv[l * W]), acc);
-    }
-    part[h * row_stride + 4 + d] = acc / fx_scale[h];
-  }
+  part[h * row_stride + 4 + d] = o / fx_scale[h];
 }
 
 hipError_t launch_value_reduce(int dtype, bool packed, int R, int B, const ValueReduceArgs& a, float* out,
                                hipStream_t s) {
   dim3 grid(a.n_splits, a.n_kv_heads, B);
   if (packed) {  // fp16 only
-    value_reduce_bits_kernel<<<grid, 256, 0, s>>>(a, R);
+    value_reduce_bits_kernel<<<grid, kVrThreads, 0, s>>>(a, R);
   } else if (dtype == COMMVQ_F16) {
     if (R == 1) value_reduce_kernel<f16, 1><<<grid, kVrThreads, 0, s>>>(a);
     else value_reduce_kernel<f16, 2><<<grid, kVrThreads, 0, s>>>(a);
