@@ -485,11 +485,14 @@ def codebook_tools_timing(reps: int = 3):
     }
 
 
-def step_kernels_timing(reps: int = 20):
+def step_kernels_timing(probes: dict, reps: int = 20):
     """The exported steps of the path, each on its own at the 128K layer shape (llama8b_128k_r2 inputs, fp16,
     R = 2), against the HBM roofline of its algorithmic bytes: the RoPE phase table for 131072 positions (bytes
     written), the query x codebook table of the 32 q heads (codebook read, table written), and the value reduction
-    (value codes and fp32 weights p read; bins in LDS, one partial per 2048-token split, then their sum).
+    (value codes and fp32 weights p read; bins in LDS, one partial per 2048-token split, then their sum). The value
+    reduction's binning makes one random 64-bit LDS add per (token, KV head, group, residual, head pair) (the
+    weights here are non-negative, so two heads share a bin word); at the live bin-add probe's rate those adds
+    alone take `lds_floor_us`, the bound that this step actually meets.
     `reps` launches of each are captured in one HIP graph and the replay is timed, so the figure is the kernels'
     own time and not the host's launch rate (the table kernels run for a few microseconds)."""
     import torch
@@ -541,8 +544,18 @@ def step_kernels_timing(reps: int = 20):
         "timing": f"{reps} launches in one HIP graph, 5 replays",
         "rope_table": line(t_rope, rope.numel() * 4),
         "qcodebook_table": line(t_tab, cb_bytes + table.numel() * table.element_size()),
-        "value_reduce": line(t_val, ly.v_codes.numel() * ly.v_codes.element_size() + p.numel() * 4),
+        "value_reduce": dict(line(t_val, ly.v_codes.numel() * ly.v_codes.element_size() + p.numel() * 4),
+                             **lds_adds_floor(2 * T * cfg.n_kv_heads * cfg.n_groups * cfg.n_residuals, t_val, probes)),
     }
+
+
+def lds_adds_floor(lane_adds: int, seconds: float, probes: dict) -> dict:
+    """LDS floor of `lane_adds` random 64-bit LDS adds (64 per wave instruction) at the bin-add probe's measured
+    cost per wave instruction per CU, over 256 CUs at 2.4 GHz."""
+    clk = probes["lds_bin_add"]["clk_per_wave_add_per_cu_at_2.4GHz"]
+    floor_s = lane_adds / 64 * clk / (256 * CLOCK_GHZ * 1e9)
+    return {"lds_bin_adds": lane_adds, "bin_add_clk_per_wave_instruction": clk, "lds_floor_us": floor_s * 1e6,
+            "frac_of_lds_floor": floor_s / seconds}
 
 
 # workloads of bench.py --profile (one attention kernel per workload kind; 20 launches each)
@@ -834,7 +847,7 @@ def main():
         "probes": probes,
         "kernel_source_sha256_16": {kind: kernel_source_hash(kind) for kind in KERNELS},
     }
-    line["steps"] = step_kernels_timing()
+    line["steps"] = step_kernels_timing(probes)
     line["codebook_tools"] = codebook_tools_timing()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, base)
