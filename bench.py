@@ -372,10 +372,10 @@ def run_config(cfg, steps: int, warmup: int, layers: int, use_graph: bool, check
         with torch.cuda.graph(g):
             for i in range(layers):
                 Ls[i].attn_decode()
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, steps // layers)
+        # the replays run for 0.5 s before the timed ones, and at least 20 replays are timed: a single replay
+        # also times the graph launch and reads up to 15% slow at 128K
+        settle(lambda i: g.replay(), 0.5)
+        reps = max(20, steps // layers)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
