@@ -184,11 +184,12 @@ int commvq_attn_decode_noalloc(const commvq_dims* d /* host */, const void* q, c
  * v_codes: the byte planes [Hkv][R][T][G], or (bit-packed layout) the word planes [Hkv][words][T].
  * p: [B][Hq][max_len] fp32, any finite real values, used as given (no renormalisation); entries at
  * t >= L_b are ignored. workspace: commvq_value_reduce_workspace_size(d, max_len) bytes.
- * Resolution: the bins are integer fixed point per (b, h, 2048-token split of t): each weight is rounded to
- * a multiple of 2^-19 * 2^e, where 2^e is the power of two just above the split's max |p| (fp16 storage),
- * and its rounding residual once more at 2^-39 * 2^e (fp32 storage). A weight below half that step (about
- * 2^-20, resp. 2^-40, of the split's largest) thus contributes nothing, and every other one is represented
- * to that absolute step; the result does not depend on the order of the adds.
+ * Resolution: the bins are integer fixed point per (b, h, work item of t): 4096 tokens for fp16 storage in the
+ * byte layout, 2048 for fp32 storage and for the bit-packed layout. Each weight is rounded to a multiple of
+ * 2^-B * 2^e, where 2^e is the power of two just above the item's max |p| and B = 18 (fp16 byte layout) or 19;
+ * for fp32 storage its rounding residual is binned once more, at 2^-(2B+1) * 2^e. A weight below half that
+ * step (about 2^-(B+1), resp. 2^-(2B+2), of the item's largest) thus contributes nothing, and every other one
+ * is represented to that absolute step; the result does not depend on the order of the adds.
  * seq_start / seq_len are clamped as in commvq_attn_decode (length at most max_len and the rows left).
  * ------------------------------------------------------------------------------------------- */
 size_t commvq_value_reduce_workspace_size(const commvq_dims* d /* host */, int32_t max_len);

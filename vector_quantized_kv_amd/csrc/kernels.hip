@@ -117,27 +117,42 @@ hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, 
 }
 
 // ----------------------------------------------------------------------------------- value bins
-// Fixed-point bins: LDS float atomics are slow on this chip, integer ones are not. Per (split, head) the
-// weights are scaled by a power of two, fx_scale = 2^(19 - e) with max|w| < 2^e, so |rint(w * fx_scale)| <= 2^19
-// and a 2048-token split's bin sums stay within 2^30 (inside int32). Pass 0 bins rint(w * fx_scale); the fp32
-// path adds pass 1, which bins rint((w * fx_scale - rint(w * fx_scale)) * 2^20), the rounding residual of
-// pass 0 at 2^20 times the resolution (at most 2^19 in magnitude; every step exact, as the scale is a power of
-// two). A weight is thus represented to 2^-20 of the split's max|w| (fp16 storage) or 2^-40 (fp32). bins layout
-// [kGqa][kGroups][R][kCodes].
+// Fixed-point bins: LDS float atomics are slow on this chip, integer ones are not. Per (work item, head) the
+// weights are scaled by a power of two, fx_scale = 2^(B - e) with max|w| < 2^e, so |rint(w * fx_scale)| <= 2^B,
+// and a work item of 2^(30 - B) tokens keeps every bin sum within 2^30 (inside int32): B = 18 for the 4096-token
+// items of the byte layout in fp16 storage, B = 19 for the 2048-token items of fp32 storage and of the bit-packed
+// layout. Pass 0 bins rint(w * fx_scale);
+// the fp32 path adds pass 1, which bins rint((w * fx_scale - rint(w * fx_scale)) * 2^(B + 1)), the rounding
+// residual of pass 0 at 2^(B + 1) times the resolution (at most 2^B in magnitude; every step exact, as the scales
+// are powers of two). A weight is thus represented to 2^-(B + 1) of the item's max|w| (fp16 storage) or
+// 2^-(2B + 2) (fp32). bins layout [kGqa][kGroups][R][kCodes].
+// tokens per (sequence, KV head) work item and the fixed-point bits B, by storage type of the byte layout (the
+// fp32 kernel keeps 2048-token items: at 4096 its registers spill)
+template <typename T>
+constexpr int kVrItemTokens = sizeof(T) == 2 ? 2 * kSplitTokens : kSplitTokens;
+template <typename T>
+constexpr int kVrBits = sizeof(T) == 2 ? 18 : 19;
+constexpr int kVrBitsPacked = 19;  // bit-packed layout: 2048-token items
+static_assert((static_cast<int64_t>(kVrItemTokens<f16>) << kVrBits<f16>) <= (int64_t{1} << 30) &&
+                  (static_cast<int64_t>(kVrItemTokens<float>) << kVrBits<float>) <= (int64_t{1} << 30) &&
+                  (static_cast<int64_t>(kSplitTokens) << kVrBitsPacked) <= (int64_t{1} << 30),
+              "bin sums stay within 2^30");
+template <int kBits>
 __device__ __forceinline__ int32_t fixed_point(float w, float fx_scale, int pass) {
   const float x = w * fx_scale;
   const float hi = rintf(x);
-  return static_cast<int32_t>(pass == 0 ? hi : rintf((x - hi) * 1048576.f));
+  return static_cast<int32_t>(pass == 0 ? hi : rintf((x - hi) * static_cast<float>(1 << (kBits + 1))));
 }
 
+template <int kBits>
 __device__ __forceinline__ float fixed_point_scale(float max_abs) {
   if (!(max_abs > 0.f)) return 1.f;
   int e;
   frexpf(max_abs, &e);  // max_abs = m 2^e, m in [0.5, 1)
-  return ldexpf(1.f, 19 - e);
+  return ldexpf(1.f, kBits - e);
 }
 
-template <int R, int TPT>
+template <int R, int TPT, int kBits>
 __device__ __forceinline__ void bin_weights(int32_t* bins, const uint4 (&vc)[TPT][R], const float (&w)[TPT][kGqa],
                                             const bool (&valid)[TPT], const float (&fx_scale)[kGqa], int pass) {
 #pragma unroll
@@ -145,7 +160,7 @@ __device__ __forceinline__ void bin_weights(int32_t* bins, const uint4 (&vc)[TPT
     if (!valid[k]) continue;
     int32_t fx[kGqa];
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) fx[h] = fixed_point(w[k][h], fx_scale[h], pass);
+    for (int h = 0; h < kGqa; ++h) fx[h] = fixed_point<kBits>(w[k][h], fx_scale[h], pass);
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
 #pragma unroll
@@ -160,7 +175,7 @@ __device__ __forceinline__ void bin_weights(int32_t* bins, const uint4 (&vc)[TPT
 // Non-negative weights (a softmax's, the usual case): two heads share a 64-bit bin, layout [2 head pairs][kGroups]
 // [R][kCodes] (the same bytes as the int32 bins). A bin's sums stay within 2^30 (see fixed_point_scale), so the
 // low head never carries into the high one and one ds_add_u64 does the work of two ds_add_u32.
-template <int R, int TPT>
+template <int R, int TPT, int kBits>
 __device__ __forceinline__ void bin_weights_pairs(unsigned long long* bins, const uint4 (&vc)[TPT][R],
                                                   const float (&w)[TPT][kGqa], const bool (&valid)[TPT],
                                                   const float (&fx_scale)[kGqa]) {
@@ -169,7 +184,7 @@ __device__ __forceinline__ void bin_weights_pairs(unsigned long long* bins, cons
     if (!valid[k]) continue;
     uint32_t fx[kGqa];
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<uint32_t>(fixed_point(w[k][h], fx_scale[h], 0));
+    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<uint32_t>(fixed_point<kBits>(w[k][h], fx_scale[h], 0));
     const unsigned long long p01 = fx[0] | (static_cast<unsigned long long>(fx[1]) << 32);
     const unsigned long long p23 = fx[2] | (static_cast<unsigned long long>(fx[3]) << 32);
 #pragma unroll
@@ -312,19 +327,22 @@ __device__ __forceinline__ void contract_bins_mfma(const int32_t* bins, const ui
 
 // ----------------------------------------------------------------------------------- value reduce
 // The reordered value reduce of the pages: weights are binned by value code (bin_weights), then the
-// bins are contracted with the value codebook (contract_bins). One workgroup per (sequence, KV head,
-// 2048-token split); partial outputs are summed by combine_sum_kernel. Any finite weights bin exactly up
-// to the fixed-point resolution above (one pass for fp16 storage, two for fp32).
+// bins are contracted with the value codebook (contract_bins). One workgroup per (sequence, KV head, work item
+// of kVrItemTokens tokens: 4096 for fp16 storage, so a 128K context with 8 KV heads fills the 256 CUs in one round,
+// the bins taking a CU's LDS); partial outputs, one per item in the first slots of the 2048-token split partials,
+// are summed by combine_sum_kernel. Any finite weights bin exactly up to the fixed-point resolution above (one pass for fp16
+// storage, two for fp32).
 template <typename T, int R>
 __global__ void __launch_bounds__(kVrThreads) value_reduce_kernel(const ValueReduceArgs a) {
-  constexpr int TPT = kSplitTokens / kVrThreads;
+  constexpr int kItem = kVrItemTokens<T>, kBits = kVrBits<T>;
+  constexpr int TPT = kItem / kVrThreads;
   constexpr int kPasses = sizeof(T) == 4 ? 2 : 1;
   __shared__ float red[kVrWaves][kGqa];
   __shared__ __attribute__((aligned(16))) int32_t work[kGqa * kGroups * R * kCodes];
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int item = blockIdx.x, kv = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const SeqBounds sb = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens);
   const int L = sb.len;
-  const int t0 = split * kSplitTokens;
+  const int t0 = item * kItem;
   if (t0 >= L) return;
   const int64_t row0 = sb.start + t0;
   const int h0 = kv * kGqa;
@@ -369,10 +387,10 @@ __global__ void __launch_bounds__(kVrThreads) value_reduce_kernel(const ValueRed
     float mx = red[0][h];
 #pragma unroll
     for (int v = 1; v < kVrWaves; ++v) mx = fmaxf(mx, red[v][h]);
-    fx_scale[h] = fixed_point_scale(mx);
+    fx_scale[h] = fixed_point_scale<kBits>(mx);
   }
   const T* vcb = static_cast<const T*>(a.v_cb) + static_cast<int64_t>(kv) * kGroups * R * kCodes * kGroupDim;
-  float* part = a.part + ((static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits + split) * kPartFloats;
+  float* part = a.part + ((static_cast<int64_t>(b) * a.n_q_heads + h0) * a.n_splits + item) * kPartFloats;
   const int64_t row_stride = static_cast<int64_t>(a.n_splits) * kPartFloats;
   if constexpr (sizeof(T) == 2) {
     uint4 rows[kVrGpw][R][4];
@@ -384,11 +402,11 @@ __global__ void __launch_bounds__(kVrThreads) value_reduce_kernel(const ValueRed
 #pragma unroll
     for (int h = 0; h < kGqa; ++h) inv[h] = 1.f / fx_scale[h];  // a power of two: exact
     if (!any_neg) {
-      bin_weights_pairs<R, TPT>(reinterpret_cast<unsigned long long*>(work), vc, w, valid, fx_scale);
+      bin_weights_pairs<R, TPT, kBits>(reinterpret_cast<unsigned long long*>(work), vc, w, valid, fx_scale);
       __syncthreads();
       contract_bins_mfma<R, true>(work, rows, inv, part, row_stride);
     } else {
-      bin_weights<R, TPT>(work, vc, w, valid, fx_scale, 0);
+      bin_weights<R, TPT, kBits>(work, vc, w, valid, fx_scale, 0);
       __syncthreads();
       contract_bins_mfma<R, false>(work, rows, inv, part, row_stride);
     }
@@ -400,9 +418,9 @@ __global__ void __launch_bounds__(kVrThreads) value_reduce_kernel(const ValueRed
       for (int i = tid; i < kGqa * kGroups * R * kCodes / 4; i += kVrThreads)
       reinterpret_cast<int4*>(work)[i] = make_int4(0, 0, 0, 0);
       __syncthreads();
-      bin_weights<R, TPT>(work, vc, w, valid, fx_scale, pass);
+      bin_weights<R, TPT, kBits>(work, vc, w, valid, fx_scale, pass);
       __syncthreads();
-      contract_bins<T, R, kVrThreads>(work, vcb, pass == 0 ? 1.f : 1.f / 1048576.f, acc);
+      contract_bins<T, R, kVrThreads>(work, vcb, pass == 0 ? 1.f : 1.f / static_cast<float>(1 << (kBits + 1)), acc);
     }
 #pragma unroll
     for (int i = 0; i < kOut; ++i) {
@@ -412,16 +430,17 @@ __global__ void __launch_bounds__(kVrThreads) value_reduce_kernel(const ValueRed
   }
 }
 
-// One workgroup per (b, q head): thread (d, k) sums the splits k, k + 8, ... of output d (four loads in flight),
-// and the 8 partial sums are added in a fixed order.
+// One workgroup per (b, q head): thread (d, k) sums the work items k, k + 8, ... of output d (four loads in
+// flight), and the 8 partial sums are added in a fixed order. A work item covers item_tokens tokens and its partial
+// sits in slot item of the partials.
 constexpr int kCombineParts = 8;
 __global__ void __launch_bounds__(kCombineParts * kHeadDim) combine_sum_kernel(const float* part, const ValueReduceArgs a,
-                                                                             float* out) {
+                                                                             int item_tokens, float* out) {
   __shared__ float red[kCombineParts][kHeadDim];
   const int bh = blockIdx.x, b = bh / a.n_q_heads, d = threadIdx.x & (kHeadDim - 1), k = threadIdx.x / kHeadDim;
   const int L = seq_bounds(a.seq_start, a.seq_len, b, a.p_stride, a.total_tokens).len;  // as value_reduce_kernel
   const int n_splits = a.n_splits;
-  const int ns = (L + kSplitTokens - 1) / kSplitTokens;
+  const int ns = (L + item_tokens - 1) / item_tokens;
   const float* p = part + static_cast<int64_t>(bh) * n_splits * kPartFloats + 4 + d;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   int s = k;
@@ -491,7 +510,7 @@ __device__ __forceinline__ void bin_packed_tokens(int32_t* bins, int R, const ui
     if (!valid[k]) continue;
     uint32_t fx[kGqa];
 #pragma unroll
-    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<uint32_t>(fixed_point(w[k][h], fx_scale[h], 0));
+    for (int h = 0; h < kGqa; ++h) fx[h] = static_cast<uint32_t>(fixed_point<kVrBitsPacked>(w[k][h], fx_scale[h], 0));
 #pragma unroll
     for (int c = 0; c < NWIN; ++c)
       bin_packed_window<kPairs>(bins, R, c, x[k][c][0], x[k][c][1], x[k][c][2], fx,
@@ -615,7 +634,7 @@ __global__ void __launch_bounds__(kVrThreads) value_reduce_bits_kernel(const Val
     float mx = 0.f;
 #pragma unroll
     for (int v = 0; v < kVrWaves; ++v) mx = fmaxf(mx, red[v][h]);
-    fx_scale[h] = fixed_point_scale(mx);
+    fx_scale[h] = fixed_point_scale<kVrBitsPacked>(mx);
   }
   const uint32_t* rec = words + static_cast<int64_t>(kv) * wide_record_words(R) * a.total_tokens + row0 + tid;
   if (!any_neg)
@@ -650,7 +669,9 @@ __global__ void __launch_bounds__(kVrThreads) value_reduce_bits_kernel(const Val
 
 hipError_t launch_value_reduce(int dtype, bool packed, int R, int B, const ValueReduceArgs& a, float* out,
                                hipStream_t s) {
-  dim3 grid(a.n_splits, a.n_kv_heads, B);
+  // work items: 2048-token splits (bit-packed, byte layout in fp32), pairs of them (byte layout in fp16)
+  const int item_tokens = packed ? kSplitTokens : (dtype == COMMVQ_F16 ? kVrItemTokens<f16> : kVrItemTokens<float>);
+  dim3 grid((a.n_splits * kSplitTokens + item_tokens - 1) / item_tokens, a.n_kv_heads, B);
   if (packed) {  // fp16 only
     value_reduce_bits_kernel<<<grid, kVrThreads, 0, s>>>(a, R);
   } else if (dtype == COMMVQ_F16) {
@@ -662,7 +683,7 @@ hipError_t launch_value_reduce(int dtype, bool packed, int R, int B, const Value
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_sum_kernel<<<dim3(B * a.n_q_heads), dim3(kCombineParts * kHeadDim), 0, s>>>(a.part, a, out);
+  combine_sum_kernel<<<dim3(B * a.n_q_heads), dim3(kCombineParts * kHeadDim), 0, s>>>(a.part, a, item_tokens, out);
   return hipGetLastError();
 }
 
