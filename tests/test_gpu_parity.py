@@ -131,8 +131,9 @@ def test_qcodebook_table_matches_oracle(vq, dtype, R, tol):
                                             ("float16", 1, True), ("float16", 1, False), ("float16", 2, True),
                                             ("float16", 2, "mixed")])
 def test_value_reduce_matches_oracle(vq, dtype, R, signed):
-    """Weights of either sign; "mixed": negative only in a few tokens of the second 2048-token split of the first
-    sequence, so that one workgroup takes the signed bins and the others the non-negative ones."""
+    """Weights of either sign; "mixed": negative only in a few tokens past token 2048 of the first sequence (its
+    second 2048-token work item in fp32 storage, its only 4096-token item in fp16 storage), so that one workgroup
+    takes the signed bins and the others the non-negative ones."""
     announce(f"value_reduce {dtype} R={R} signed={signed}")
     cfg = workloads.custom("vr", 3, 8, 2, (2500, 1, 1024), R, dtype, 22)
     inp = workloads.make_inputs(cfg)
@@ -150,6 +151,28 @@ def test_value_reduce_matches_oracle(vq, dtype, R, signed):
     ref = oracle.value_reduce(oracle.dims_of(cfg), p, inp["v_codes"], inp["v_cb"], inp["seq_start"], inp["seq_len"], L)
     err = rowwise_rel_err(got.cpu().numpy(), ref)
     print(f"value_reduce {dtype} R={R}: {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,R,signed", [("float16", 2, False), ("float16", 1, True), ("float32", 2, True)])
+def test_value_reduce_work_item_edges(vq, dtype, R, signed):
+    """Sequence lengths at and around the work-item sizes (4096 tokens in fp16 storage, 2048 in fp32): exactly one
+    and two items, one token past an item, one token short of one, and three items plus one token."""
+    announce(f"value_reduce item edges {dtype} R={R} signed={signed}")
+    cfg = workloads.custom("vr_edges", 5, 8, 2, (8192, 4097, 4095, 4096, 12289), R, dtype, 26)
+    inp = workloads.make_inputs(cfg)
+    L = int(inp["max_len"])
+    rng = np.random.default_rng(27)
+    p = rng.uniform(-1 if signed else 0, 1, size=(5, 8, L)).astype(np.float32)
+    d = vq.dims_of(cfg)
+    dt = torch.float16 if dtype == "float16" else torch.float32
+    got = vq.value_reduce(d, torch.from_numpy(p).cuda(), torch.from_numpy(inp["v_codes"]).cuda(),
+                          torch.from_numpy(inp["v_cb"]).cuda().to(dt), torch.from_numpy(inp["seq_start"]).cuda(),
+                          torch.from_numpy(inp["seq_len"]).cuda(), L, int(inp["total_tokens"]))
+    torch.cuda.synchronize()
+    ref = oracle.value_reduce(oracle.dims_of(cfg), p, inp["v_codes"], inp["v_cb"], inp["seq_start"], inp["seq_len"], L)
+    err = rowwise_rel_err(got.cpu().numpy(), ref)
+    print(f"value_reduce item edges {dtype} R={R}: {err:.3e}", flush=True)
     assert err <= TOL[dtype]
 
 
