@@ -23,7 +23,8 @@
 // softmax by more than the 2e-3 output tolerance; in fp32 the key path is exact to a few fp32 ulps.
 // The fp32 phases of one lane (64 pairs) would take 128 registers, so they stay in LDS (32 KiB) and the key
 // pass runs group-major: a wave reads one group's phases once and applies them to 2 of its blocks (one
-// "sweep"); a full wave (8 blocks) makes four sweeps, shorter waves go block by block.
+// "sweep"); a wave with an even number of blocks makes one sweep per two, a wave with an odd number goes block
+// by block.
 //
 // LDS: two residual codebooks (64 KiB each: 16 groups x 256 rows x 8 fp16) and the phase table (32 KiB) fill
 // the CU's 160 KiB (map below). R = 1: key and value codebook, both loaded in the prologue. R = 2: the two key
@@ -419,7 +420,7 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
 #pragma unroll
     for (int ii = 0; ii < kSweep; ++ii) sc[kSweep * s + ii] = acc[2 * ii] + acc[2 * ii + 1];
   };
-  // One block alone (waves with fewer than 8 blocks): groups 0..15 with the phases read per group.
+  // One block alone (waves with an odd number of blocks): groups 0..15 with the phases read per group.
   float2 curA[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) curA[k] = qc0[k];
@@ -460,16 +461,22 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
     // requested during the value pass, four blocks ahead)
     if constexpr (i < kValueLead) request(a.v_codes, i);
   };
-  if (my_blocks == kMaxBlocks) {
+  if (my_blocks > 0 && my_blocks % kSweep == 0) {
     // each sweep first requests the next sweep's key records; the value records of the first four blocks follow
-    // their key records
+    // their key records. A wave with fewer than 8 blocks skips the sweeps past its blocks but issues the same
+    // record loads (clamped rows), so that every vmcnt count below holds, and takes part in the region A
+    // hand-over where its last sweep would have.
     static_for<kMaxBlocks / kSweep>([&](auto sc_) {
       constexpr int s = decltype(sc_)::value;
       if constexpr (kSweep * (s + 1) < kMaxBlocks) {
 #pragma unroll
         for (int i = kSweep * (s + 1); i < kSweep * (s + 2); ++i) request(a.k_codes, i);
       }
-      sweep(sc_);
+      if (kSweep * s < my_blocks) {
+        sweep(sc_);
+      } else if constexpr (s == kMaxBlocks / kSweep - 1) {
+        refill_lo();
+      }
       if constexpr (kSweep * (s + 1) <= kValueLead) {
 #pragma unroll
         for (int i = kSweep * s; i < kSweep * (s + 1); ++i) request(a.v_codes, i);
