@@ -380,16 +380,17 @@ __global__ void __launch_bounds__(kThreads16) attn_f16_kernel(const AttnArgs a) 
       constexpr int g = decltype(gc)::value;
       if constexpr (g % 4 == 0) {
         __builtin_amdgcn_s_setprio(3 - (kGroups * s + g) * 4 / (kGroups * (kMaxBlocks / kSweep)));
-        // A operands of pairs 16 (g / 4) + quad for the sweep's blocks: q'' of block i is qc0 stepped i times
+        // A operands of pairs 16 (g / 4) + quad for the sweep's blocks: q'' of block i is the first block's q''
+        // stepped i times. qc0[k] holds q'' of the sweep's first block and is stepped on past the sweep's blocks
+        // here (the same products in the same order as stepping from block 0 each time)
         constexpr int k = g / 4;
         float2 cur = qc0[k];
-#pragma unroll
-        for (int j = 0; j < kSweep * s; ++j) cur = cmul_conj(cur, stepE[k]);
 #pragma unroll
         for (int j = 0; j < kSweep; ++j) {
           A[j] = cur;
           cur = cmul_conj(cur, stepE[k]);
         }
+        qc0[k] = cur;
       }
       float w[kSweep][8];
       if constexpr (R == 1) {
