@@ -94,6 +94,24 @@ def test_attn_decode_edge_cases(vq, name, B, lengths, R, dtype):
     assert err <= TOL[dtype]
 
 
+# 8 KV heads, as in the benchmark: 64K and 96K tokens give every wave 4 and 6 key blocks (key sweeps of two blocks
+# with the later sweeps skipped); the ragged batch mixes even and odd block counts within one workgroup.
+SWEEP_CASES = [("sweeps_4_blocks_r2", 1, (65536,), 2), ("sweeps_6_blocks_r2", 1, (98304,), 2),
+               ("sweeps_6_blocks_r1", 1, (98304,), 1), ("sweeps_mixed_r2", 3, (50000, 30000, 12000), 2)]
+
+
+@pytest.mark.parametrize("name,B,lengths,R", SWEEP_CASES)
+def test_attn_decode_block_counts(vq, name, B, lengths, R):
+    announce(f"attn_decode {name} lengths={lengths} R={R}")
+    cfg = workloads.custom(name, B, 32, 8, lengths, R, "float16", 200 + len(name))
+    inp = workloads.make_inputs(cfg)
+    got = run_attn(vq, cfg, inp)
+    ref = oracle.run_config(cfg, inp, n_threads=THREADS)
+    err = rowwise_rel_err(got, ref)
+    print(f"{name}: {err:.3e}", flush=True)
+    assert err <= TOL["float16"]
+
+
 @pytest.mark.parametrize("name", ["tiny_1k_r2_f32", "llama8b_8k_r2", "llama8b_32k_r1", "ragged16_r2"])
 def test_unpack_bit_exact(vq, name):
     cfg = workloads.CONFIGS[name]
