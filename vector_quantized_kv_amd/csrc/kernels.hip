@@ -121,13 +121,13 @@ hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, 
 // weights are scaled by a power of two, fx_scale = 2^(B - e) with max|w| < 2^e, so |rint(w * fx_scale)| <= 2^B,
 // and a work item of 2^(30 - B) tokens keeps every bin sum within 2^30 (inside int32): B = 18 for the 4096-token
 // items of the byte layout in fp16 storage, B = 19 for the 2048-token items of fp32 storage and of the bit-packed
-// layout. Pass 0 bins rint(w * fx_scale);
-// the fp32 path adds pass 1, which bins rint((w * fx_scale - rint(w * fx_scale)) * 2^(B + 1)), the rounding
-// residual of pass 0 at 2^(B + 1) times the resolution (at most 2^B in magnitude; every step exact, as the scales
-// are powers of two). A weight is thus represented to 2^-(B + 1) of the item's max|w| (fp16 storage) or
-// 2^-(2B + 2) (fp32). bins layout [kGqa][kGroups][R][kCodes].
-// tokens per (sequence, KV head) work item and the fixed-point bits B, by storage type of the byte layout (the
-// fp32 kernel keeps 2048-token items: at 4096 its registers spill)
+// layout. Pass 0 bins rint(w * fx_scale); the fp32 path adds pass 1, which bins
+// rint((w * fx_scale - rint(w * fx_scale)) * 2^(B + 1)), the rounding residual of pass 0 at 2^(B + 1) times the
+// resolution (at most 2^B in magnitude; every step exact, as the scales are powers of two). A weight is thus
+// represented to 2^-(B + 1) of the item's max|w| (fp16 storage) or 2^-(2B + 2) (fp32). bins layout
+// [kGqa][kGroups][R][kCodes].
+// Tokens per (sequence, KV head) work item and the fixed-point bits B, by storage type of the byte layout (the
+// fp32 kernel keeps 2048-token items: at 4096 its registers spill).
 template <typename T>
 constexpr int kVrItemTokens = sizeof(T) == 2 ? 2 * kSplitTokens : kSplitTokens;
 template <typename T>
@@ -328,10 +328,10 @@ __device__ __forceinline__ void contract_bins_mfma(const int32_t* bins, const ui
 // ----------------------------------------------------------------------------------- value reduce
 // The reordered value reduce of the pages: weights are binned by value code (bin_weights), then the
 // bins are contracted with the value codebook (contract_bins). One workgroup per (sequence, KV head, work item
-// of kVrItemTokens tokens: 4096 for fp16 storage, so a 128K context with 8 KV heads fills the 256 CUs in one round,
-// the bins taking a CU's LDS); partial outputs, one per item in the first slots of the 2048-token split partials,
-// are summed by combine_sum_kernel. Any finite weights bin exactly up to the fixed-point resolution above (one pass for fp16
-// storage, two for fp32).
+// of kVrItemTokens tokens: 4096 for fp16 storage, so a 128K context with 8 KV heads fills the 256 CUs in one
+// round, the bins taking a CU's LDS); partial outputs, one per item in the first slots of the 2048-token split
+// partials, are summed by combine_sum_kernel. Any finite weights bin exactly up to the fixed-point resolution
+// above (one pass for fp16 storage, two for fp32).
 template <typename T, int R>
 __global__ void __launch_bounds__(kVrThreads) value_reduce_kernel(const ValueReduceArgs a) {
   constexpr int kItem = kVrItemTokens<T>, kBits = kVrBits<T>;
