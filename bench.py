@@ -492,7 +492,8 @@ def step_kernels_timing(probes: dict, reps: int = 20):
     (value codes and fp32 weights p read; bins in LDS, one partial per 2048-token split, then their sum). The value
     reduction's binning makes one random 64-bit LDS add per (token, KV head, group, residual, head pair) (the
     weights here are non-negative, so two heads share a bin word); at the live bin-add probe's rate those adds
-    alone take `lds_floor_us`, the bound that this step actually meets.
+    alone take `lds_floor_us`, the bound that this step actually meets. `pages_setting` times the same two table
+    steps on the pages' own bit-packed layout (64-dim groups, 64 codewords, R = 21) at the same context.
     `reps` launches of each are captured in one HIP graph and the replay is timed, so the figure is the kernels'
     own time and not the host's launch rate (the table kernels run for a few microseconds)."""
     import torch
@@ -539,6 +540,27 @@ def step_kernels_timing(probes: dict, reps: int = 20):
     t_val = timed(lambda: vq.value_reduce(d, p, ly.v_codes, ly.v_cb, ly.seq_start, ly.seq_len, ly.max_len, T,
                                           workspace=ws, out=vout))
     cb_bytes = ly.k_cb.numel() * ly.k_cb.element_size()
+    # the pages' own setting: bit-packed records, R = 21, the same context and heads
+    pcfg = workloads.PAGES_CONFIGS["pages_g64_r21_128k"]
+    pd = vq.dims_of(pcfg)
+    pinp = workloads.make_inputs(pcfg)
+    ply = vq.Layer(pd, pinp)
+    ptable = vq.qcodebook_table(pd, ply.q, ply.k_cb)
+    pvout = vq.value_reduce(pd, p, ply.v_codes, ply.v_cb, ply.seq_start, ply.seq_len, ply.max_len, T)
+    pws = torch.empty(max(vq.value_reduce_workspace_size(pd, ply.max_len), 16), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    t_ptab = timed(lambda: vq.qcodebook_table(pd, ply.q, ply.k_cb, out=ptable))
+    t_pval = timed(lambda: vq.value_reduce(pd, p, ply.v_codes, ply.v_cb, ply.seq_start, ply.seq_len, ply.max_len, T,
+                                           workspace=pws, out=pvout))
+    pcb_bytes = ply.k_cb.numel() * ply.k_cb.element_size()
+    pages = {
+        "shape": f"{T} tokens, {pcfg.n_kv_heads} KV / {pcfg.n_q_heads} q heads, bit-packed, G=2, N=64, "
+                 f"R={pcfg.n_residuals}, fp16",
+        "qcodebook_table": line(t_ptab, pcb_bytes + ptable.numel() * ptable.element_size()),
+        "value_reduce": dict(line(t_pval, ply.v_codes.numel() * ply.v_codes.element_size() + p.numel() * 4),
+                             **lds_adds_floor(2 * T * pcfg.n_kv_heads * pcfg.n_groups * pcfg.n_residuals, t_pval,
+                                              probes)),
+    }
     return {
         "shape": f"{T} tokens, {cfg.n_kv_heads} KV / {cfg.n_q_heads} q heads, R={cfg.n_residuals}, fp16",
         "timing": f"{reps} launches in one HIP graph, 5 replays",
@@ -546,6 +568,7 @@ def step_kernels_timing(probes: dict, reps: int = 20):
         "qcodebook_table": line(t_tab, cb_bytes + table.numel() * table.element_size()),
         "value_reduce": dict(line(t_val, ly.v_codes.numel() * ly.v_codes.element_size() + p.numel() * 4),
                              **lds_adds_floor(2 * T * cfg.n_kv_heads * cfg.n_groups * cfg.n_residuals, t_val, probes)),
+        "pages_setting": pages,
     }
 
 
