@@ -65,26 +65,34 @@ hipError_t launch_rope_table(double base, int32_t n_positions, float2* table, hi
 }
 
 // ------------------------------------------------------------------------- query x codebook table
-// grid (G*R, Hq, B), block N: thread l writes the W/2 complex entries of code l. Byte layout G = 16, N = 256,
-// W = 8; bit-packed layout G = 2, N = 64, W = 64. Codeword and entries move in 16-byte pieces (a codeword row
-// is W * sizeof(T) >= 16 bytes and 16-byte aligned), so a wave's loads and stores cover whole contiguous rows.
+// grid (G*R, Hq, B): the workgroup writes the N x W/2 complex entries of one (b, h, g, r). Byte layout G = 16,
+// N = 256, W = 8; bit-packed layout G = 2, N = 64, W = 64. Codeword and entries move in 16-byte pieces (a codeword
+// row is W * sizeof(T) >= 16 bytes and 16-byte aligned); consecutive threads take consecutive pieces (thread i:
+// piece i mod P of row i / P, P pieces per row), so every wave instruction loads and stores whole contiguous rows.
+template <typename T, int W>
+constexpr int qtable_pieces = W / (16 / static_cast<int>(sizeof(T)));  // 16-byte pieces per codeword row
+template <typename T, int G, int N>
+constexpr int qtable_threads = N * qtable_pieces<T, kHeadDim / G> < 256 ? N * qtable_pieces<T, kHeadDim / G> : 256;
 template <typename T, int G, int N>
 __global__ void __launch_bounds__(256) qtable_kernel(const T* q, const T* kcb, T* out, int Hq, int Hkv, int R) {
   constexpr int W = kHeadDim / G;
   constexpr int kPer = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte piece
-  static_assert(W % kPer == 0, "codeword rows are whole 16-byte pieces");
-  const int gr = blockIdx.x, h = blockIdx.y, b = blockIdx.z, l = threadIdx.x;
+  constexpr int P = qtable_pieces<T, W>, kThreads = qtable_threads<T, G, N>;
+  static_assert(W % kPer == 0 && (N * P) % kThreads == 0, "codeword rows are whole 16-byte pieces");
+  const int gr = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int g = gr / R, r = gr % R, kv = h / (Hq / Hkv);
   const T* qq = q + (static_cast<int64_t>(b) * Hq + h) * kHeadDim + W * g;
-  const uint4* c = reinterpret_cast<const uint4*>(kcb + (((static_cast<int64_t>(kv) * G + g) * R + r) * N + l) * W);
-  uint4* o = reinterpret_cast<uint4*>(out + ((((static_cast<int64_t>(b) * Hq + h) * G + g) * R + r) * N + l) * W);
+  const uint4* c = reinterpret_cast<const uint4*>(kcb + (((static_cast<int64_t>(kv) * G + g) * R + r) * N) * W);
+  uint4* o = reinterpret_cast<uint4*>(out + ((((static_cast<int64_t>(b) * Hq + h) * G + g) * R + r) * N) * W);
 #pragma unroll
-  for (int piece = 0; piece < W / kPer; ++piece) {
+  for (int it = 0; it < N * P / kThreads; ++it) {
+    const int item = static_cast<int>(threadIdx.x) + kThreads * it;  // = row * P + piece
+    const int piece = item % P;
     union {
       uint4 v;
       T e[kPer];
     } in, res;
-    in.v = c[piece];
+    in.v = c[item];
 #pragma unroll
     for (int u = 0; u < kPer / 2; ++u) {
       const int d = piece * kPer + 2 * u;
@@ -93,26 +101,25 @@ __global__ void __launch_bounds__(256) qtable_kernel(const T* q, const T* kcb, T
       res.e[2 * u] = static_cast<T>(q0 * a + q1 * bb);
       res.e[2 * u + 1] = static_cast<T>(q0 * bb - q1 * a);
     }
-    o[piece] = res.v;
+    o[item] = res.v;
   }
 }
 
 hipError_t launch_qtable(int dtype, bool packed, int R, int B, int Hq, int Hkv, const void* q, const void* kcb,
                          void* out, hipStream_t s) {
   if (packed) {  // fp16 only
-    qtable_kernel<f16, kWideGroups, kWideCodes><<<dim3(kWideGroups * R, Hq, B), kWideCodes, 0, s>>>(
-        static_cast<const f16*>(q), static_cast<const f16*>(kcb), static_cast<f16*>(out), Hq, Hkv, R);
+    qtable_kernel<f16, kWideGroups, kWideCodes>
+        <<<dim3(kWideGroups * R, Hq, B), qtable_threads<f16, kWideGroups, kWideCodes>, 0, s>>>(
+            static_cast<const f16*>(q), static_cast<const f16*>(kcb), static_cast<f16*>(out), Hq, Hkv, R);
     return hipGetLastError();
   }
   dim3 grid(kGroups * R, Hq, B);
   if (dtype == COMMVQ_F16)
-    qtable_kernel<f16, kGroups, kCodes><<<grid, kCodes, 0, s>>>(static_cast<const f16*>(q),
-                                                                static_cast<const f16*>(kcb), static_cast<f16*>(out),
-                                                                Hq, Hkv, R);
+    qtable_kernel<f16, kGroups, kCodes><<<grid, qtable_threads<f16, kGroups, kCodes>, 0, s>>>(
+        static_cast<const f16*>(q), static_cast<const f16*>(kcb), static_cast<f16*>(out), Hq, Hkv, R);
   else
-    qtable_kernel<float, kGroups, kCodes><<<grid, kCodes, 0, s>>>(static_cast<const float*>(q),
-                                                                  static_cast<const float*>(kcb),
-                                                                  static_cast<float*>(out), Hq, Hkv, R);
+    qtable_kernel<float, kGroups, kCodes><<<grid, qtable_threads<float, kGroups, kCodes>, 0, s>>>(
+        static_cast<const float*>(q), static_cast<const float*>(kcb), static_cast<float*>(out), Hq, Hkv, R);
   return hipGetLastError();
 }
 
